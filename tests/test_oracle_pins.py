@@ -1,0 +1,347 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Every check below compares the oracle with something independent of its
+code: exact rational arithmetic of the printed matrix form of the gated delta
+rule (explicit I - beta k k^T, explicit matrix products), closed forms of
+special cases, invariants of the recurrence, and identities between the
+chain, tree and chunked orchestrations.  A dropped term, a wrong sign, a
+transposed operand, a pre-update output read or a wrong parent index each
+fails at least one of them.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from gated_deltanet_recurrence_gdn_amd import workloads as wl
+
+
+# --------------------------------------------------------------------------
+# exact rational brute force of the printed rule
+#   S' = alpha S (I - beta k k^T) + beta v k^T,  o = scale S' q
+# with S (d_v x d_k), matrices built entry by entry and multiplied naively.
+# --------------------------------------------------------------------------
+def _frac(x):
+    return Fraction(float(x))
+
+
+def _rational_step(S, q, k, v, alpha, beta, scale=Fraction(1)):
+    dv, dk = len(S), len(S[0])
+    M = [[(Fraction(1) if r == c else Fraction(0)) - beta * k[r] * k[c] for c in range(dk)]
+         for r in range(dk)]
+    SM = [[sum(S[j][m] * M[m][c] for m in range(dk)) for c in range(dk)] for j in range(dv)]
+    Sn = [[alpha * SM[j][c] + beta * v[j] * k[c] for c in range(dk)] for j in range(dv)]
+    o = [scale * sum(Sn[j][c] * q[c] for c in range(dk)) for j in range(dv)]
+    return Sn, o
+
+
+def _dyadic(rng, shape, denom=8, lo=-8, hi=8):
+    return rng.integers(lo, hi + 1, size=shape).astype(np.float64) / denom
+
+
+def _close(a, b, tol):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    return float(np.max(np.abs(a - b))) <= tol * scale if a.size else True
+
+
+@pytest.mark.parametrize("dk,dv", [(3, 2), (2, 3), (4, 4)])
+def test_step_matches_exact_rational_matrix_rule(oracle_mod, dk, dv):
+    rng = np.random.default_rng(7)
+    for _ in range(5):
+        S = _dyadic(rng, (dv, dk))
+        q = _dyadic(rng, dk)
+        k = _dyadic(rng, dk)
+        v = _dyadic(rng, dv)
+        alpha, beta, scale = 0.75, 0.375, 0.5
+        Sn, o = oracle_mod.step(S, q, k, v, alpha, beta, scale)
+        Sr, orr = _rational_step([[_frac(x) for x in row] for row in S], [_frac(x) for x in q],
+                                 [_frac(x) for x in k], [_frac(x) for x in v], _frac(alpha),
+                                 _frac(beta), _frac(scale))
+        assert _close(Sn, [[float(x) for x in r] for r in Sr], 1e-15)
+        assert _close(o, [float(x) for x in orr], 1e-15)
+
+
+def test_chain_matches_exact_rational_composition(oracle_mod):
+    """A 6-node chain, 2 value heads on 1 q/k head, d_k != d_v."""
+    rng = np.random.default_rng(11)
+    B, N, Hqk, Hv, dk, dv = 1, 6, 1, 2, 3, 2
+    q = _dyadic(rng, (B, N, Hqk, dk))
+    k = _dyadic(rng, (B, N, Hqk, dk))
+    v = _dyadic(rng, (B, N, Hv, dv))
+    alpha = rng.integers(0, 5, size=(B, N, Hv)) / 4.0
+    beta = rng.integers(0, 5, size=(B, N, Hv)) / 4.0
+    S0 = _dyadic(rng, (B, Hv, dv, dk))
+    res = oracle_mod.chain(q, k, v, alpha, beta, S0, scale=1.0)
+    for h in range(Hv):
+        S = [[_frac(x) for x in row] for row in S0[0, h]]
+        for n in range(N):
+            S, o = _rational_step(S, [_frac(x) for x in q[0, n, 0]], [_frac(x) for x in k[0, n, 0]],
+                                  [_frac(x) for x in v[0, n, h]], _frac(alpha[0, n, h]),
+                                  _frac(beta[0, n, h]))
+            assert _close(res["nodes"][0, n, h], [[float(x) for x in r] for r in S], 1e-14)
+            assert _close(res["out"][0, n, h], [float(x) for x in o], 1e-14)
+        assert _close(res["final"][0, h], [[float(x) for x in r] for r in S], 1e-14)
+
+
+def _rand_inputs(seed, B=2, N=7, Hqk=2, Hv=4, dk=8, dv=6):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, N, Hqk, dk))
+    k = rng.standard_normal((B, N, Hqk, dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, N, Hv, dv))
+    alpha = np.exp(-np.logaddexp(0, rng.standard_normal((B, N, Hv))))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((B, N, Hv))))
+    S0 = 0.1 * rng.standard_normal((B, Hv, dv, dk))
+    return q, k, v, alpha, beta, S0
+
+
+def test_beta0_alpha1_keeps_state_and_reads_it(oracle_mod):
+    q, k, v, alpha, beta, S0 = _rand_inputs(1)
+    alpha[:] = 1.0
+    beta[:] = 0.0
+    res = oracle_mod.chain(q, k, v, alpha, beta, S0)
+    G = 2
+    for n in range(q.shape[1]):
+        assert np.array_equal(res["nodes"][:, n], S0)
+        for h in range(4):
+            np.testing.assert_allclose(res["out"][:, n, h], np.einsum("bji,bi->bj", S0[:, h], q[:, n, h // G]),
+                                       rtol=0, atol=1e-15)
+
+
+def test_beta0_is_pure_decay(oracle_mod):
+    q, k, v, alpha, beta, S0 = _rand_inputs(2)
+    beta[:] = 0.0
+    res = oracle_mod.chain(q, k, v, alpha, beta, S0)
+    decay = np.cumprod(alpha, axis=1)  # [B][N][Hv]
+    for n in range(q.shape[1]):
+        np.testing.assert_allclose(res["nodes"][:, n], decay[:, n, :, None, None] * S0, rtol=1e-14, atol=0)
+
+
+def test_alpha0_resets_and_output_reads_updated_state(oracle_mod):
+    q, k, v, alpha, beta, S0 = _rand_inputs(3)
+    alpha[:, 0] = 0.0
+    r1 = oracle_mod.chain(q, k, v, alpha, beta, S0)
+    r2 = oracle_mod.chain(q, k, v, alpha, beta, S0 * -3.0 + 1.0)
+    assert np.array_equal(r1["nodes"], r2["nodes"])
+    assert np.array_equal(r1["out"], r2["out"])
+    G = 2
+    for h in range(4):
+        kk = k[:, 0, h // G]
+        qq = q[:, 0, h // G]
+        expect_S = beta[:, 0, h, None, None] * v[:, 0, h, :, None] * kk[:, None, :]
+        np.testing.assert_allclose(r1["nodes"][:, 0, h], expect_S, rtol=0, atol=1e-15)
+        # o_0 = S_0 q_0 = beta v (k . q): only true if the output reads the updated state
+        expect_o = beta[:, 0, h, None] * v[:, 0, h] * np.sum(kk * qq, axis=-1)[:, None]
+        np.testing.assert_allclose(r1["out"][:, 0, h], expect_o, rtol=0, atol=1e-15)
+
+
+def test_delta_write_recovers_value(oracle_mod):
+    """beta = 1, alpha = 1, |k| = 1: after the step the state maps k to v."""
+    rng = np.random.default_rng(4)
+    for dk, dv in ((8, 8), (5, 9), (12, 3)):
+        S = rng.standard_normal((dv, dk))
+        k = rng.standard_normal(dk)
+        k /= np.linalg.norm(k)
+        v = rng.standard_normal(dv)
+        Sn, _ = oracle_mod.step(S, k, k, v, 1.0, 1.0)
+        np.testing.assert_allclose(Sn @ k, v, rtol=0, atol=1e-13)
+        # the part of S orthogonal to k is untouched
+        P = np.eye(dk) - np.outer(k, k)
+        np.testing.assert_allclose(Sn @ P, S @ P, rtol=0, atol=1e-13)
+
+
+def test_orthonormal_keys_replace_one_column(oracle_mod):
+    """k = e_i, alpha = beta = 1: column i of S becomes v, the rest stay."""
+    rng = np.random.default_rng(5)
+    dk, dv = 6, 5
+    S = rng.standard_normal((dv, dk))
+    for i in range(dk):
+        k = np.zeros(dk); k[i] = 1.0
+        v = rng.standard_normal(dv)
+        m = (i + 2) % dk
+        q = np.zeros(dk); q[m] = 1.0
+        Sn, o = oracle_mod.step(S, q, k, v, 1.0, 1.0)
+        expect = S.copy(); expect[:, i] = v
+        assert np.array_equal(Sn, expect)
+        assert np.array_equal(o, expect[:, m])
+        S = Sn
+
+
+def test_joint_linearity_in_state_and_values(oracle_mod):
+    q, k, v1, alpha, beta, S1 = _rand_inputs(6)
+    _, _, v2, _, _, S2 = _rand_inputs(7)
+    a, b = 0.7, -1.3
+    r1 = oracle_mod.chain(q, k, v1, alpha, beta, S1)
+    r2 = oracle_mod.chain(q, k, v2, alpha, beta, S2)
+    r = oracle_mod.chain(q, k, a * v1 + b * v2, alpha, beta, a * S1 + b * S2)
+    np.testing.assert_allclose(r["nodes"], a * r1["nodes"] + b * r2["nodes"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(r["out"], a * r1["out"] + b * r2["out"], rtol=0, atol=1e-13)
+
+
+def test_scale_scales_outputs_only(oracle_mod):
+    q, k, v, alpha, beta, S0 = _rand_inputs(8)
+    r1 = oracle_mod.chain(q, k, v, alpha, beta, S0, scale=1.0)
+    r2 = oracle_mod.chain(q, k, v, alpha, beta, S0, scale=0.125)
+    assert np.array_equal(r1["nodes"], r2["nodes"])
+    np.testing.assert_allclose(r2["out"], 0.125 * r1["out"], rtol=1e-15, atol=0)
+
+
+def test_gqa_value_head_reads_its_group(oracle_mod):
+    """Value head h uses q/k head h // (Hv/Hqk): changing q/k head 1 leaves heads 0, 1 alone."""
+    q, k, v, alpha, beta, S0 = _rand_inputs(9)
+    r1 = oracle_mod.chain(q, k, v, alpha, beta, S0)
+    q2, k2 = q.copy(), k.copy()
+    q2[:, :, 1] *= -0.5
+    k2[:, :, 1] = np.roll(k2[:, :, 1], 1, axis=-1)
+    r2 = oracle_mod.chain(q2, k2, v, alpha, beta, S0)
+    assert np.array_equal(r1["nodes"][:, :, :2], r2["nodes"][:, :, :2])
+    assert not np.allclose(r1["nodes"][:, :, 2:], r2["nodes"][:, :, 2:])
+
+
+def test_magnitude_bound(oracle_mod):
+    """||S_n||_2 <= alpha ||S_p||_2 + beta ||k|| ||v|| for |k| = 1, beta in [0, 1]."""
+    q, k, v, alpha, beta, S0 = _rand_inputs(10)
+    r = oracle_mod.chain(q, k, v, alpha, beta, S0)
+    G = 2
+    for b in range(q.shape[0]):
+        for h in range(4):
+            prev = S0[b, h]
+            for n in range(q.shape[1]):
+                cur = r["nodes"][b, n, h]
+                bound = alpha[b, n, h] * np.linalg.norm(prev, 2) + beta[b, n, h] * np.linalg.norm(v[b, n, h])
+                assert np.linalg.norm(cur, 2) <= bound * (1 + 1e-12)
+                prev = cur
+
+
+# --------------------------------------------------------------------------
+# trees
+# --------------------------------------------------------------------------
+def _path(parent, n):
+    p = []
+    while n >= 0:
+        p.append(n)
+        n = int(parent[n])
+    return p[::-1]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tree_node_equals_chain_over_its_root_path(oracle_mod, seed):
+    rng = np.random.default_rng(100 + seed)
+    N = 22
+    q, k, v, alpha, beta, S0 = _rand_inputs(20 + seed, B=2, N=N)
+    parent = wl.random_tree(N, 16, rng)
+    rt = oracle_mod.tree(q, k, v, alpha, beta, S0, parent)
+    for n in range(N):
+        path = _path(parent, n)
+        rc = oracle_mod.chain(q[:, path], k[:, path], v[:, path], alpha[:, path], beta[:, path], S0)
+        assert np.array_equal(rt["nodes"][:, n], rc["nodes"][:, -1])
+        assert np.array_equal(rt["out"][:, n], rc["out"][:, -1])
+
+
+def test_tree_non_ancestors_do_not_reach_a_node(oracle_mod):
+    rng = np.random.default_rng(200)
+    N = 22
+    q, k, v, alpha, beta, S0 = _rand_inputs(30, B=1, N=N)
+    parent = wl.random_tree(N, 16, rng)
+    base = oracle_mod.tree(q, k, v, alpha, beta, S0, parent)
+    for n in (5, 13, 21):
+        anc = set(_path(parent, n))
+        others = [m for m in range(N) if m not in anc]
+        q2, k2, v2, a2, b2 = q.copy(), k.copy(), v.copy(), alpha.copy(), beta.copy()
+        v2[:, others] += 3.0
+        a2[:, others] *= 0.5
+        b2[:, others] = 1.0 - b2[:, others]
+        k2[:, others] = -k2[:, others]
+        pert = oracle_mod.tree(q2, k2, v2, a2, b2, S0, parent)
+        assert np.array_equal(pert["nodes"][:, n], base["nodes"][:, n])
+        assert np.array_equal(pert["out"][:, n], base["out"][:, n])
+
+
+def test_tree_with_chain_parents_is_the_chain(oracle_mod):
+    q, k, v, alpha, beta, S0 = _rand_inputs(31)
+    N = q.shape[1]
+    rt = oracle_mod.tree(q, k, v, alpha, beta, S0, wl.chain_parent(N))
+    rc = oracle_mod.chain(q, k, v, alpha, beta, S0)
+    assert np.array_equal(rt["nodes"], rc["nodes"])
+    assert np.array_equal(rt["out"], rc["out"])
+
+
+def test_tree_per_sequence_parents(oracle_mod):
+    rng = np.random.default_rng(300)
+    N = 12
+    q, k, v, alpha, beta, S0 = _rand_inputs(32, B=3, N=N)
+    parents = np.stack([wl.random_tree(N, 16, rng) for _ in range(3)])
+    r = oracle_mod.tree(q, k, v, alpha, beta, S0, parents)
+    for b in range(3):
+        rb = oracle_mod.tree(q[b:b + 1], k[b:b + 1], v[b:b + 1], alpha[b:b + 1], beta[b:b + 1],
+                             S0[b:b + 1], parents[b])
+        assert np.array_equal(r["nodes"][b], rb["nodes"][0])
+
+
+def test_tree_rejects_bad_parent(oracle_mod):
+    q, k, v, alpha, beta, S0 = _rand_inputs(33, B=1, N=4)
+    with pytest.raises(ValueError):
+        oracle_mod.tree(q, k, v, alpha, beta, S0, np.array([-1, 0, 2, 1], np.int32))
+
+
+# --------------------------------------------------------------------------
+# chunked (WY / UT) form
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("C", [1, 2, 3, 7, 16, 64, 256])
+def test_chunked_equals_stepwise(oracle_mod, C):
+    q, k, v, alpha, beta, S0 = _rand_inputs(40, B=1, N=200, Hqk=1, Hv=2, dk=16, dv=24)
+    ref = oracle_mod.chain(q, k, v, alpha, beta, S0, nodes=False)
+    got = oracle_mod.chunked(q, k, v, alpha, beta, S0, chunk=C)
+    assert _close(got["out"], ref["out"], 1e-12)
+    assert _close(got["final"], ref["final"], 1e-12)
+
+
+def test_chunked_handles_zero_gates_exactly(oracle_mod):
+    q, k, v, alpha, beta, S0 = _rand_inputs(41, B=1, N=150, Hqk=1, Hv=2, dk=8, dv=8)
+    alpha[:, ::13] = 0.0
+    beta[:, 5::17] = 0.0
+    ref = oracle_mod.chain(q, k, v, alpha, beta, S0, nodes=False)
+    got = oracle_mod.chunked(q, k, v, alpha, beta, S0, chunk=16)
+    assert _close(got["out"], ref["out"], 1e-12)
+    assert _close(got["final"], ref["final"], 1e-12)
+
+
+def test_chunked_resume_equals_one_pass(oracle_mod):
+    q, k, v, alpha, beta, S0 = _rand_inputs(42, B=1, N=130, Hqk=1, Hv=2, dk=8, dv=8)
+    whole = oracle_mod.chunked(q, k, v, alpha, beta, S0, chunk=16)
+    t1 = 37
+    a = oracle_mod.chunked(q[:, :t1], k[:, :t1], v[:, :t1], alpha[:, :t1], beta[:, :t1], S0, chunk=16)
+    b = oracle_mod.chunked(q[:, t1:], k[:, t1:], v[:, t1:], alpha[:, t1:], beta[:, t1:], a["final"], chunk=16)
+    assert _close(np.concatenate([a["out"], b["out"]], axis=1), whole["out"], 1e-12)
+    assert _close(b["final"], whole["final"], 1e-12)
+
+
+def test_zero_length_chain_keeps_state(oracle_mod):
+    q, k, v, alpha, beta, S0 = _rand_inputs(43, B=2, N=0)
+    r = oracle_mod.chain(q, k, v, alpha, beta, S0)
+    assert np.array_equal(r["final"], S0)
+
+
+# --------------------------------------------------------------------------
+# commit
+# --------------------------------------------------------------------------
+def test_commit_definition(oracle_mod):
+    rng = np.random.default_rng(50)
+    B, N, Hv, dv, dk = 4, 5, 2, 3, 3
+    nodes = rng.standard_normal((B, N, Hv, dv, dk))
+    final = rng.standard_normal((B, Hv, dv, dk))
+    state = rng.standard_normal((6, Hv, dv, dk))
+    slots = np.array([5, 0, 3, 1], np.int32)
+    acc = np.array([0, N - 1, 7, 2], np.int32)
+    new, bad = oracle_mod.commit(state, nodes, acc, final=final, state_slot=slots)
+    assert bad == 1
+    assert np.array_equal(new[5], nodes[0, 0])
+    assert np.array_equal(new[0], final[1])
+    assert np.array_equal(new[3], state[3])      # rejected node index: untouched
+    assert np.array_equal(new[1], nodes[3, 2])
+    assert np.array_equal(new[2], state[2]) and np.array_equal(new[4], state[4])
+    new2, _ = oracle_mod.commit(state[:4], nodes, np.array([N - 1] * 4, np.int32))
+    assert np.array_equal(new2, nodes[:, N - 1])
