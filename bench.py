@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Throughput of the verify + commit step on one MI355X.
+
+One step = gdn_verify_chain over a 16-node draft (batch 1, 16 q/k heads,
+48 value heads, d_k = d_v = 128, bf16 q/k/v, fp32 state, f16 persisted node
+states, fp32 outputs and final state) followed by gdn_commit of a seeded
+accepted length.  The metric is verified draft tokens per second per GDN
+layer: 16 nodes per step per layer.
+
+Inputs are resident in device memory before the timed region.  Steps rotate
+over enough independent buffer sets (> 256 MB in total) that the 256 MB
+Infinity Cache cannot hold one step's data from the previous visit, so every
+step streams its state and writes its node states to HBM.
+
+Printed: one JSON line with the metric, the roofline of the verify kernel
+(algorithmic bytes per launch / average launch time from HIP events), the
+oracle timed on this host's cores, and secondary measurements of the tree
+and batched workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "verified draft tokens/s per GDN layer (48 v-heads, d=128) + % HBM roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev_set(torch, d, dev):
+    t = {n: torch.from_numpy(np.ascontiguousarray(d[n + "_bits"]).view(np.int16)).to(dev).view(torch.bfloat16)
+         for n in ("q", "k", "v")}
+    for n in ("alpha", "beta", "state0"):
+        t[n] = torch.from_numpy(np.ascontiguousarray(d[n])).to(dev)
+    t["accepted"] = torch.from_numpy(d["accepted"]).to(dev)
+    return t
+
+
+def make_sets(torch, wl, w, nsets, dev, tree=False):
+    sets = []
+    for i in range(nsets):
+        d = wl.make_inputs(w, seed=wl.WORKLOAD_SEEDS[w.name] + 7919 * i)
+        t = dev_set(torch, d, dev)
+        B, N = w.batch, w.n_nodes
+        t["out"] = torch.empty(B, N, w.h_v, w.d_v, device=dev)
+        t["persist"] = torch.empty(B, N, w.h_v, w.d_v, w.d_k, device=dev, dtype=torch.float16)
+        t["final"] = None if tree else torch.empty(B, w.h_v, w.d_v, w.d_k, device=dev)
+        t["parent"] = d["parent"]
+        sets.append(t)
+    return sets
+
+
+def time_steps(torch, sets, step_fn, kernel_fn, steps, warmup):
+    """Whole-step time (clean region) and verify-kernel time (events around
+    every verify launch, on the launching stream, over a second region)."""
+    for i in range(warmup):
+        step_fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step_fn(sets[i % len(sets)])
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        s = sets[i % len(sets)]
+        evs[i][0].record()
+        kernel_fn(s)
+        evs[i][1].record()
+        step_fn(s, verify=False)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return step_ms, kern_ms
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--sets", type=int, default=12, help="rotating buffer sets (chain and tree)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work of the oracle baseline")
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--skip-secondary", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: the path "
+              "has no cross-GPU step (each (sequence, head) recurrence is independent).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from gated_deltanet_recurrence_gdn_amd import binding as gb
+    from gated_deltanet_recurrence_gdn_amd import workloads as wl
+
+    gb.lib()
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS["chain"]
+    ledger = wl.algorithmic_bytes_verify(w)
+    sets = make_sets(torch, wl, w, args.sets, dev)
+    set_bytes = ledger["total"]
+    log(f"chain: {args.sets} buffer sets, {set_bytes * args.sets / 1e6:.0f} MB rotated")
+
+    def verify_fn(s):
+        gb.gdn_verify_chain(s["q"], s["k"], s["v"], s["alpha"], s["beta"], s["state0"], out=s["out"],
+                            persist=s["persist"], final_state=s["final"])
+
+    def step(s, verify=True):
+        if verify:
+            verify_fn(s)
+        gb.gdn_commit(s["accepted"], s["persist"], s["state0"], final_state=s["final"])
+
+    step_ms, kern_ms = time_steps(torch, sets, step, verify_fn, args.steps, args.warmup)
+    tokens_per_step = w.batch * w.n_nodes
+    value = tokens_per_step / (step_ms * 1e-3)
+    achieved = ledger["verify_total"] / (kern_ms * 1e-3) / 1e9
+    log(f"chain step {step_ms * 1e3:.2f} us, verify kernel {kern_ms * 1e3:.2f} us, {achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "chain verify + commit: batch 1, 16 q/k heads, 48 value heads, d_k=d_v=128, "
+                        "16-node draft, bf16 q/k/v, fp32 state, f16 persisted node states, fp32 outputs",
+            "batch": w.batch, "nodes": w.n_nodes, "h_qk": w.h_qk, "h_v": w.h_v, "d_k": w.d_k, "d_v": w.d_v,
+            "buffer_sets": args.sets, "rotated_bytes": set_bytes * args.sets,
+            "step_bytes": set_bytes, "step_hbm_gbs": set_bytes / (step_ms * 1e-3) / 1e9,
+            "step_hbm_frac": set_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        },
+        "roofline": {
+            "kernel": "verify_chain_kernel<128,1,f16 persist>",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": ledger["verify_total"],
+            "avg_launch_us": kern_ms * 1e3,
+        },
+    }
+    del sets
+    torch.cuda.empty_cache()
+
+    if not args.skip_secondary:
+        result["secondary"] = secondary(torch, gb, wl, dev, args)
+
+    if not args.skip_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl, w, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def secondary(torch, gb, wl, dev, args):
+    out = {}
+    # tree: 22 nodes, batch 1
+    w = wl.WORKLOADS["tree"]
+    led = wl.algorithmic_bytes_verify(w)
+    sets = make_sets(torch, wl, w, args.sets, dev, tree=True)
+
+    def tverify(s):
+        gb.gdn_verify_tree(s["parent"], s["q"], s["k"], s["v"], s["alpha"], s["beta"], s["state0"], out=s["out"],
+                           persist=s["persist"])
+
+    def tstep(s, verify=True):
+        if verify:
+            tverify(s)
+        gb.gdn_commit(s["accepted"], s["persist"], s["state0"])
+
+    sm, km = time_steps(torch, sets, tstep, tverify, args.steps, args.warmup)
+    out["tree"] = {"nodes_per_s_per_layer": w.n_nodes / (sm * 1e-3), "ms_per_step": sm, "verify_us": km * 1e3,
+                   "verify_gbs": led["verify_total"] / (km * 1e-3) / 1e9, "step_bytes": led["total"]}
+    log("tree", out["tree"])
+    del sets
+    torch.cuda.empty_cache()
+    # batched: 8 sequences x 48 layers in one launch
+    w = wl.WORKLOADS["batched_chain"]
+    led = wl.algorithmic_bytes_verify(w)
+    sets = make_sets(torch, wl, w, 1, dev)
+
+    def bverify(s):
+        gb.gdn_verify_chain(s["q"], s["k"], s["v"], s["alpha"], s["beta"], s["state0"], out=s["out"],
+                            persist=s["persist"], final_state=s["final"])
+
+    def bstep(s, verify=True):
+        if verify:
+            bverify(s)
+        gb.gdn_commit(s["accepted"], s["persist"], s["state0"], final_state=s["final"])
+
+    n = max(5, args.steps // 50)
+    sm, km = time_steps(torch, sets, bstep, bverify, n, max(2, args.warmup // 25))
+    out["batched_chain"] = {"tokens_per_s_per_layer": w.batch * w.n_nodes / (sm * 1e-3),
+                            "ms_per_step": sm, "verify_ms": km, "step_bytes": led["total"],
+                            "step_hbm_gbs": led["total"] / (sm * 1e-3) / 1e9,
+                            "verify_gbs": led["verify_total"] / (km * 1e-3) / 1e9,
+                            "commit_ms": sm - km}
+    log("batched_chain", out["batched_chain"])
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(wl, w, seconds):
+    import oracle
+
+    d = wl.make_inputs(w)
+    nthreads = oracle.default_threads()
+    args = [d[n].astype(np.float64) for n in ("q", "k", "v", "alpha", "beta", "state0")]
+    reps, t_total = 0, 0.0
+    while t_total < seconds or reps == 0:
+        t0 = time.perf_counter()
+        ref = oracle.chain(*args, nthreads=nthreads)
+        oracle.commit(args[5], ref["nodes"], d["accepted"], final=ref["final"])
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": w.batch * w.n_nodes * reps / t_total, "unit": "tokens/s/layer", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"{reps} repetitions of the full step on one input set of the same workload "
+                      f"(48 heads x 16 nodes, fp64, every node state kept, then the commit), {t_total:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,271 @@
+// abi.cpp -- the C entry points declared in gdn.h: host-side validation,
+// tree walk planning and launch configuration.  Every check runs before any
+// HIP call, so a rejected request enqueues nothing and touches no buffer.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+using namespace gdn;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_dtype(int32_t d) { return d == GDN_F32 || d == GDN_BF16 || d == GDN_F16; }
+
+// Checks shared by verify (chain and tree): sizes, dtypes, pointers.
+int check_verify(const gdn_shape* sh, const void* q, const void* k, const void* v, const float* alpha,
+                 const float* beta, const float* state, const int32_t* state_slot, const void* out,
+                 const void* persist, const float* final_state) {
+    if (sh == nullptr) return GDN_ERR_NULL;
+    if (sh->batch < 0 || sh->n_nodes < 1 || sh->n_nodes > GDN_MAX_NODES) return GDN_ERR_SHAPE;
+    if (sh->h_qk < 1 || sh->h_v < 1 || sh->h_v % sh->h_qk != 0) return GDN_ERR_SHAPE;
+    if (sh->d_k != 32 && sh->d_k != 64 && sh->d_k != 128) return GDN_ERR_SHAPE;
+    if (sh->d_v < 16 || sh->d_v > 256 || sh->d_v % 16 != 0) return GDN_ERR_SHAPE;
+    if (state_slot != nullptr && sh->n_slots < 1) return GDN_ERR_SHAPE;
+    if (!valid_dtype(sh->qkv_dtype) || !valid_dtype(sh->out_dtype) || !valid_dtype(sh->persist_dtype))
+        return GDN_ERR_DTYPE;
+    if (sh->qkv_dtype == GDN_F16) return GDN_ERR_DTYPE;
+    if (persist != nullptr && sh->persist_dtype == GDN_BF16) return GDN_ERR_DTYPE;
+    if (!std::isfinite(sh->scale)) return GDN_ERR_SHAPE;
+    if (sh->batch == 0) return GDN_OK;
+    if (!q || !k || !v || !alpha || !beta || !state) return GDN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state, 16)) return GDN_ERR_ALIGN;
+    if (!aligned(alpha, 4) || !aligned(beta, 4) || !aligned(state_slot, 4)) return GDN_ERR_ALIGN;
+    if (!aligned(out, 4) || !aligned(persist, 16) || !aligned(final_state, 16)) return GDN_ERR_ALIGN;
+    return GDN_OK;
+}
+
+struct VerifyPlan {
+    int m_groups, waves, rows_per_wg, slices;
+    size_t lds;
+};
+
+size_t stage_bytes(int n, int d_k, int rows) {
+    const int floats = (2 * n * d_k + n * rows + 3 * n + 3) & ~3;
+    return (size_t)floats * 4;
+}
+
+// Rows per wave R = m_groups * 512 / d_k.  Small problems take one row group
+// per wave (more waves in flight for a batch-1 step); large ones take two at
+// d_k = 128, halving the per-node LDS traffic of k and q per row.  Waves per
+// workgroup: the most (<= 4) that divide d_v and fit the LDS budget.
+int plan_verify(const gdn_shape* sh, int fork_slots, VerifyPlan* p) {
+    const int rpg = 512 / sh->d_k;
+    int m = 1;
+    const long long waves_m1 = (long long)sh->batch * sh->h_v * (sh->d_v / rpg);
+    if (sh->d_k == 128 && fork_slots == 0 && waves_m1 >= 16384 && sh->d_v % (2 * rpg) == 0) m = 2;
+    const int R = m * rpg;
+    if (sh->d_v % R != 0) return GDN_ERR_UNSUPPORTED;
+    for (int w = 4; w >= 1; w /= 2) {
+        if (sh->d_v % (w * R) != 0) continue;
+        const int rows = w * R;
+        const size_t lds = stage_bytes(sh->n_nodes, sh->d_k, rows) + (size_t)fork_slots * rows * sh->d_k * 4;
+        if (lds > (size_t)kMaxLdsBytes) continue;
+        p->m_groups = m;
+        p->waves = w;
+        p->rows_per_wg = rows;
+        p->slices = sh->d_v / rows;
+        p->lds = lds;
+        return GDN_OK;
+    }
+    return GDN_ERR_UNSUPPORTED;
+}
+
+VerifyArgs make_args(const gdn_shape* sh, const VerifyPlan& p, const void* q, const void* k, const void* v,
+                     const float* alpha, const float* beta, const float* state, const int32_t* state_slot,
+                     void* out, void* persist, float* final_state, int32_t* status) {
+    VerifyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state = state; a.state_slot = state_slot;
+    a.out = out; a.persist = persist; a.final_state = final_state; a.status = status;
+    a.seq0 = 0; a.n_seq = sh->batch; a.n_nodes = sh->n_nodes; a.h_qk = sh->h_qk; a.h_v = sh->h_v;
+    a.d_v = sh->d_v; a.n_slots = sh->n_slots; a.group = sh->h_v / sh->h_qk;
+    a.rows_per_wg = p.rows_per_wg; a.slices = p.slices;
+    a.qkv_bf16 = sh->qkv_dtype == GDN_BF16; a.out_dtype = sh->out_dtype;
+    a.fork_slots = 0; a.per_seq_tree = 0; a.scale = sh->scale;
+    return a;
+}
+
+int persist_mode(const gdn_shape* sh, const void* persist) {
+    if (persist == nullptr) return 0;
+    return sh->persist_dtype == GDN_F16 ? 1 : 2;
+}
+
+// Validate one parent array and write its depth-first walk.  Children are
+// visited in index order; a node with two or more children is saved to the
+// next free fork slot after it is computed and released when its last child
+// starts, so live slots form a stack along the current root path (at most
+// depth - 1 of them).
+int plan_tree(const int32_t* par, int n, uint16_t* walk, int* max_slots) {
+    int depth[GDN_MAX_NODES], nchild[GDN_MAX_NODES], started[GDN_MAX_NODES], slot_of[GDN_MAX_NODES];
+    int first_child[GDN_MAX_NODES], next_sib[GDN_MAX_NODES], last_child[GDN_MAX_NODES];
+    if (par[0] != -1) return GDN_ERR_PARENT;
+    for (int i = 0; i < n; ++i) {
+        nchild[i] = 0; started[i] = 0; slot_of[i] = -1; first_child[i] = -1; next_sib[i] = -1; last_child[i] = -1;
+    }
+    depth[0] = 1;
+    for (int i = 1; i < n; ++i) {
+        const int p = par[i];
+        if (p < 0 || p >= i) return GDN_ERR_PARENT;
+        depth[i] = depth[p] + 1;
+        if (depth[i] > GDN_MAX_TREE_DEPTH) return GDN_ERR_PARENT;
+        ++nchild[p];
+        if (first_child[p] < 0) first_child[p] = i; else next_sib[last_child[p]] = i;
+        last_child[p] = i;
+    }
+    int stack[GDN_MAX_NODES], sp = 0, top = 0, prev = -1, steps = 0;
+    stack[sp++] = 0;
+    while (sp > 0) {
+        const int x = stack[--sp];
+        uint16_t code = (uint16_t)x;
+        if (x != 0) {
+            const int p = par[x];
+            if (p != prev) {
+                if (slot_of[p] < 0 || slot_of[p] != top - 1) return GDN_ERR_PARENT;  // cannot happen
+                code |= kSchedRestore | (uint16_t)(slot_of[p] << 6);
+            }
+            if (++started[p] == nchild[p] && nchild[p] >= 2) { --top; slot_of[p] = -1; }
+        }
+        if (nchild[x] >= 2) {
+            if (top >= kMaxForkSlots) return GDN_ERR_PARENT;
+            slot_of[x] = top++;
+            code |= kSchedSave | (uint16_t)(slot_of[x] << 11);
+            if (top > *max_slots) *max_slots = top;
+        }
+        walk[steps++] = code;
+        prev = x;
+        // push children so the lowest index is visited first
+        int kids[GDN_MAX_NODES], nk = 0;
+        for (int c = first_child[x]; c >= 0; c = next_sib[c]) kids[nk++] = c;
+        for (int i = nk - 1; i >= 0; --i) stack[sp++] = kids[i];
+    }
+    return steps == n ? GDN_OK : GDN_ERR_PARENT;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case GDN_ERR_DTYPE: return "dtype not allowed here";
+        case GDN_ERR_ALIGN: return "pointer not aligned as required";
+        case GDN_ERR_PARENT: return "parent array is not a valid tree";
+        case GDN_ERR_NODE: return "accepted node out of range";
+        case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDN_ERR_UNSUPPORTED: return "request not supported by this build";
+        case GDN_ERR_HIP: return "HIP launch failed";
+        case GDN_ERR_SLOT: return "state slot out of range";
+        default: return "unknown status";
+    }
+}
+
+int gdn_tree_walk(const int32_t* parent, int32_t n_nodes, uint16_t* walk, int32_t* fork_slots) {
+    if (parent == nullptr || walk == nullptr || fork_slots == nullptr) return GDN_ERR_NULL;
+    if (n_nodes < 1 || n_nodes > GDN_MAX_NODES) return GDN_ERR_SHAPE;
+    int slots = 0;
+    const int rc = plan_tree(parent, n_nodes, walk, &slots);
+    *fork_slots = rc == GDN_OK ? slots : 0;
+    return rc;
+}
+
+int gdn_verify_chain(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                     const float* alpha, const float* beta, const float* state,
+                     const int32_t* state_slot, void* out, void* persist, float* final_state,
+                     int32_t* status, void* stream) {
+    int rc = check_verify(shape, q, k, v, alpha, beta, state, state_slot, out, persist, final_state);
+    if (rc != GDN_OK || shape->batch == 0) return rc;
+    if (final_state == state && state_slot != nullptr) return GDN_ERR_SHAPE;  // in-place needs slot = b
+    VerifyPlan p;
+    if ((rc = plan_verify(shape, 0, &p)) != GDN_OK) return rc;
+    VerifyArgs a = make_args(shape, p, q, k, v, alpha, beta, state, state_slot, out, persist, final_state, status);
+    const long long grid = (long long)shape->batch * shape->h_v * p.slices;
+    if (grid > 0x7fffffffLL) return GDN_ERR_SHAPE;
+    hipError_t e = launch_verify(a, nullptr, shape->d_k, p.m_groups, persist_mode(shape, persist), p.waves,
+                                 p.lds, (int)grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_verify_tree(const gdn_shape* shape, const int32_t* parent, int32_t n_trees, const void* q,
+                    const void* k, const void* v, const float* alpha, const float* beta,
+                    const float* state, const int32_t* state_slot, void* out, void* persist,
+                    int32_t* status, void* stream) {
+    int rc = check_verify(shape, q, k, v, alpha, beta, state, state_slot, out, persist, nullptr);
+    if (rc != GDN_OK) return rc;
+    if (parent == nullptr) return GDN_ERR_NULL;
+    const int B = shape->batch, N = shape->n_nodes;
+    if (!(n_trees == 1 || (n_trees == B && B > 0))) return GDN_ERR_SHAPE;
+    // validate every tree before anything is launched
+    int max_slots = 0;
+    uint16_t walk[GDN_MAX_NODES];
+    for (int t = 0; t < n_trees; ++t)
+        if ((rc = plan_tree(parent + (size_t)t * N, N, walk, &max_slots)) != GDN_OK) return rc;
+    if (B == 0) return GDN_OK;
+    VerifyPlan p;
+    if ((rc = plan_verify(shape, max_slots, &p)) != GDN_OK) return rc;
+    VerifyArgs a = make_args(shape, p, q, k, v, alpha, beta, state, state_slot, out, persist, nullptr, status);
+    a.fork_slots = max_slots;
+    const int pm = persist_mode(shape, persist);
+    TreeSched ts;
+    std::memset(&ts, 0, sizeof(ts));
+    if (n_trees == 1) {
+        plan_tree(parent, N, ts.step[0], &max_slots);
+        a.per_seq_tree = 0;
+        const long long grid = (long long)B * shape->h_v * p.slices;
+        if (grid > 0x7fffffffLL) return GDN_ERR_SHAPE;
+        hipError_t e = launch_verify(a, &ts, shape->d_k, p.m_groups, pm, p.waves, p.lds, (int)grid,
+                                     static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    }
+    // one tree per sequence: kTreesPerLaunch sequences per launch
+    a.per_seq_tree = 1;
+    for (int s0 = 0; s0 < B; s0 += kTreesPerLaunch) {
+        const int ns = (B - s0 < kTreesPerLaunch) ? (B - s0) : kTreesPerLaunch;
+        for (int t = 0; t < ns; ++t) plan_tree(parent + (size_t)(s0 + t) * N, N, ts.step[t], &max_slots);
+        a.seq0 = s0;
+        a.n_seq = ns;
+        const int grid = ns * shape->h_v * p.slices;
+        hipError_t e = launch_verify(a, &ts, shape->d_k, p.m_groups, pm, p.waves, p.lds, grid,
+                                     static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return GDN_ERR_HIP;
+    }
+    return GDN_OK;
+}
+
+int gdn_commit(const gdn_shape* shape, const int32_t* accepted_node, const void* persist,
+               const float* final_state, float* state, const int32_t* state_slot, int32_t* status,
+               void* stream) {
+    if (shape == nullptr) return GDN_ERR_NULL;
+    const gdn_shape* sh = shape;
+    if (sh->batch < 0 || sh->n_nodes < 1 || sh->n_nodes > GDN_MAX_NODES || sh->h_v < 1) return GDN_ERR_SHAPE;
+    if (sh->d_k != 32 && sh->d_k != 64 && sh->d_k != 128) return GDN_ERR_SHAPE;
+    if (sh->d_v < 16 || sh->d_v > 256 || sh->d_v % 16 != 0) return GDN_ERR_SHAPE;
+    if (state_slot != nullptr && sh->n_slots < 1) return GDN_ERR_SHAPE;
+    if (sh->persist_dtype != GDN_F16 && sh->persist_dtype != GDN_F32) return GDN_ERR_DTYPE;
+    if (sh->batch == 0) return GDN_OK;
+    if (!accepted_node || !persist || !state) return GDN_ERR_NULL;
+    if (!aligned(persist, 16) || !aligned(state, 16) || !aligned(final_state, 16)) return GDN_ERR_ALIGN;
+    if (!aligned(accepted_node, 4) || !aligned(state_slot, 4)) return GDN_ERR_ALIGN;
+    CommitArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.accepted = accepted_node; a.persist = persist; a.final_state = final_state; a.state = state;
+    a.state_slot = state_slot; a.status = status; a.batch = sh->batch; a.n_nodes = sh->n_nodes;
+    a.h_v = sh->h_v; a.head_elems = sh->d_v * sh->d_k; a.n_slots = sh->n_slots;
+    const int block = 256;
+    a.tiles_per_head = (a.head_elems / 8 + block - 1) / block;
+    const long long grid = (long long)sh->batch * sh->h_v * a.tiles_per_head;
+    if (grid > 0x7fffffffLL) return GDN_ERR_SHAPE;
+    hipError_t e = launch_commit(a, sh->persist_dtype == GDN_F16, (int)grid, block, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // extern "C"

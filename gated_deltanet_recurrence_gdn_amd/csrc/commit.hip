@@ -1,0 +1,74 @@
+// commit.hip -- copy the accepted node's state into the state cache (gfx950).
+//
+// Page "400 tok/s with Qwen3.5", section "Handling recurrent state": after
+// verification the recurrent state is set to the accepted boundary, and a
+// fully accepted block uses the verified state directly.  Here the boundary
+// state is the node's persisted copy (f16 widened exactly to fp32, or fp32),
+// or the exact fp32 final state when the whole chain was accepted.
+//
+// One workgroup covers 256 x 8 consecutive elements of one (sequence, head);
+// each lane moves one 16-byte f16 (or 32-byte fp32) vector and writes 32
+// bytes.  The accepted index and the slot are read per workgroup from device
+// memory, so no host synchronisation is needed between verify and commit.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+template <bool F16>
+__global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a) {
+    int blk = blockIdx.x;
+    const int tile = blk % a.tiles_per_head;
+    blk /= a.tiles_per_head;
+    const int h = blk % a.h_v;
+    const int b = blk / a.h_v;
+
+    const int acc = a.accepted[b];
+    if (acc < 0 || acc >= a.n_nodes) {
+        if (tile == 0 && h == 0 && threadIdx.x == 0 && a.status != nullptr) a.status[0] = GDN_ERR_NODE;
+        return;
+    }
+    int s = b;
+    if (a.state_slot != nullptr) {
+        s = a.state_slot[b];
+        if (s < 0 || s >= a.n_slots) {
+            if (tile == 0 && h == 0 && threadIdx.x == 0 && a.status != nullptr) a.status[0] = GDN_ERR_SLOT;
+            return;
+        }
+    }
+    const size_t e = ((size_t)tile * blockDim.x + threadIdx.x) * 8;
+    if (e >= (size_t)a.head_elems) return;
+    float* dst = a.state + ((size_t)s * a.h_v + h) * a.head_elems + e;
+    f32x4 x0, x1;
+    if (a.final_state != nullptr && acc == a.n_nodes - 1) {
+        const float* src = a.final_state + ((size_t)b * a.h_v + h) * a.head_elems + e;
+        x0 = *reinterpret_cast<const f32x4*>(src);
+        x1 = *reinterpret_cast<const f32x4*>(src + 4);
+    } else {
+        const size_t off = (((size_t)b * a.n_nodes + acc) * a.h_v + h) * a.head_elems + e;
+        if constexpr (F16) {
+            const f16x8 hv = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(a.persist) + off);
+            x0 = f32x4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};
+            x1 = f32x4{(float)hv[4], (float)hv[5], (float)hv[6], (float)hv[7]};
+        } else {
+            const float* src = static_cast<const float*>(a.persist) + off;
+            x0 = *reinterpret_cast<const f32x4*>(src);
+            x1 = *reinterpret_cast<const f32x4*>(src + 4);
+        }
+    }
+    *reinterpret_cast<f32x4*>(dst) = x0;
+    *reinterpret_cast<f32x4*>(dst + 4) = x1;
+}
+
+}  // namespace
+
+hipError_t launch_commit(const CommitArgs& a, bool persist_f16, int grid, int block, hipStream_t stream) {
+    if (persist_f16)
+        hipLaunchKernelGGL(commit_kernel<true>, dim3(grid), dim3(block), 0, stream, a);
+    else
+        hipLaunchKernelGGL(commit_kernel<false>, dim3(grid), dim3(block), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

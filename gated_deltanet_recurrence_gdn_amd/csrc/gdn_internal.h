@@ -1,0 +1,89 @@
+// gdn_internal.h -- kernel argument blocks and launch entry points shared by
+// the host dispatch (abi.cpp) and the gfx950 kernels (*.hip).  Internal to
+// the HIP library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+constexpr int kMaxNodes = GDN_MAX_NODES;
+constexpr int kTreesPerLaunch = 16;  // tree schedules carried in one kernarg block
+constexpr int kMaxForkSlots = GDN_MAX_TREE_DEPTH - 1;
+constexpr int kMaxLdsBytes = 64 * 1024;
+
+// One step of a tree walk (depth-first order), packed in 16 bits:
+//   bits 0-4   node index
+//   bit  5     restore the working state from fork slot (bits 6-9) first
+//   bit  10    after the node, save the working state to fork slot (bits 11-14)
+// Node 0 (the root) always comes first and starts from the cached state; a
+// step without the restore bit continues from the previous step's state.
+constexpr uint16_t kSchedRestore = 1u << 5;
+constexpr uint16_t kSchedSave = 1u << 10;
+__host__ __device__ constexpr int sched_node(uint16_t c) { return c & 31; }
+__host__ __device__ constexpr int sched_restore_slot(uint16_t c) { return (c >> 6) & 15; }
+__host__ __device__ constexpr int sched_save_slot(uint16_t c) { return (c >> 11) & 15; }
+
+struct VerifyArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    const float* state;
+    const int32_t* state_slot;
+    void* out;
+    void* persist;
+    float* final_state;
+    int32_t* status;
+    int32_t seq0;        // first sequence handled by this launch
+    int32_t n_seq;       // sequences handled by this launch
+    int32_t n_nodes;
+    int32_t h_qk;
+    int32_t h_v;
+    int32_t d_v;
+    int32_t n_slots;     // valid slot range when state_slot != nullptr
+    int32_t group;       // h_v / h_qk
+    int32_t rows_per_wg; // value rows of one head handled by one workgroup
+    int32_t slices;      // d_v / rows_per_wg
+    int32_t qkv_bf16;    // 1: q, k, v are bf16; 0: fp32
+    int32_t out_dtype;   // gdn_dtype
+    int32_t fork_slots;  // fork slots reserved in LDS (tree walks)
+    int32_t per_seq_tree;// 0: tree 0 for every sequence; 1: tree b - seq0
+    float scale;
+};
+
+// Depth-first walk of up to kTreesPerLaunch trees (tree launches only).
+struct TreeSched {
+    uint16_t step[kTreesPerLaunch][kMaxNodes];
+};
+
+struct CommitArgs {
+    const int32_t* accepted;
+    const void* persist;
+    const float* final_state;
+    float* state;
+    const int32_t* state_slot;
+    int32_t* status;
+    int32_t batch;
+    int32_t n_nodes;
+    int32_t h_v;
+    int32_t head_elems;     // d_v * d_k
+    int32_t tiles_per_head; // workgroups per (sequence, head)
+    int32_t n_slots;
+};
+
+// Verify kernel launch.  d_k selects the instantiation; m_groups is the number
+// of row groups each wave keeps (see verify.hip); persist_mode 0 = none,
+// 1 = f16, 2 = fp32; tree == nullptr launches the chain kernel.
+hipError_t launch_verify(const VerifyArgs& a, const TreeSched* tree, int d_k, int m_groups,
+                         int persist_mode, int waves_per_wg, size_t lds_bytes, int grid,
+                         hipStream_t stream);
+
+hipError_t launch_commit(const CommitArgs& a, bool persist_f16, int grid, int block,
+                         hipStream_t stream);
+
+}  // namespace gdn

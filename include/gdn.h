@@ -1,0 +1,163 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet recurrent-state library for MI355X
+ * (gfx950): speculative-draft verify over a chain or a tree, commit of the
+ * accepted node, and chunked prefill.
+ *
+ * The recurrence, per (sequence, value head), with S the d_v x d_k state:
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t                     (read after the update)
+ * This is the gated delta rule (Yang, Kautz, Hatamizadeh, "Gated Delta
+ * Networks: Improving Mamba2 with Delta Rule", ICLR 2025).  The pages
+ * describe the layer in words: page "LightSeek's TokenSpeed Hits 580 Tokens
+ * per Second on Qwen3.5's 400B Model", section "Why Qwen3.5 is hard to serve
+ * fast" (a fixed state of head-dimension-squared size per layer, updated per
+ * token, outputs read from the current state).
+ *
+ * Conventions for every entry point
+ *  - All tensors are dense, C-contiguous, in device memory, with these
+ *    layouts (B = shape.batch, N = shape.n_nodes):
+ *        q, k         [B][N][h_qk][d_k]      qkv_dtype (F32 or BF16)
+ *        v            [B][N][h_v][d_v]       qkv_dtype
+ *        alpha, beta  [B][N][h_v]            fp32
+ *        state        [n_slots][h_v][d_v][d_k] fp32   (row j = value channel j)
+ *        state_slot   [B] int32, nullable: sequence b uses state[state_slot[b]];
+ *                     NULL means sequence b uses state[b]
+ *        out          [B][N][h_v][d_v]       out_dtype (F32, F16 or BF16)
+ *        persist      [B][N][h_v][d_v][d_k]  persist_dtype (F16 or F32)
+ *        final_state  [B][h_v][d_v][d_k]     fp32
+ *    Value head h reads q/k head h / (h_v / h_qk).
+ *  - q, k, v, state, persist and final_state must be 16-byte aligned; the
+ *    other pointers 4-byte aligned.
+ *  - The caller owns every buffer.  The library allocates no memory, keeps no
+ *    mutable global state and is safe to call from several host threads.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work on it and return; they never synchronise the host.
+ *  - Errors found on the host (null or misaligned pointers, bad shapes or
+ *    dtypes, bad parent arrays, small workspace) return a negative
+ *    gdn_status before anything is enqueued; no buffer is touched.
+ *    Errors only the device can see (an out-of-range accepted node or state
+ *    slot) skip that sequence, leave its buffers untouched and store the
+ *    code into *status when `status` is not NULL.  The caller zeroes
+ *    *status beforehand; concurrent errors leave one of their codes.
+ *  - A failed kernel launch returns GDN_ERR_HIP.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_MAX_NODES 32      /* draft nodes per verify call (a 22-node tree plus margin) */
+#define GDN_MAX_TREE_DEPTH 16 /* nodes on a root-to-leaf path, root included */
+#define GDN_PREFILL_CHUNK 64  /* tokens per chunk of gdn_prefill_chunked */
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,        /* a required pointer is NULL */
+    GDN_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    GDN_ERR_DTYPE = -3,       /* a dtype code is not allowed where it was given */
+    GDN_ERR_ALIGN = -4,       /* a pointer is not aligned as required */
+    GDN_ERR_PARENT = -5,      /* the parent array is not a valid tree */
+    GDN_ERR_NODE = -6,        /* device: accepted node outside [0, N) */
+    GDN_ERR_WORKSPACE = -7,   /* workspace missing or too small */
+    GDN_ERR_UNSUPPORTED = -8, /* valid request this build does not implement */
+    GDN_ERR_HIP = -9,         /* the HIP runtime refused the launch */
+    GDN_ERR_SLOT = -10        /* device: state slot outside [0, n_slots) */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype;
+
+typedef struct gdn_shape {
+    int32_t batch;         /* independent sequences (or sequence x layer units), >= 0 */
+    int32_t n_nodes;       /* draft nodes per sequence; tokens per sequence for prefill */
+    int32_t h_qk;          /* q/k heads, >= 1 */
+    int32_t h_v;           /* value heads, a multiple of h_qk */
+    int32_t d_k;           /* key channels: 32, 64 or 128 */
+    int32_t d_v;           /* value channels: a multiple of 16, at most 256 */
+    int32_t n_slots;       /* rows of `state` when state_slot is given (ignored otherwise) */
+    int32_t qkv_dtype;     /* GDN_F32 or GDN_BF16 */
+    int32_t out_dtype;     /* GDN_F32, GDN_F16 or GDN_BF16 */
+    int32_t persist_dtype; /* GDN_F16 or GDN_F32 */
+    float scale;           /* output scale; 1 for the plain rule */
+} gdn_shape;
+
+/*
+ * Verify a causal chain of N draft nodes per sequence.
+ * Page "400 tok/s with Qwen3.5", sections "Speculative verification in a
+ * megakernel" and "Handling recurrent state": the target checks a block of
+ * draft tokens in one causal pass, keeping the recurrent working state on
+ * chip across the block.
+ *
+ * Node n of sequence b starts from node n-1 (node 0 from the cached state
+ * state[slot(b)], which is only read).  For every node the output goes to
+ * out (nullable) and the state after the node to persist (nullable), stored
+ * in persist_dtype with round-to-nearest-even: page "We got 207 tok/s with
+ * Qwen3.5-27B on an RTX 3090", section "Key wins" (an f16 per-node cache,
+ * written by the recurrence kernel itself).  The fp32 state after node N-1
+ * goes to final_state (nullable), exactly as computed.  final_state may be
+ * `state` itself (in-place advance) when state_slot is NULL.
+ */
+int gdn_verify_chain(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                     const float* alpha, const float* beta, const float* state,
+                     const int32_t* state_slot, void* out, void* persist, float* final_state,
+                     int32_t* status, void* stream);
+
+/*
+ * Verify a tree of N draft nodes per sequence.
+ * Page "Qwen3.6 27B: From 20 t/s to 184 t/s", section "Diffusion applied to
+ * text": a best-first tree of up to 22 nodes is verified in one target pass.
+ *
+ * `parent` is a HOST array of n_trees x N int32, n_trees = 1 (one tree for
+ * every sequence) or batch (one per sequence).  parent[0] = -1 (node 0, the
+ * root, starts from the cached state); for n >= 1, 0 <= parent[n] < n; no
+ * root-to-leaf path holds more than GDN_MAX_TREE_DEPTH nodes.  Node n starts
+ * from the exact fp32 state of node parent[n]; outputs and persisted states
+ * are indexed by node.  The array is read during the call only.
+ */
+int gdn_verify_tree(const gdn_shape* shape, const int32_t* parent, int32_t n_trees, const void* q,
+                    const void* k, const void* v, const float* alpha, const float* beta,
+                    const float* state, const int32_t* state_slot, void* out, void* persist,
+                    int32_t* status, void* stream);
+
+/*
+ * Commit the accepted node of every sequence into the state cache.
+ * Page "400 tok/s with Qwen3.5", section "Handling recurrent state": after a
+ * rejection the state is set to the accepted boundary; a fully accepted
+ * block uses the verified state directly.
+ *
+ * accepted_node is a DEVICE array [B] of node indices (node L-1 for an
+ * accepted chain prefix of length L; the last node of the accepted path in a
+ * tree).  state[slot(b)] <- persist[b][a] widened to fp32, or final_state[b]
+ * when final_state is not NULL and a = N-1.  Only shape.batch, n_nodes, h_v,
+ * d_k, d_v, n_slots and persist_dtype are read.  An accepted node outside
+ * [0, N) or a slot outside [0, n_slots) skips the sequence and sets *status.
+ */
+int gdn_commit(const gdn_shape* shape, const int32_t* accepted_node, const void* persist,
+               const float* final_state, float* state, const int32_t* state_slot,
+               int32_t* status, void* stream);
+
+/*
+ * Plan (and validate) the walk gdn_verify_tree takes through one tree.
+ * Host-only; enqueues nothing.  Writes n_nodes steps to `walk` (host,
+ * uint16 each): bits 0-4 the node, bit 5 "restore the parent's state from
+ * fork slot bits 6-9 first", bit 10 "save the state to fork slot bits 11-14
+ * after the node".  Nodes are visited depth first, children in index order;
+ * a step without bit 5 continues from the previous step's state (node 0 from
+ * the cached state).  *fork_slots receives the number of slots the walk
+ * needs (at most GDN_MAX_TREE_DEPTH - 1).  Returns GDN_ERR_PARENT for an
+ * invalid tree, with the rules of gdn_verify_tree.
+ */
+int gdn_tree_walk(const int32_t* parent, int32_t n_nodes, uint16_t* walk, int32_t* fork_slots);
+
+/* Human-readable name of a gdn_status code (static storage). */
+const char* gdn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

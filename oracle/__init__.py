@@ -62,6 +62,19 @@ def _load():
     return lib
 
 
+def default_threads() -> int:
+    """Worker threads for the oracle: the CPUs this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _threads(n: int) -> int:
+    return int(n) if n and n > 0 else default_threads()
+
+
 def _f64(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
 
@@ -112,7 +125,7 @@ def chain(q, k, v, alpha, beta, state0, scale: float = 1.0, nodes: bool = True,
     fin = np.zeros((B, Hv, dv, dk))
     rc = lib.oracle_gdn_chain(B, N, Hqk, Hv, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v),
                               _ptr(alpha), _ptr(beta), _ptr(state0), _ptr(out), _ptr(nd),
-                              _ptr(fin), int(nthreads))
+                              _ptr(fin), _threads(nthreads))
     _check(rc, "chain")
     return {"out": out, "nodes": nd, "final": fin}
 
@@ -135,7 +148,7 @@ def tree(q, k, v, alpha, beta, state0, parent, scale: float = 1.0, nodes: bool =
     nd = np.zeros((B, N, Hv, dv, dk)) if nodes else None
     rc = lib.oracle_gdn_tree(B, N, Hqk, Hv, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v),
                              _ptr(alpha), _ptr(beta), _ptr(state0),
-                             par.ctypes.data_as(_ip), _ptr(out), _ptr(nd), int(nthreads))
+                             par.ctypes.data_as(_ip), _ptr(out), _ptr(nd), _threads(nthreads))
     _check(rc, "tree")
     return {"out": out, "nodes": nd}
 
@@ -149,7 +162,7 @@ def chunked(q, k, v, alpha, beta, state0, chunk: int, scale: float = 1.0, nthrea
     fin = np.zeros((B, Hv, dv, dk))
     rc = lib.oracle_gdn_chunked(B, T, Hqk, Hv, dk, dv, float(scale), int(chunk), _ptr(q),
                                 _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state0),
-                                _ptr(out), _ptr(fin), int(nthreads))
+                                _ptr(out), _ptr(fin), _threads(nthreads))
     _check(rc, "chunked")
     return {"out": out, "final": fin}
 

@@ -1,0 +1,181 @@
+"""The C ABI on the host: the library loads, exports what include/gdn.h
+declares, and rejects bad requests before any HIP call (no GPU needed: every
+call here fails host validation or has batch 0, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gated_deltanet_recurrence_gdn_amd import binding as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")]
+
+FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced here
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(gdn_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    L = gb.lib()
+    names = declared_functions()
+    assert "gdn_verify_chain" in names and "gdn_commit" in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code, name in gb.STATUS.items():
+        s = gb.gdn_status_string(code)
+        assert isinstance(s, str) and s
+    assert gb.gdn_status_string(0) == "ok"
+    assert gb.gdn_status_string(12345) == "unknown status"
+
+
+def shape(**kw):
+    d = dict(batch=1, n_nodes=16, h_qk=16, h_v=48, d_k=128, d_v=128, n_slots=1, qkv_dtype=gb.GDN_BF16,
+             out_dtype=gb.GDN_F32, persist_dtype=gb.GDN_F16, scale=1.0)
+    d.update(kw)
+    return gb.GdnShape(*[d[f] for f, _ in gb.GdnShape._fields_])
+
+
+def chain(sh, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, st=FAKE, slot=None, out=FAKE, per=FAKE, fin=None):
+    return gb.lib().gdn_verify_chain(ctypes.byref(sh) if sh is not None else None, q, k, v, a, b, st, slot,
+                                     out, per, fin, None, None)
+
+
+def tree(sh, parent, n_trees=1, q=FAKE):
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    return gb.lib().gdn_verify_tree(ctypes.byref(sh), par.ctypes.data if par.size else None, n_trees, q, FAKE,
+                                    FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None)
+
+
+E = gb.CODES
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_nodes=0), "GDN_ERR_SHAPE"),
+    (dict(n_nodes=33), "GDN_ERR_SHAPE"),
+    (dict(batch=-1), "GDN_ERR_SHAPE"),
+    (dict(h_v=47), "GDN_ERR_SHAPE"),
+    (dict(h_qk=0), "GDN_ERR_SHAPE"),
+    (dict(d_k=96), "GDN_ERR_SHAPE"),
+    (dict(d_v=24), "GDN_ERR_SHAPE"),
+    (dict(d_v=512), "GDN_ERR_SHAPE"),
+    (dict(qkv_dtype=gb.GDN_F16), "GDN_ERR_DTYPE"),
+    (dict(qkv_dtype=7), "GDN_ERR_DTYPE"),
+    (dict(persist_dtype=gb.GDN_BF16), "GDN_ERR_DTYPE"),
+    (dict(scale=float("nan")), "GDN_ERR_SHAPE"),
+])
+def test_verify_chain_rejects_bad_shapes(kw, code):
+    assert chain(shape(**kw)) == E[code]
+
+
+def test_verify_chain_rejects_null_and_misaligned():
+    assert chain(None) == E["GDN_ERR_NULL"]
+    assert chain(shape(), q=None) == E["GDN_ERR_NULL"]
+    assert chain(shape(), st=None) == E["GDN_ERR_NULL"]
+    assert chain(shape(), q=FAKE + 2) == E["GDN_ERR_ALIGN"]
+    assert chain(shape(), per=FAKE + 8) == E["GDN_ERR_ALIGN"]
+    assert chain(shape(), a=FAKE + 2) == E["GDN_ERR_ALIGN"]
+    assert chain(shape(n_slots=0), slot=FAKE) == E["GDN_ERR_SHAPE"]
+    # in-place final state needs the identity slot map
+    assert chain(shape(), slot=FAKE, fin=FAKE) == E["GDN_ERR_SHAPE"]
+
+
+def test_batch_zero_is_a_no_op():
+    assert chain(shape(batch=0), q=None, k=None, v=None, a=None, b=None, st=None) == 0
+    assert tree(shape(batch=0, n_nodes=3), [-1, 0, 0]) == 0
+
+
+@pytest.mark.parametrize("parent", [
+    [0, 0, 1],            # root must be -1
+    [-1, 1, 0],           # parent[1] must be < 1
+    [-1, 0, 3, 1],        # parent after child
+    [-1, -1, 0],          # second root
+    [-1, 0, -2],          # negative
+    [-1] + list(range(16)),  # 17 nodes deep
+])
+def test_verify_tree_rejects_bad_parents(parent):
+    assert tree(shape(n_nodes=len(parent)), parent) == E["GDN_ERR_PARENT"]
+
+
+def test_verify_tree_rejects_bad_tree_count():
+    p = np.array([[-1, 0, 0], [-1, 0, 1]], np.int32)
+    assert tree(shape(batch=3, n_nodes=3), p, n_trees=2) == E["GDN_ERR_SHAPE"]
+    bad = np.array([[-1, 0, 0], [-1, 0, 2], [-1, 0, 1]], np.int32)
+    assert tree(shape(batch=3, n_nodes=3), bad, n_trees=3) == E["GDN_ERR_PARENT"]
+    assert gb.lib().gdn_verify_tree(ctypes.byref(shape(n_nodes=3)), None, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, None, FAKE, FAKE, None, None) == E["GDN_ERR_NULL"]
+
+
+def test_commit_rejects_bad_requests():
+    L = gb.lib()
+    c = lambda sh, acc=FAKE, per=FAKE, fin=None, st=FAKE, slot=None: L.gdn_commit(  # noqa: E731
+        ctypes.byref(sh) if sh is not None else None, acc, per, fin, st, slot, None, None)
+    assert c(None) == E["GDN_ERR_NULL"]
+    assert c(shape(), acc=None) == E["GDN_ERR_NULL"]
+    assert c(shape(), per=None) == E["GDN_ERR_NULL"]
+    assert c(shape(persist_dtype=gb.GDN_BF16)) == E["GDN_ERR_DTYPE"]
+    assert c(shape(n_nodes=40)) == E["GDN_ERR_SHAPE"]
+    assert c(shape(), st=FAKE + 4) == E["GDN_ERR_ALIGN"]
+    assert c(shape(), acc=FAKE + 1) == E["GDN_ERR_ALIGN"]
+    assert c(shape(batch=0), acc=None, per=None, st=None) == 0
+
+
+def simulate_walk(walk, parent):
+    """Replay a walk on symbolic states: each state is the node it came from."""
+    cur, slots, seen = -1, {}, []
+    for code in walk:
+        node = int(code) & 31
+        if code & (1 << 5):
+            cur = slots[(int(code) >> 6) & 15]
+        assert cur == parent[node], (node, cur, parent[node])
+        cur = node
+        if code & (1 << 10):
+            slots[(int(code) >> 11) & 15] = node
+        seen.append(node)
+    return seen
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_tree_walk_reaches_every_node_from_its_parent(seed):
+    from gated_deltanet_recurrence_gdn_amd import workloads as wl
+    rng = np.random.default_rng(seed)
+    for n in (1, 2, 5, 22, 32):
+        for _ in range(100):
+            parent = wl.random_tree(n, 16, rng)
+            walk, slots = gb.gdn_tree_walk(parent)
+            seen = simulate_walk(walk, parent)
+            assert sorted(seen) == list(range(n))
+            assert slots <= max(0, wl.tree_depths(parent).max() - 1)
+
+
+def test_tree_walk_of_a_chain_has_no_forks():
+    walk, slots = gb.gdn_tree_walk(np.arange(-1, 15, dtype=np.int32))
+    assert slots == 0 and list(walk) == list(range(16))
+
+
+def test_tree_walk_star_and_deep_fork():
+    star = np.array([-1] + [0] * 21, np.int32)
+    walk, slots = gb.gdn_tree_walk(star)
+    assert slots == 1 and simulate_walk(walk, star) == list(range(22))
+    # a 16-deep spine where every spine node also has a leaf: 15 live forks
+    par = [-1]
+    spine = [0]
+    for d in range(1, 16):
+        par.append(spine[-1]); spine.append(len(par) - 1)
+    for s in spine[:-1]:
+        par.append(s)
+    par = np.array(par, np.int32)
+    walk, slots = gb.gdn_tree_walk(par)
+    assert simulate_walk(walk, par) and slots <= 15

@@ -1,0 +1,352 @@
+"""GPU parity of chain / tree verify and commit against the fp64 oracle,
+through the C ABI.  Bar: max relative error (max |x - ref| / max |ref|) <= 2e-3
+for outputs and fp32 states, <= 1e-2 for persisted f16 states; index and copy
+handling bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_deltanet_recurrence_gdn_amd import binding as gb
+from gated_deltanet_recurrence_gdn_amd import workloads as wl
+from helpers import (DEV, OUT_TOL, PERSIST_TOL, STATE_TOL, alloc_outputs, dev_inputs, max_rel, run_chain,
+                     run_tree, say, small_inputs, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+def _commit(t_acc, persist, state, final=None, slot=None):
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gb.gdn_commit(t_acc, persist, state, final_state=final, state_slot=slot, status=status)
+    torch.cuda.synchronize()
+    return int(status.item())
+
+
+# --------------------------------------------------------------------------
+# the workloads at full size
+# --------------------------------------------------------------------------
+def test_tiny_chain_fp32_parity():
+    w = wl.WORKLOADS["tiny_chain"]
+    d = wl.make_inputs(w)
+    say("tiny_chain", w)
+    t = dev_inputs(d, bf16=False)
+    out, persist, fin = run_chain(t, w.n_nodes, persist_dtype=torch.float32)
+    ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"])
+    assert max_rel(to_host(out), ref["out"]) <= OUT_TOL
+    assert max_rel(to_host(fin), ref["final"]) <= STATE_TOL
+    assert max_rel(to_host(persist), ref["nodes"]) <= STATE_TOL
+    # fp32 throughout: far inside the bar
+    assert max_rel(to_host(out), ref["out"]) <= 1e-5
+
+
+def test_chain_parity_and_commit():
+    w = wl.WORKLOADS["chain"]
+    d = wl.make_inputs(w)
+    say("chain", w, "accepted", d["accepted"])
+    t = dev_inputs(d)
+    out, persist, fin = run_chain(t, w.n_nodes)
+    ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"])
+    e_out, e_fin, e_p = (max_rel(to_host(out), ref["out"]), max_rel(to_host(fin), ref["final"]),
+                         max_rel(to_host(persist), ref["nodes"]))
+    say(f"chain max-rel out {e_out:.2e} final {e_fin:.2e} persist {e_p:.2e}")
+    assert e_out <= OUT_TOL and e_fin <= STATE_TOL and e_p <= PERSIST_TOL
+    # commit at the drawn accepted length, and at full acceptance
+    for acc in (d["accepted"], np.array([w.n_nodes - 1], np.int32)):
+        state = t["state0"].clone()
+        assert _commit(torch.from_numpy(acc).to(DEV), persist, state, final=fin) == 0
+        a = int(acc[0])
+        expect = fin[0] if a == w.n_nodes - 1 else persist[0, a].float()
+        assert torch.equal(state[0], expect)
+        new, _ = oracle.commit(d["state0"].astype(np.float64), ref["nodes"], acc, final=ref["final"])
+        assert max_rel(to_host(state), new) <= STATE_TOL
+
+
+def test_tree_parity_and_commit():
+    w = wl.WORKLOADS["tree"]
+    d = wl.make_inputs(w)
+    say("tree", w, "parent", d["parent"].tolist(), "accepted", d["accepted"])
+    t = dev_inputs(d)
+    out, persist = run_tree(t, d["parent"], w.n_nodes)
+    ref = oracle.tree(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], d["parent"])
+    e_out, e_p = max_rel(to_host(out), ref["out"]), max_rel(to_host(persist), ref["nodes"])
+    say(f"tree max-rel out {e_out:.2e} persist {e_p:.2e}")
+    assert e_out <= OUT_TOL and e_p <= PERSIST_TOL
+    state = t["state0"].clone()
+    acc = d["accepted"]
+    assert _commit(torch.from_numpy(acc).to(DEV), persist, state) == 0
+    assert torch.equal(state[0], persist[0, int(acc[0])].float())
+    new, _ = oracle.commit(d["state0"].astype(np.float64), ref["nodes"], acc)
+    assert max_rel(to_host(state), new) <= STATE_TOL
+
+
+def test_batched_chain_full_size_sampled():
+    """8 sequences x 48 layers in one launch (the benchmark's configuration);
+    the oracle checks a sample of whole (sequence x layer) units."""
+    w = wl.WORKLOADS["batched_chain"]
+    d = wl.make_inputs(w)
+    say("batched_chain", w)
+    t = dev_inputs(d)
+    out, persist, fin = run_chain(t, w.n_nodes)
+    state = t["state0"].clone()
+    acc_t = torch.from_numpy(d["accepted"]).to(DEV)
+    assert _commit(acc_t, persist, state, final=fin) == 0
+    for b in (0, 1, 191, 250, w.batch - 1):
+        sl = slice(b, b + 1)
+        ref = oracle.chain(d["q"][sl], d["k"][sl], d["v"][sl], d["alpha"][sl], d["beta"][sl], d["state0"][sl])
+        e = (max_rel(to_host(out[sl]), ref["out"]), max_rel(to_host(fin[sl]), ref["final"]),
+             max_rel(to_host(persist[sl]), ref["nodes"]))
+        say(f"unit {b}: out {e[0]:.2e} final {e[1]:.2e} persist {e[2]:.2e}")
+        assert e[0] <= OUT_TOL and e[1] <= STATE_TOL and e[2] <= PERSIST_TOL
+        a = int(d["accepted"][b])
+        expect = fin[b] if a == w.n_nodes - 1 else persist[b, a].float()
+        assert torch.equal(state[b], expect)
+    # units not sampled: every committed state equals its source (bit-exact index work)
+    a = acc_t.long()
+    src = persist[torch.arange(w.batch, device=DEV), a].float()
+    full = a == w.n_nodes - 1
+    src[full] = fin[full]
+    assert torch.equal(state, src)
+
+
+# --------------------------------------------------------------------------
+# shapes, dtypes, options
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("B,N,Hqk,Hv,dk,dv", [
+    (3, 1, 2, 4, 64, 64),      # one node, odd batch
+    (2, 5, 1, 3, 32, 64),      # d_k != d_v, GQA 3
+    (1, 32, 4, 8, 128, 128),   # maximum nodes
+    (5, 16, 2, 2, 128, 32),    # d_v < d_k
+    (2, 7, 2, 4, 128, 256),    # d_v > d_k
+    (1, 16, 1, 1, 32, 16),     # smallest d_v
+])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_chain_shapes(B, N, Hqk, Hv, dk, dv, bf16):
+    w, d = small_inputs(11 + B + N + dk, B, N, Hqk, Hv, dk, dv, bf16=bf16)
+    say("chain shape", (B, N, Hqk, Hv, dk, dv), "bf16", bf16)
+    t = dev_inputs(d, bf16=bf16)
+    out, persist, fin = run_chain(t, N)
+    ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"])
+    assert max_rel(to_host(out), ref["out"]) <= OUT_TOL
+    assert max_rel(to_host(fin), ref["final"]) <= STATE_TOL
+    assert max_rel(to_host(persist), ref["nodes"]) <= PERSIST_TOL
+
+
+@pytest.mark.parametrize("out_dtype,persist_dtype", [(torch.float16, torch.float32), (torch.bfloat16, torch.float16)])
+def test_output_and_persist_dtypes(out_dtype, persist_dtype):
+    w, d = small_inputs(5, 2, 16, 2, 6, 128, 128)
+    t = dev_inputs(d)
+    out, persist, fin = run_chain(t, 16, persist_dtype=persist_dtype, out_dtype=out_dtype, scale=128 ** -0.5)
+    ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], scale=128 ** -0.5)
+    # bf16 outputs carry their own rounding (2^-9 relative); f16 2^-12
+    tol = 4e-3 if out_dtype == torch.bfloat16 else OUT_TOL
+    assert max_rel(to_host(out), ref["out"]) <= tol
+    assert max_rel(to_host(persist), ref["nodes"]) <= (STATE_TOL if persist_dtype == torch.float32 else PERSIST_TOL)
+    if persist_dtype == torch.float32:
+        assert torch.equal(persist[:, -1], fin)
+
+
+def test_optional_outputs_and_in_place_advance():
+    w, d = small_inputs(6, 3, 16, 2, 4, 128, 128)
+    t = dev_inputs(d)
+    ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"])
+    # only the final state, written over the input state (a plain advance)
+    state = t["state0"].clone()
+    gb.gdn_verify_chain(t["q"], t["k"], t["v"], t["alpha"], t["beta"], state, final_state=state)
+    torch.cuda.synchronize()
+    assert max_rel(to_host(state), ref["final"]) <= STATE_TOL
+    # outputs only
+    out = torch.zeros(3, 16, 4, 128, device=DEV)
+    gb.gdn_verify_chain(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["state0"], out=out)
+    torch.cuda.synchronize()
+    assert max_rel(to_host(out), ref["out"]) <= OUT_TOL
+
+
+def test_state_slots():
+    w, d = small_inputs(7, 4, 8, 1, 2, 64, 64)
+    t = dev_inputs(d)
+    n_slots = 9
+    slots = np.array([7, 2, 5, 0], np.int32)
+    pool = torch.randn(n_slots, 2, 64, 64, device=DEV)
+    pool[torch.from_numpy(slots).long()] = t["state0"]
+    slot_t = torch.from_numpy(slots).to(DEV)
+    out, persist, fin = run_chain(t, 8, state=pool, state_slot=slot_t)
+    ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"])
+    assert max_rel(to_host(out), ref["out"]) <= OUT_TOL
+    assert max_rel(to_host(fin), ref["final"]) <= STATE_TOL
+    before = pool.clone()
+    acc = torch.tensor([0, 7, 3, 5], dtype=torch.int32, device=DEV)
+    assert _commit(acc, persist, pool, final=fin, slot=slot_t) == 0
+    for b, s in enumerate(slots):
+        a = int(acc[b])
+        expect = fin[b] if a == 7 else persist[b, a].float()
+        assert torch.equal(pool[s], expect)
+    untouched = [s for s in range(n_slots) if s not in set(slots.tolist())]
+    assert torch.equal(pool[untouched], before[untouched])
+
+
+def test_per_sequence_trees_cross_launch_boundary():
+    rng = np.random.default_rng(77)
+    B, N = 21, 22  # more sequences than one launch carries
+    w, d = small_inputs(8, B, N, 2, 4, 128, 128, tree=True)
+    parents = np.stack([wl.random_tree(N, 16, rng) for _ in range(B)])
+    t = dev_inputs(d)
+    out, persist = run_tree(t, parents, N)
+    ref = oracle.tree(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], parents)
+    assert max_rel(to_host(out), ref["out"]) <= OUT_TOL
+    assert max_rel(to_host(persist), ref["nodes"]) <= PERSIST_TOL
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 64), (64, 32), (128, 128)])
+def test_tree_deep_forks(dk, dv):
+    """A 16-node spine with a leaf on every spine node: 15 live fork slots."""
+    par = [-1]
+    spine = [0]
+    for _ in range(15):
+        par.append(spine[-1]); spine.append(len(par) - 1)
+    for s in spine[:-1]:
+        par.append(s)
+    par = np.array(par, np.int32)
+    N = len(par)
+    w, d = small_inputs(9, 2, N, 1, 2, dk, dv, tree=True)
+    t = dev_inputs(d)
+    out, persist = run_tree(t, par, N, persist_dtype=torch.float32)
+    ref = oracle.tree(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], par)
+    assert max_rel(to_host(out), ref["out"]) <= OUT_TOL
+    assert max_rel(to_host(persist), ref["nodes"]) <= STATE_TOL
+
+
+# --------------------------------------------------------------------------
+# bit-exact properties of the GPU path
+# --------------------------------------------------------------------------
+def test_tree_node_equals_gpu_chain_over_its_path():
+    w = wl.WORKLOADS["tree"]
+    d = wl.make_inputs(w)
+    t = dev_inputs(d)
+    out, persist = run_tree(t, d["parent"], w.n_nodes, persist_dtype=torch.float32)
+    parent = d["parent"]
+    for n in range(w.n_nodes):
+        path = []
+        m = n
+        while m >= 0:
+            path.append(m); m = int(parent[m])
+        path = path[::-1]
+        idx = torch.tensor(path, device=DEV)
+        tp = {k_: (v_[:, idx].contiguous() if k_ != "state0" else v_) for k_, v_ in t.items()}
+        cout, cpersist, _ = run_chain(tp, len(path), persist_dtype=torch.float32, final=False)
+        assert torch.equal(persist[:, n], cpersist[:, -1]), n
+        assert torch.equal(out[:, n], cout[:, -1]), n
+
+
+def test_non_ancestor_inputs_do_not_reach_a_node():
+    w = wl.WORKLOADS["tree"]
+    d = wl.make_inputs(w)
+    t = dev_inputs(d)
+    out, persist = run_tree(t, d["parent"], w.n_nodes, persist_dtype=torch.float32)
+    n = w.n_nodes - 1
+    anc, m = set(), n
+    while m >= 0:
+        anc.add(m); m = int(d["parent"][m])
+    others = torch.tensor([i for i in range(w.n_nodes) if i not in anc], device=DEV)
+    t2 = {k_: v_.clone() for k_, v_ in t.items()}
+    t2["v"][:, others] = -t2["v"][:, others]
+    t2["alpha"][:, others] *= 0.5
+    t2["k"][:, others] = t2["k"][:, others].roll(1, dims=-1)
+    out2, persist2 = run_tree(t2, d["parent"], w.n_nodes, persist_dtype=torch.float32)
+    assert torch.equal(persist2[:, n], persist[:, n]) and torch.equal(out2[:, n], out[:, n])
+
+
+def test_identity_gates_keep_state_bitwise():
+    w, d = small_inputs(12, 2, 16, 2, 4, 128, 128)
+    t = dev_inputs(d)
+    t["alpha"].fill_(1.0)
+    t["beta"].fill_(0.0)
+    out, persist, fin = run_chain(t, 16, persist_dtype=torch.float32)
+    assert torch.equal(fin, t["state0"])
+    assert torch.equal(persist, t["state0"][:, None].expand_as(persist))
+    ref = oracle.chain(d["q"], d["k"], d["v"], np.ones_like(d["alpha"]), np.zeros_like(d["beta"]), d["state0"])
+    assert max_rel(to_host(out), ref["out"]) <= 1e-5
+
+
+def test_zero_decay_resets_bitwise():
+    w, d = small_inputs(13, 2, 16, 2, 4, 128, 128)
+    t = dev_inputs(d)
+    t["alpha"][:, 3] = 0.0
+    out1, p1, f1 = run_chain(t, 16, persist_dtype=torch.float32)
+    out2, p2, f2 = run_chain(t, 16, persist_dtype=torch.float32, state=t["state0"] * -2.5 + 0.25)
+    assert torch.equal(p1[:, 3:], p2[:, 3:]) and torch.equal(f1, f2) and torch.equal(out1[:, 3:], out2[:, 3:])
+    assert not torch.equal(p1[:, :3], p2[:, :3])
+
+
+def test_deterministic():
+    w = wl.WORKLOADS["chain"]
+    d = wl.make_inputs(w, seed=5)
+    t = dev_inputs(d)
+    a = run_chain(t, 16)
+    b = run_chain(t, 16)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+# --------------------------------------------------------------------------
+# device-side error handling, guard bands, streams
+# --------------------------------------------------------------------------
+def test_bad_slot_and_bad_node_skip_and_report():
+    w, d = small_inputs(14, 3, 8, 1, 2, 64, 64)
+    t = dev_inputs(d)
+    out, persist, fin = alloc_outputs(t, 8)
+    out.zero_(); persist.zero_(); fin.zero_()
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    slots = torch.tensor([0, 5, 2], dtype=torch.int32, device=DEV)  # 5 is outside 3 slots
+    gb.gdn_verify_chain(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["state0"], out=out, persist=persist,
+                        final_state=fin, state_slot=slots, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == gb.CODES["GDN_ERR_SLOT"]
+    assert torch.count_nonzero(out[1]) == 0 and torch.count_nonzero(persist[1]) == 0
+    assert torch.count_nonzero(out[0]) > 0 and torch.count_nonzero(out[2]) > 0
+    state = t["state0"].clone()
+    acc = torch.tensor([3, 8, -1], dtype=torch.int32, device=DEV)
+    assert _commit(acc, persist, state, final=fin) == gb.CODES["GDN_ERR_NODE"]
+    assert torch.equal(state[1], t["state0"][1]) and torch.equal(state[2], t["state0"][2])
+    assert torch.equal(state[0], persist[0, 3].float())
+
+
+def test_guard_bands_untouched():
+    B, N, Hqk, Hv, dk, dv = 3, 22, 2, 6, 128, 128
+    w, d = small_inputs(15, B, N, Hqk, Hv, dk, dv, tree=True)
+    t = dev_inputs(d)
+    pad = 4096
+
+    def guarded(shape, dtype):
+        n = int(np.prod(shape))
+        esz = torch.tensor([], dtype=dtype).element_size()
+        pe = pad // esz
+        buf = torch.full((n + 2 * pe,), 1234.5, dtype=dtype, device=DEV)
+        return buf, buf[pe:pe + n].view(shape), pe
+
+    ob, out, pe_o = guarded((B, N, Hv, dv), torch.float32)
+    pb, persist, pe_p = guarded((B, N, Hv, dv, dk), torch.float16)
+    fb, fin, pe_f = guarded((B, Hv, dv, dk), torch.float32)
+    gb.gdn_verify_chain(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["state0"], out=out, persist=persist,
+                        final_state=fin)
+    gb.gdn_verify_tree(d["parent"], t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["state0"], out=out,
+                       persist=persist)
+    sb, st, pe_s = guarded((B, Hv, dv, dk), torch.float32)
+    st.copy_(t["state0"])
+    gb.gdn_commit(torch.from_numpy(d["accepted"]).to(DEV), persist, st)
+    torch.cuda.synchronize()
+    for buf, pe in ((ob, pe_o), (pb, pe_p), (fb, pe_f), (sb, pe_s)):
+        assert bool((buf[:pe] == 1234.5).all()) and bool((buf[-pe:] == 1234.5).all())
+
+
+def test_runs_on_a_side_stream():
+    w, d = small_inputs(16, 2, 16, 2, 4, 128, 128)
+    t = dev_inputs(d)
+    ref_out, ref_p, ref_f = run_chain(t, 16)
+    s = torch.cuda.Stream()
+    out, persist, fin = alloc_outputs(t, 16)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        gb.gdn_verify_chain(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["state0"], out=out, persist=persist,
+                            final_state=fin)
+    s.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(persist, ref_p) and torch.equal(fin, ref_f)
