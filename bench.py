@@ -63,8 +63,12 @@ def make_sets(torch, wl, w, nsets, dev, tree=False):
 
 
 def time_steps(torch, sets, step_fn, kernel_fn, steps, warmup):
-    """Whole-step time (clean region) and verify-kernel time (events around
-    every verify launch, on the launching stream, over a second region)."""
+    """Whole-step time and verify-kernel time, both from HIP events on the
+    launching stream (torch's current stream).  The step region times K
+    verify + commit steps; the kernel region times K verify launches back to
+    back over the same rotating sets, so its per-launch average is the
+    kernel's duration including its launch and drain, as a kernel trace
+    reports it."""
     for i in range(warmup):
         step_fn(sets[i % len(sets)])
     torch.cuda.synchronize()
@@ -76,16 +80,12 @@ def time_steps(torch, sets, step_fn, kernel_fn, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
+    t0.record()
     for i in range(steps):
-        s = sets[i % len(sets)]
-        evs[i][0].record()
-        kernel_fn(s)
-        evs[i][1].record()
-        step_fn(s, verify=False)
+        kernel_fn(sets[i % len(sets)])
+    t1.record()
     torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kern_ms = t0.elapsed_time(t1) / steps
     return step_ms, kern_ms
 
 

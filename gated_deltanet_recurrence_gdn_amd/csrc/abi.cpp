@@ -46,8 +46,10 @@ struct VerifyPlan {
     size_t lds;
 };
 
+// LDS staging of one workgroup: k and q rows (fp32), per-node coefficients
+// (4 floats), beta * v for the workgroup's rows, and the tree walk.
 size_t stage_bytes(int n, int d_k, int rows) {
-    const int floats = (2 * n * d_k + n * rows + 3 * n + 3) & ~3;
+    const int floats = (2 * n * d_k + 4 * n + n * rows + n + 3) & ~3;
     return (size_t)floats * 4;
 }
 

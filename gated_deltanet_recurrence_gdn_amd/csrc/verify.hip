@@ -33,7 +33,43 @@
 namespace gdn {
 namespace {
 
-template <int DK, int M, bool TREE, int PMODE>
+// Output element store in the output dtype (OUT: 0 fp32, 1 bf16, 2 f16).
+template <int OUT>
+__device__ __forceinline__ void put_out(void* out, size_t idx, float o) {
+    if constexpr (OUT == 0) static_cast<float*>(out)[idx] = o;
+    else if constexpr (OUT == 2) static_cast<_Float16*>(out)[idx] = (_Float16)o;
+    else static_cast<uint16_t*>(out)[idx] = f32_to_bf16(o);
+}
+
+// Per-node operands a lane needs, read from LDS one node ahead of use.
+template <int M>
+struct NodeOps {
+    float k[8], q[8];
+    f32x4 coef;  // alpha, beta, q.k, unused
+    float vb[M]; // beta * v for this lane's rows
+};
+
+template <int DK, int M>
+__device__ __forceinline__ void read_node(NodeOps<M>& x, const float* kL, const float* qL, const f32x4* cL,
+                                          const float* vbL, int node, int c, int vr0, int rows) {
+    constexpr int RPG = 64 / (DK / 8);
+    const f32x4 k0 = *reinterpret_cast<const f32x4*>(kL + node * DK + 8 * c);
+    const f32x4 k1 = *reinterpret_cast<const f32x4*>(kL + node * DK + 8 * c + 4);
+    const f32x4 q0 = *reinterpret_cast<const f32x4*>(qL + node * DK + 8 * c);
+    const f32x4 q1 = *reinterpret_cast<const f32x4*>(qL + node * DK + 8 * c + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x.k[e] = k0[e];
+        x.k[4 + e] = k1[e];
+        x.q[e] = q0[e];
+        x.q[4 + e] = q1[e];
+    }
+    x.coef = cL[node];
+#pragma unroll
+    for (int m = 0; m < M; ++m) x.vb[m] = vbL[node * rows + vr0 + m * RPG];
+}
+
+template <int DK, int M, bool TREE, int PMODE, int OUT>
 __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t* walk) {
     constexpr int LPR = DK / 8;   // lanes per state row
     constexpr int RPG = 64 / LPR; // rows per row group
@@ -64,17 +100,17 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
         }
     }
 
-    // LDS: k[N][DK], q[N][DK], v[N][rows], alpha[N], beta[N], qk[N], fork slots.
+    // LDS: k[N][DK], q[N][DK] (fp32), coef[N] (alpha, beta, q.k), beta*v[N][rows],
+    // walk[N] (trees), then the fork slots.
     float* kL = lds;
     float* qL = kL + N * DK;
-    float* vL = qL + N * DK;
-    float* aL = vL + N * rows;
-    float* bL = aL + N;
-    float* qkL = bL + N;
-    const int stage_floats = (2 * N * DK + N * rows + 3 * N + 3) & ~3;
+    f32x4* cL = reinterpret_cast<f32x4*>(qL + N * DK);
+    float* vbL = reinterpret_cast<float*>(cL + N);
+    int* walkL = reinterpret_cast<int*>(vbL + N * rows);
+    const int stage_floats = (2 * N * DK + 4 * N + N * rows + N + 3) & ~3;
     float* forkL = lds + stage_floats;
 
-    // 1. this wave's state rows -> VGPRs (issued first; its latency overlaps staging)
+    // 1. this wave's state rows -> VGPRs (issued first; the loads overlap staging)
     const int c = lane % LPR, r = lane / LPR;
     const int wrow = wave * R;  // first row of this wave inside the slice
     const size_t head_elems = (size_t)DV * DK;
@@ -93,20 +129,35 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
         }
     }
 
-    // 2. stage k, q (as fp32) and q.k for every node
+    // 2. stage every node's inputs.  One pass issues all of a thread's global
+    //    loads (k and q chunks, beta * v, the gates) before any LDS store, so
+    //    the common case (N * d_k / 8 <= threads) costs one memory round trip.
     const bool bf16 = a.qkv_bf16 != 0;
-    const int chunks = N * LPR;  // 8-element chunks per tensor
-    for (int base = wave * 64; base < chunks; base += nthr) {
+    const int chunks = N * LPR;  // 8-element chunks of k (and of q)
+    const int nvb = N * rows;
+    const int items = chunks > nvb ? chunks : nvb;
+    for (int base = wave * 64; base < items; base += nthr) {
         const int e = base + lane;
-        float part = 0.f;
-        if (e < chunks) {
-            const int n = e / LPR, cc = e % LPR;
-            const size_t src = (((size_t)b * N + n) * a.h_qk + g) * DK + 8 * cc;
-            float kf[8], qf[8];
+        float kf[8], qf[8], vv = 0.f, vbeta = 0.f, ga = 0.f, gb = 0.f;
+        const bool has_kq = e < chunks, has_v = e < nvb, has_g = e < N;
+        if (has_kq) {
+            const size_t src = (((size_t)b * N + e / LPR) * a.h_qk + g) * DK + 8 * (e % LPR);
             load8_as_f32(a.k, src, bf16, kf);
             load8_as_f32(a.q, src, bf16, qf);
-            float* kd = kL + n * DK + 8 * cc;
-            float* qd = qL + n * DK + 8 * cc;
+        }
+        if (has_v) {
+            const int n = e / rows, j = e % rows;
+            vv = load1_as_f32(a.v, (((size_t)b * N + n) * a.h_v + h) * DV + row0 + j, bf16);
+            vbeta = a.beta[((size_t)b * N + n) * a.h_v + h];
+        }
+        if (has_g) {
+            ga = a.alpha[((size_t)b * N + e) * a.h_v + h];
+            gb = a.beta[((size_t)b * N + e) * a.h_v + h];
+        }
+        float part = 0.f;
+        if (has_kq) {
+            float* kd = kL + (e / LPR) * DK + 8 * (e % LPR);
+            float* qd = qL + (e / LPR) * DK + 8 * (e % LPR);
             *reinterpret_cast<f32x4*>(kd) = f32x4{kf[0], kf[1], kf[2], kf[3]};
             *reinterpret_cast<f32x4*>(kd + 4) = f32x4{kf[4], kf[5], kf[6], kf[7]};
             *reinterpret_cast<f32x4*>(qd) = f32x4{qf[0], qf[1], qf[2], qf[3]};
@@ -115,32 +166,32 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
             for (int i = 0; i < 8; ++i) part = fmaf(kf[i], qf[i], part);
         }
         part = group_sum<LPR>(part);
-        if (e < chunks && (e % LPR) == 0) qkL[e / LPR] = part;
-    }
-    // this slice of v, and the gates
-    for (int e = tid; e < N * rows; e += nthr) {
-        const int n = e / rows, j = e % rows;
-        vL[e] = load1_as_f32(a.v, (((size_t)b * N + n) * a.h_v + h) * DV + row0 + j, bf16);
-    }
-    for (int n = tid; n < N; n += nthr) {
-        aL[n] = a.alpha[((size_t)b * N + n) * a.h_v + h];
-        bL[n] = a.beta[((size_t)b * N + n) * a.h_v + h];
+        if (has_kq && (e % LPR) == 0) reinterpret_cast<float*>(cL + e / LPR)[2] = part;
+        if (has_v) vbL[e] = vbeta * vv;
+        if (has_g) {
+            reinterpret_cast<float*>(cL + e)[0] = ga;
+            reinterpret_cast<float*>(cL + e)[1] = gb;
+            if constexpr (TREE) walkL[e] = walk[e];
+        }
     }
     __syncthreads();
 
-    // 3. node loop: reductions, update, persist, output
+    // 3. node loop: reductions, update, persist, output; next node's operands
+    //    are read from LDS while the current node computes.
     const size_t node_elems = (size_t)a.h_v * head_elems;  // persist elements per node
     const size_t prow = (size_t)h * head_elems + (size_t)(row0 + wrow + r) * DK + 8 * c;
     const int fork_stride = nwaves * R * DK;
     float* myfork = forkL + wrow * DK;
-    for (int st = 0; st < N; ++st) {
-        int node = st;
-        uint16_t code = 0;
+    const float scale = a.scale;
+    const int vr0 = wrow + r;  // this lane's first row inside the slice
+
+    // One node: optional fork restore, the two row reductions, the update,
+    // the persisted copy, the output, optional fork save.
+    auto step = [&](const NodeOps<M>& x, int code) {
+        const int node = sched_node((uint16_t)code);
         if constexpr (TREE) {
-            code = walk[st];
-            node = sched_node(code);
             if (code & kSchedRestore) {
-                const float* src = myfork + sched_restore_slot(code) * fork_stride;
+                const float* src = myfork + sched_restore_slot((uint16_t)code) * fork_stride;
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (m * 64 + lane) * 8);
@@ -153,38 +204,29 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
                 }
             }
         }
-        float kf[8], qf[8];
-        {
-            const f32x4 k0 = *reinterpret_cast<const f32x4*>(kL + node * DK + 8 * c);
-            const f32x4 k1 = *reinterpret_cast<const f32x4*>(kL + node * DK + 8 * c + 4);
-            const f32x4 q0 = *reinterpret_cast<const f32x4*>(qL + node * DK + 8 * c);
-            const f32x4 q1 = *reinterpret_cast<const f32x4*>(qL + node * DK + 8 * c + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kf[e] = k0[e];
-                kf[4 + e] = k1[e];
-                qf[e] = q0[e];
-                qf[4 + e] = q1[e];
-            }
-        }
-        const float al = aL[node], be = bL[node], qk = qkL[node];
+        const float al = x.coef[0];
+        const float bal = x.coef[1] * al;     // beta * alpha
+        const float sal = scale * al;         // scale * alpha
+        const float sqk = scale * x.coef[2];  // scale * (q . k)
         const size_t nbase = ((size_t)b * N + node);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            float pk = 0.f, pq = 0.f;
+            // two accumulators per product halve the dependent FMA chain
+            float pk0 = S[m][0] * x.k[0], pk1 = S[m][1] * x.k[1];
+            float pq0 = S[m][0] * x.q[0], pq1 = S[m][1] * x.q[1];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pk = fmaf(S[m][e], kf[e], pk);
-                pq = fmaf(S[m][e], qf[e], pq);
+            for (int e = 2; e < 8; e += 2) {
+                pk0 = fmaf(S[m][e], x.k[e], pk0);
+                pk1 = fmaf(S[m][e + 1], x.k[e + 1], pk1);
+                pq0 = fmaf(S[m][e], x.q[e], pq0);
+                pq1 = fmaf(S[m][e + 1], x.q[e + 1], pq1);
             }
-            pk = group_sum<LPR>(pk);
-            pq = group_sum<LPR>(pq);
-            const int vr = wrow + m * RPG + r;  // row inside the slice
-            const float vj = vL[node * rows + vr];
-            const float u = be * (vj - al * pk);
-            const float o = a.scale * (al * pq + qk * u);
+            const float pk = group_sum<LPR>(pk0 + pk1);
+            const float pq = group_sum<LPR>(pq0 + pq1);
+            const float u = fmaf(-bal, pk, x.vb[m]);  // beta (v - alpha S k)
+            const float o = fmaf(sal, pq, sqk * u);   // scale (alpha S q + (q.k) u)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) S[m][e] = fmaf(al, S[m][e], u * kf[e]);
+            for (int e = 0; e < 8; ++e) S[m][e] = fmaf(al, S[m][e], u * x.k[e]);
             if constexpr (PMODE == 1) {
                 f16x8 hv;
 #pragma unroll
@@ -197,11 +239,11 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
                 *reinterpret_cast<f32x4*>(dst + 4) = f32x4{S[m][4], S[m][5], S[m][6], S[m][7]};
             }
             if (a.out != nullptr && c == 0)
-                store_out(a.out, (nbase * a.h_v + h) * DV + row0 + vr, o, a.out_dtype);
+                put_out<OUT>(a.out, (nbase * a.h_v + h) * DV + row0 + vr0 + m * RPG, o);
         }
         if constexpr (TREE) {
             if (code & kSchedSave) {
-                float* dst = myfork + sched_save_slot(code) * fork_stride;
+                float* dst = myfork + sched_save_slot((uint16_t)code) * fork_stride;
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     *reinterpret_cast<f32x4*>(dst + (m * 64 + lane) * 8) = f32x4{S[m][0], S[m][1], S[m][2], S[m][3]};
@@ -209,6 +251,22 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
                 }
             }
         }
+    };
+    auto code_at = [&](int st) { return TREE ? walkL[st < N ? st : N - 1] : (st < N ? st : N - 1); };
+
+    // Two operand buffers in ping-pong: while one node computes, the next
+    // node's operands are already on their way from LDS.
+    NodeOps<M> opA, opB;
+    int codeA = code_at(0), codeB;
+    read_node<DK, M>(opA, kL, qL, cL, vbL, sched_node((uint16_t)codeA), c, vr0, rows);
+    for (int st = 0; st < N; st += 2) {
+        codeB = code_at(st + 1);
+        read_node<DK, M>(opB, kL, qL, cL, vbL, sched_node((uint16_t)codeB), c, vr0, rows);
+        step(opA, codeA);
+        if (st + 1 >= N) break;
+        codeA = code_at(st + 2);
+        read_node<DK, M>(opA, kL, qL, cL, vbL, sched_node((uint16_t)codeA), c, vr0, rows);
+        step(opB, codeB);
     }
 
     // 4. final state (chains): the exact fp32 state after node N-1
@@ -225,25 +283,34 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
     }
 }
 
-template <int DK, int M, int PMODE>
+template <int DK, int M, int PMODE, int OUT>
 __global__ __launch_bounds__(256) void verify_chain_kernel(const VerifyArgs a) {
-    verify_body<DK, M, false, PMODE>(a, nullptr);
+    verify_body<DK, M, false, PMODE, OUT>(a, nullptr);
 }
 
-template <int DK, int M, int PMODE>
+template <int DK, int M, int PMODE, int OUT>
 __global__ __launch_bounds__(256) void verify_tree_kernel(const VerifyArgs a, const TreeSched t) {
     const int bl = xcd_logical_block(blockIdx.x, gridDim.x) / (a.slices * a.h_v);
-    verify_body<DK, M, true, PMODE>(a, t.step[a.per_seq_tree ? bl : 0]);
+    verify_body<DK, M, true, PMODE, OUT>(a, t.step[a.per_seq_tree ? bl : 0]);
+}
+
+template <int DK, int M, int PMODE, int OUT>
+hipError_t launch_one(const VerifyArgs& a, const TreeSched* t, int waves, size_t lds, int grid, hipStream_t st) {
+    if (t != nullptr)
+        hipLaunchKernelGGL((verify_tree_kernel<DK, M, PMODE, OUT>), dim3(grid), dim3(64 * waves), lds, st, a, *t);
+    else
+        hipLaunchKernelGGL((verify_chain_kernel<DK, M, PMODE, OUT>), dim3(grid), dim3(64 * waves), lds, st, a);
+    return hipGetLastError();
 }
 
 template <int DK, int M, int PMODE>
-hipError_t launch_dkmp(const VerifyArgs& a, const TreeSched* t, int waves, size_t lds, int grid,
-                       hipStream_t st) {
-    if (t != nullptr)
-        hipLaunchKernelGGL((verify_tree_kernel<DK, M, PMODE>), dim3(grid), dim3(64 * waves), lds, st, a, *t);
-    else
-        hipLaunchKernelGGL((verify_chain_kernel<DK, M, PMODE>), dim3(grid), dim3(64 * waves), lds, st, a);
-    return hipGetLastError();
+hipError_t launch_dkmp(const VerifyArgs& a, const TreeSched* t, int waves, size_t lds, int grid, hipStream_t st) {
+    switch (a.out_dtype) {
+        case GDN_F32: return launch_one<DK, M, PMODE, 0>(a, t, waves, lds, grid, st);
+        case GDN_BF16: return launch_one<DK, M, PMODE, 1>(a, t, waves, lds, grid, st);
+        case GDN_F16: return launch_one<DK, M, PMODE, 2>(a, t, waves, lds, grid, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int DK, int M>
