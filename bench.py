@@ -225,7 +225,55 @@ def secondary(torch, gb, wl, dev, args):
     log("batched_chain", out["batched_chain"])
     del sets
     torch.cuda.empty_cache()
+    out["prefill"] = bench_prefill(torch, gb, wl, dev, max(5, args.steps // 25))
+    log("prefill", out["prefill"])
     return out
+
+
+def prefill_flops(w) -> float:
+    """Algorithmic matrix FLOPs of the chunked form (full C x C tiles): per
+    (chunk, value head) W, U', W H, Q H, P U, K^T U; per (chunk, q/k head)
+    K K^T and Q K^T."""
+    C, dk, dv = w.chunk, w.d_k, w.d_v
+    nch = (w.n_nodes + C - 1) // C
+    per_vh = 2 * C * C * dk + 2 * C * C * dv + 3 * 2 * C * dk * dv + 2 * C * C * dv
+    per_qk = 2 * 2 * C * C * dk
+    return float(w.batch * nch * (w.h_v * per_vh + w.h_qk * per_qk))
+
+
+def bench_prefill(torch, gb, wl, dev, reps):
+    w = wl.WORKLOADS["prefill"]
+    d = wl.make_inputs(w)
+    t = dev_set(torch, d, dev)
+    out = torch.empty(w.batch, w.n_nodes, w.h_v, w.d_v, device=dev, dtype=torch.float16)
+    st = t["state0"].clone()
+
+    def run():
+        st.copy_(t["state0"])
+        gb.gdn_prefill_chunked(t["q"], t["k"], t["v"], t["alpha"], t["beta"], st, out)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    copy_ms = 0.0
+    t0.record()
+    for _ in range(reps):
+        st.copy_(t["state0"])
+    t1.record()
+    torch.cuda.synchronize()
+    copy_ms = t0.elapsed_time(t1) / reps
+    t0.record()
+    for _ in range(reps):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps - copy_ms
+    fl = prefill_flops(w)
+    return {"ms": ms, "tokens_per_s": w.batch * w.n_nodes / (ms * 1e-3), "algorithmic_gflop": fl / 1e9,
+            "tflops": fl / (ms * 1e-3) / 1e12, "mfma_frac_f16_peak": fl / (ms * 1e-3) / 2.5e15,
+            "out_dtype": "f16"}
 
 
 def cpu_baseline(wl, w, seconds):

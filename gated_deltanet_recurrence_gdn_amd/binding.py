@@ -50,6 +50,8 @@ _SIGS = {
     "gdn_commit": [ctypes.POINTER(GdnShape)] + [_vp] * 7,
     "gdn_status_string": [ctypes.c_int],
     "gdn_tree_walk": [_vp, ctypes.c_int32, _vp, _vp],
+    "gdn_prefill_workspace_bytes": [ctypes.POINTER(GdnShape)],
+    "gdn_prefill_chunked": [ctypes.POINTER(GdnShape)] + [_vp] * 9 + [ctypes.c_size_t, _vp, _vp],
 }
 
 
@@ -64,7 +66,8 @@ def lib() -> ctypes.CDLL:
         for name, args in _SIGS.items():
             fn = getattr(L, name)
             fn.argtypes = args
-            fn.restype = ctypes.c_char_p if name == "gdn_status_string" else ctypes.c_int
+            fn.restype = {"gdn_status_string": ctypes.c_char_p,
+                          "gdn_prefill_workspace_bytes": ctypes.c_size_t}.get(name, ctypes.c_int)
         _lib = L
     return _lib
 
@@ -170,3 +173,35 @@ def gdn_commit(accepted_node, persist, state, *, final_state=None, state_slot=No
                           _dev_ptr(state, "state"), _dev_ptr(state_slot, "state_slot"),
                           _dev_ptr(status, "status"), _stream(stream))
     _check(rc, "gdn_commit")
+
+
+def _prefill_shape(q, v, state, out, scale) -> GdnShape:
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    return GdnShape(B, T, Hqk, Hv, dk, dv, state.shape[0], _dtype_code(q), _dtype_code(out), GDN_F16,
+                    float(scale))
+
+
+def gdn_prefill_workspace_bytes(q, v, state, out, scale: float = 1.0) -> int:
+    sh = _prefill_shape(q, v, state, out, scale)
+    return int(lib().gdn_prefill_workspace_bytes(ctypes.byref(sh)))
+
+
+def gdn_prefill_chunked(q, k, v, alpha, beta, state, out, *, state_slot=None, status=None, workspace=None,
+                        scale: float = 1.0, stream=None) -> None:
+    """Chunked prefill; ``state`` is updated in place (see include/gdn.h).
+
+    ``workspace`` is a device tensor of at least gdn_prefill_workspace_bytes
+    bytes; when omitted one is allocated here with torch (plumbing only).
+    """
+    sh = _prefill_shape(q, v, state, out, scale)
+    if workspace is None:
+        need = int(lib().gdn_prefill_workspace_bytes(ctypes.byref(sh)))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().gdn_prefill_chunked(ctypes.byref(sh), _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                   _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"), _dev_ptr(state, "state"),
+                                   _dev_ptr(state_slot, "state_slot"), _dev_ptr(out, "out"),
+                                   _dev_ptr(workspace, "workspace"), ws_bytes, _dev_ptr(status, "status"),
+                                   _stream(stream))
+    _check(rc, "gdn_prefill_chunked")

@@ -270,4 +270,50 @@ int gdn_commit(const gdn_shape* shape, const int32_t* accepted_node, const void*
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+namespace {
+int check_prefill(const gdn_shape* sh) {
+    if (sh == nullptr) return GDN_ERR_NULL;
+    if (sh->batch < 0 || sh->n_nodes < 0) return GDN_ERR_SHAPE;
+    if (sh->h_qk < 1 || sh->h_v < 1 || sh->h_v % sh->h_qk != 0) return GDN_ERR_SHAPE;
+    if (sh->d_k != 32 && sh->d_k != 64 && sh->d_k != 128) return GDN_ERR_SHAPE;
+    if (sh->d_v < 32 || sh->d_v > 256 || sh->d_v % 32 != 0) return GDN_ERR_SHAPE;
+    if (sh->qkv_dtype != GDN_F32 && sh->qkv_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (!valid_dtype(sh->out_dtype)) return GDN_ERR_DTYPE;
+    if (!std::isfinite(sh->scale)) return GDN_ERR_SHAPE;
+    return GDN_OK;
+}
+}  // namespace
+
+size_t gdn_prefill_workspace_bytes(const gdn_shape* shape) {
+    if (check_prefill(shape) != GDN_OK || shape->batch == 0 || shape->n_nodes == 0) return 0;
+    return prefill_workspace_bytes(shape->batch, shape->n_nodes, shape->h_qk, shape->h_v, shape->d_k);
+}
+
+int gdn_prefill_chunked(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, float* state, const int32_t* state_slot,
+                        void* out, void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
+    int rc = check_prefill(shape);
+    if (rc != GDN_OK) return rc;
+    const gdn_shape* sh = shape;
+    if (state_slot != nullptr && sh->n_slots < 1) return GDN_ERR_SHAPE;
+    if (sh->batch == 0 || sh->n_nodes == 0) return GDN_OK;
+    if (!q || !k || !v || !alpha || !beta || !state || !out) return GDN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return GDN_ERR_ALIGN;
+    if (!aligned(alpha, 4) || !aligned(beta, 4) || !aligned(state, 4) || !aligned(out, 4) ||
+        !aligned(state_slot, 4))
+        return GDN_ERR_ALIGN;
+    const size_t need = prefill_workspace_bytes(sh->batch, sh->n_nodes, sh->h_qk, sh->h_v, sh->d_k);
+    if (workspace == nullptr || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return GDN_ERR_ALIGN;
+    PrefillArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.workspace = workspace;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state = state; a.state_slot = state_slot;
+    a.out = out; a.status = status; a.batch = sh->batch; a.T = sh->n_nodes; a.h_qk = sh->h_qk; a.h_v = sh->h_v;
+    a.d_v = sh->d_v; a.group = sh->h_v / sh->h_qk; a.slices = sh->d_v / 32; a.n_slots = sh->n_slots;
+    a.qkv_bf16 = sh->qkv_dtype == GDN_BF16; a.scale = sh->scale;
+    hipError_t e = launch_prefill(a, sh->d_k, sh->out_dtype, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 }  // extern "C"

@@ -76,12 +76,41 @@ struct CommitArgs {
     int32_t n_slots;
 };
 
+struct PrefillArgs {
+    void* workspace; // see prefill_workspace_bytes
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    float* state;
+    const int32_t* state_slot;
+    void* out;
+    int32_t* status;
+    int32_t batch;
+    int32_t T;       // tokens per sequence
+    int32_t h_qk;
+    int32_t h_v;
+    int32_t d_v;
+    int32_t group;   // h_v / h_qk
+    int32_t slices;  // d_v / 32 (value columns per workgroup)
+    int32_t n_slots;
+    int32_t qkv_bf16;
+    float scale;
+};
+
 // Verify kernel launch.  d_k selects the instantiation; m_groups is the number
 // of row groups each wave keeps (see verify.hip); persist_mode 0 = none,
 // 1 = f16, 2 = fp32; tree == nullptr launches the chain kernel.
 hipError_t launch_verify(const VerifyArgs& a, const TreeSched* tree, int d_k, int m_groups,
                          int persist_mode, int waves_per_wg, size_t lds_bytes, int grid,
                          hipStream_t stream);
+
+// Chunked prefill: a parallel prepare kernel per (sequence, chunk, value head)
+// writes the state-independent chunk operands to the workspace; a scan kernel
+// per (sequence, value head, 32 value columns) then walks the chunks.
+size_t prefill_workspace_bytes(int batch, int T, int h_qk, int h_v, int d_k);
+hipError_t launch_prefill(const PrefillArgs& a, int d_k, int out_dtype, hipStream_t stream);
 
 hipError_t launch_commit(const CommitArgs& a, bool persist_f16, int grid, int block,
                          hipStream_t stream);

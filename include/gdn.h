@@ -141,6 +141,38 @@ int gdn_commit(const gdn_shape* shape, const int32_t* accepted_node, const void*
                int32_t* status, void* stream);
 
 /*
+ * Chunked prefill of a prompt: the same recurrence over shape.n_nodes = T
+ * tokens per sequence, evaluated GDN_PREFILL_CHUNK tokens at a time in the
+ * WY / UT form.  Page "We got 207 tok/s with Qwen3.5-27B on an RTX 3090",
+ * section "Prefill" (prompts are processed in micro-batches of tokens); the
+ * chunk algebra is derived from the rule (see the kernel source).
+ *
+ * q, k [B][T][h_qk][d_k], v [B][T][h_v][d_v] (qkv_dtype F32 or BF16; values
+ * are converted to f16 for the matrix cores, so they must lie inside the f16
+ * range, and magnitudes below 2^-14 keep an absolute precision of 2^-25);
+ * alpha, beta [B][T][h_v] fp32; out [B][T][h_v][d_v] in out_dtype (F32, F16
+ * or BF16).  state[slot(b)] holds the initial state on entry and the state
+ * after token T-1 on return (updated in place).  A zero alpha resets the state
+ * up to a factor e^-80 (the log-gate is clamped at -80).  d_k must be 32, 64 or
+ * 128 and d_v a multiple of 32.  persist_dtype is ignored.  T = 0 or batch = 0
+ * is a no-op.
+ *
+ * `workspace` is caller-owned device memory of at least
+ * gdn_prefill_workspace_bytes(shape) bytes (16-byte aligned), used during the
+ * call for the per-chunk operands that do not depend on the state (the UT
+ * transform and masked Q K^T per chunk and value head in f16, the gate factors,
+ * K^T per chunk and q/k head); about 1 MB per 64 tokens at 48 value heads and
+ * d_k = 128.  Its contents on entry are ignored.  A missing or short workspace
+ * returns GDN_ERR_WORKSPACE.  Calls sharing one workspace must be ordered on
+ * one stream.
+ */
+size_t gdn_prefill_workspace_bytes(const gdn_shape* shape);
+int gdn_prefill_chunked(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, float* state,
+                        const int32_t* state_slot, void* out, void* workspace,
+                        size_t workspace_bytes, int32_t* status, void* stream);
+
+/*
  * Plan (and validate) the walk gdn_verify_tree takes through one tree.
  * Host-only; enqueues nothing.  Writes n_nodes steps to `walk` (host,
  * uint16 each): bits 0-4 the node, bit 5 "restore the parent's state from

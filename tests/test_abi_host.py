@@ -179,3 +179,28 @@ def test_tree_walk_star_and_deep_fork():
     par = np.array(par, np.int32)
     walk, slots = gb.gdn_tree_walk(par)
     assert simulate_walk(walk, par) and slots <= 15
+
+
+def prefill(sh, q=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 40, st=FAKE):
+    return gb.lib().gdn_prefill_chunked(ctypes.byref(sh) if sh is not None else None, q, FAKE, FAKE, FAKE, FAKE,
+                                        st, None, out, ws, ws_bytes, None, None)
+
+
+def test_prefill_rejects_bad_requests():
+    P = dict(n_nodes=4096, d_k=128, d_v=128)
+    assert prefill(None) == E["GDN_ERR_NULL"]
+    assert prefill(shape(**{**P, "d_v": 48})) == E["GDN_ERR_SHAPE"]
+    assert prefill(shape(**{**P, "d_k": 96})) == E["GDN_ERR_SHAPE"]
+    assert prefill(shape(**{**P, "h_v": 47})) == E["GDN_ERR_SHAPE"]
+    assert prefill(shape(**{**P, "qkv_dtype": gb.GDN_F16})) == E["GDN_ERR_DTYPE"]
+    assert prefill(shape(**P), q=None) == E["GDN_ERR_NULL"]
+    assert prefill(shape(**P), out=None) == E["GDN_ERR_NULL"]
+    assert prefill(shape(**P), q=FAKE + 4) == E["GDN_ERR_ALIGN"]
+    assert prefill(shape(**P), ws=None) == E["GDN_ERR_WORKSPACE"]
+    sh = shape(**P)
+    need = gb.lib().gdn_prefill_workspace_bytes(ctypes.byref(sh))
+    # 64 chunks x (48 heads x (T + P) f16 + 48 x 3 x 64 fp32 gates + 16 q/k heads x K^T f16)
+    assert need == 64 * (48 * 2 * 64 * 64 * 2 + 48 * 3 * 64 * 4 + 16 * 128 * 64 * 2)
+    assert prefill(sh, ws_bytes=need - 1) == E["GDN_ERR_WORKSPACE"]
+    assert prefill(shape(**{**P, "n_nodes": 0}), q=None, ws=None) == 0
+    assert prefill(shape(**{**P, "batch": 0}), q=None, ws=None) == 0

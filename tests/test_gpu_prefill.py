@@ -1,0 +1,158 @@
+"""GPU parity of the chunked prefill against the stepwise fp64 oracle,
+through the C ABI.  Bar: max relative error <= 2e-3 on outputs and on the
+final fp32 state."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_deltanet_recurrence_gdn_amd import binding as gb
+from gated_deltanet_recurrence_gdn_amd import workloads as wl
+from helpers import DEV, OUT_TOL, STATE_TOL, dev_inputs, max_rel, say, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(t, out_dtype=torch.float32, scale=1.0, state=None, **kw):
+    B, T, _, _ = t["q"].shape
+    Hv, dv = t["v"].shape[2], t["v"].shape[3]
+    st = (t["state0"] if state is None else state).clone()
+    out = torch.full((B, T, Hv, dv), float("nan"), dtype=out_dtype, device=DEV)
+    gb.gdn_prefill_chunked(t["q"], t["k"], t["v"], t["alpha"], t["beta"], st, out, scale=scale, **kw)
+    torch.cuda.synchronize()
+    return out, st
+
+
+def sub_inputs(d, heads, G):
+    """Inputs restricted to value heads `heads` (consecutive group members kept with their q/k head)."""
+    qk = sorted({h // G for h in heads})
+    hv = [h for h in heads]
+    e = {}
+    for n in ("q", "k"):
+        e[n] = d[n][:, :, qk]
+    e["v"] = d["v"][:, :, hv]
+    for n in ("alpha", "beta"):
+        e[n] = d[n][:, :, hv]
+    e["state0"] = d["state0"][:, hv]
+    return e
+
+
+def test_prefill_full_size_sampled_heads():
+    w = wl.WORKLOADS["prefill"]
+    d = wl.make_inputs(w)
+    say("prefill", w)
+    t = dev_inputs(d)
+    out, st = run_prefill(t)
+    G = w.h_v // w.h_qk
+    for h in (0, 1, 2, 22, 47):
+        e = sub_inputs(d, [h], G)
+        # one value head reading its own q/k head
+        ref = oracle.chain(e["q"], e["k"], e["v"], e["alpha"], e["beta"], e["state0"], nodes=False)
+        eo = max_rel(to_host(out[:, :, h:h + 1]), ref["out"])
+        ef = max_rel(to_host(st[:, h:h + 1]), ref["final"])
+        say(f"head {h}: out {eo:.2e} final {ef:.2e}")
+        assert eo <= OUT_TOL and ef <= STATE_TOL
+
+
+@pytest.mark.parametrize("B,T,Hqk,Hv,dk,dv", [
+    (1, 1, 1, 1, 128, 32),
+    (1, 63, 1, 2, 128, 64),
+    (2, 64, 2, 4, 128, 128),
+    (1, 65, 1, 1, 64, 32),
+    (3, 200, 1, 3, 32, 64),
+    (1, 130, 2, 2, 64, 96),
+    (1, 300, 1, 1, 128, 256),
+])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_prefill_shapes_and_ragged_tails(B, T, Hqk, Hv, dk, dv, bf16):
+    w = wl.Workload("custom", B, T, Hqk, Hv, dk, dv, qkv_bf16=bf16)
+    d = wl.make_inputs(w, seed=T + dk + dv)
+    say("prefill shape", (B, T, Hqk, Hv, dk, dv), "bf16", bf16)
+    t = dev_inputs(d, bf16=bf16)
+    out, st = run_prefill(t)
+    ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], nodes=False)
+    assert max_rel(to_host(out), ref["out"]) <= OUT_TOL
+    assert max_rel(to_host(st), ref["final"]) <= STATE_TOL
+
+
+def test_prefill_resume_equals_one_pass():
+    w = wl.Workload("custom", 1, 257, 2, 4, 128, 64)
+    d = wl.make_inputs(w, seed=3)
+    t = dev_inputs(d)
+    whole_out, whole_st = run_prefill(t)
+    t1 = 100  # not a chunk multiple
+    a = {n: (x[:, :t1].contiguous() if n != "state0" else x) for n, x in t.items()}
+    o1, s1 = run_prefill(a)
+    b = {n: (x[:, t1:].contiguous() if n != "state0" else x) for n, x in t.items()}
+    o2, s2 = run_prefill(b, state=s1)
+    ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], nodes=False)
+    assert max_rel(to_host(torch.cat([o1, o2], dim=1)), ref["out"]) <= OUT_TOL
+    assert max_rel(to_host(s2), ref["final"]) <= STATE_TOL
+    assert max_rel(to_host(s2), to_host(whole_st)) <= STATE_TOL
+
+
+def test_prefill_f16_output_scale_and_zero_gates():
+    w = wl.Workload("custom", 1, 192, 2, 6, 128, 128)
+    d = wl.make_inputs(w, seed=4)
+    d["alpha"][:, 70] = 0.0   # a reset inside a chunk
+    d["alpha"][:, 128] = 0.0  # a reset at a chunk start
+    d["beta"][:, 5:9] = 0.0
+    t = dev_inputs(d)
+    sc = 128 ** -0.5
+    out, st = run_prefill(t, out_dtype=torch.float16, scale=sc)
+    ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], scale=sc, nodes=False)
+    assert max_rel(to_host(out), ref["out"]) <= OUT_TOL
+    assert max_rel(to_host(st), ref["final"]) <= STATE_TOL
+
+
+def test_prefill_state_slots_and_guard_bands():
+    w = wl.Workload("custom", 3, 100, 1, 2, 64, 64)
+    d = wl.make_inputs(w, seed=5)
+    t = dev_inputs(d)
+    slots = torch.tensor([4, 0, 2], dtype=torch.int32, device=DEV)
+    pool = torch.randn(6, 2, 64, 64, device=DEV)
+    pool[slots.long()] = t["state0"]
+    before = pool.clone()
+    pad = 1024
+    buf = torch.full((3 * 100 * 2 * 64 + 2 * pad,), 7.25, device=DEV)
+    out = buf[pad:pad + 3 * 100 * 2 * 64].view(3, 100, 2, 64)
+    gb.gdn_prefill_chunked(t["q"], t["k"], t["v"], t["alpha"], t["beta"], pool, out, state_slot=slots)
+    torch.cuda.synchronize()
+    ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], nodes=False)
+    assert max_rel(to_host(out), ref["out"]) <= OUT_TOL
+    assert max_rel(to_host(pool[slots.long()]), ref["final"]) <= STATE_TOL
+    assert torch.equal(pool[[1, 3, 5]], before[[1, 3, 5]])
+    assert bool((buf[:pad] == 7.25).all()) and bool((buf[-pad:] == 7.25).all())
+
+
+def test_prefill_bad_slot_reports_and_skips():
+    w = wl.Workload("custom", 2, 70, 1, 1, 32, 32)
+    d = wl.make_inputs(w, seed=6)
+    t = dev_inputs(d)
+    st = t["state0"].clone()
+    out = torch.zeros(2, 70, 1, 32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gb.gdn_prefill_chunked(t["q"], t["k"], t["v"], t["alpha"], t["beta"], st, out,
+                           state_slot=torch.tensor([1, 9], dtype=torch.int32, device=DEV), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == gb.CODES["GDN_ERR_SLOT"]
+    assert torch.count_nonzero(out[1]) == 0 and torch.equal(st[0], t["state0"][0])
+
+
+def test_prefill_deterministic_and_workspace():
+    w = wl.Workload("custom", 1, 128, 1, 3, 128, 128)
+    d = wl.make_inputs(w, seed=7)
+    t = dev_inputs(d)
+    a = run_prefill(t)
+    b = run_prefill(t)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    need = gb.gdn_prefill_workspace_bytes(t["q"], t["v"], t["state0"], a[0])
+    # 2 chunks x (3 heads x (T + P) f16 + 3 heads x gates + 1 q/k head x K^T f16)
+    assert need == 2 * (3 * 2 * 64 * 64 * 2 + 3 * 3 * 64 * 4 + 128 * 64 * 2)
+    # a caller-provided workspace with stale contents gives the same result
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
+    c = run_prefill(t, workspace=ws)
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+    with pytest.raises(gb.GdnError) as ei:
+        run_prefill(t, workspace=ws[:need - 16])
+    assert ei.value.code == gb.CODES["GDN_ERR_WORKSPACE"]
