@@ -32,6 +32,34 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+VERIFY_SOURCES = ["gated_deltanet_recurrence_gdn_amd/csrc/verify.hip",
+                  "gated_deltanet_recurrence_gdn_amd/csrc/gdn_device.h",
+                  "gated_deltanet_recurrence_gdn_amd/csrc/gdn_internal.h"]
+
+
+def source_sha(paths) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str, sha: str):
+    """HBM bytes per launch of a kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known size), or None
+    when there is none for the current kernel source."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("bytes_per_launch")
 METRIC = "verified draft tokens/s per GDN layer (48 v-heads, d=128) + % HBM roofline"
 
 
@@ -98,6 +126,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work of the oracle baseline")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (reads and writes MIB MiB), to scale "
+                         "memory counters in a profile")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -112,6 +143,14 @@ def main() -> int:
 
     gb.lib()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)  # one elementwise kernel: n*4 bytes read, n*4 written
+        torch.cuda.synchronize()
+        del src, dst
     w = wl.WORKLOADS["chain"]
     ledger = wl.algorithmic_bytes_verify(w)
     sets = make_sets(torch, wl, w, args.sets, dev)
@@ -161,7 +200,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic("verify_chain_batch1", source_sha(VERIFY_SOURCES)),
             "algorithmic_bytes_per_launch": ledger["verify_total"],
             "avg_launch_us": kern_ms * 1e3,
         },

@@ -345,3 +345,19 @@ def test_commit_definition(oracle_mod):
     assert np.array_equal(new[2], state[2]) and np.array_equal(new[4], state[4])
     new2, _ = oracle_mod.commit(state[:4], nodes, np.array([N - 1] * 4, np.int32))
     assert np.array_equal(new2, nodes[:, N - 1])
+
+
+def test_regression_fixture(oracle_mod):
+    """The oracle still reproduces its stored outputs on the fixed tiny input."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "oracle_regression.json")
+    g = json.load(open(path))
+    i = {n: np.array(a) for n, a in g["inputs"].items()}
+    ch = oracle_mod.chain(i["q"][:, :3], i["k"][:, :3], i["v"][:, :3], i["alpha"][:, :3], i["beta"][:, :3],
+                          i["state0"])
+    assert np.array_equal(ch["out"], np.array(g["chain"]["out"]))
+    assert np.array_equal(ch["final"], np.array(g["chain"]["final"]))
+    tr = oracle_mod.tree(i["q"], i["k"], i["v"], i["alpha"], i["beta"], i["state0"], g["parent"])
+    assert np.array_equal(tr["out"], np.array(g["tree"]["out"]))
+    assert np.array_equal(tr["nodes"], np.array(g["tree"]["nodes"]))
