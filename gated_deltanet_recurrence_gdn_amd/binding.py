@@ -47,6 +47,7 @@ _vp = ctypes.c_void_p
 _SIGS = {
     "gdn_verify_chain": [ctypes.POINTER(GdnShape)] + [_vp] * 12,
     "gdn_verify_tree": [ctypes.POINTER(GdnShape), _vp, ctypes.c_int32] + [_vp] * 11,
+    "gdn_commit_verify_chain": [ctypes.POINTER(GdnShape)] + [_vp] * 15,
     "gdn_commit": [ctypes.POINTER(GdnShape)] + [_vp] * 7,
     "gdn_status_string": [ctypes.c_int],
     "gdn_tree_walk": [_vp, ctypes.c_int32, _vp, _vp],
@@ -131,6 +132,21 @@ def gdn_verify_chain(q, k, v, alpha, beta, state, *, out=None, persist=None, fin
                                 _dev_ptr(persist, "persist"), _dev_ptr(final_state, "final_state"),
                                 _dev_ptr(status, "status"), _stream(stream))
     _check(rc, "gdn_verify_chain")
+
+
+def gdn_commit_verify_chain(accepted_prev, persist_prev, q, k, v, alpha, beta, state, *, final_prev=None,
+                            out=None, persist=None, final_state=None, state_slot=None, status=None,
+                            scale: float = 1.0, stream=None) -> None:
+    """Commit the previous step's accepted node and verify the next chain, in one launch."""
+    sh = _verify_shape(q, v, state, out, persist if persist is not None else persist_prev, scale)
+    rc = lib().gdn_commit_verify_chain(ctypes.byref(sh), _dev_ptr(accepted_prev, "accepted_prev"),
+                                       _dev_ptr(persist_prev, "persist_prev"), _dev_ptr(final_prev, "final_prev"),
+                                       _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                       _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"), _dev_ptr(state, "state"),
+                                       _dev_ptr(state_slot, "state_slot"), _dev_ptr(out, "out"),
+                                       _dev_ptr(persist, "persist"), _dev_ptr(final_state, "final_state"),
+                                       _dev_ptr(status, "status"), _stream(stream))
+    _check(rc, "gdn_commit_verify_chain")
 
 
 def _host_parent(parent) -> np.ndarray:

@@ -91,6 +91,12 @@ VerifyArgs make_args(const gdn_shape* sh, const VerifyPlan& p, const void* q, co
     a.rows_per_wg = p.rows_per_wg; a.slices = p.slices;
     a.qkv_bf16 = sh->qkv_dtype == GDN_BF16; a.out_dtype = sh->out_dtype;
     a.fork_slots = 0; a.per_seq_tree = 0; a.scale = sh->scale;
+    // Write-once outputs go out with non-temporal stores in small launches (measured
+    // faster at batch 1: the end-of-kernel drain is shorter) and with plain stores in
+    // large ones (measured faster at 384 units); the switch is at 256 MB of states written.
+    const size_t pbytes = persist == nullptr ? 0 : (sh->persist_dtype == GDN_F16 ? 2 : 4);
+    const double written = (double)sh->batch * sh->n_nodes * sh->h_v * sh->d_v * sh->d_k * pbytes;
+    a.nt_stores = written < 256.0 * (1 << 20);
     return a;
 }
 
@@ -190,6 +196,31 @@ int gdn_verify_chain(const gdn_shape* shape, const void* q, const void* k, const
     VerifyPlan p;
     if ((rc = plan_verify(shape, 0, &p)) != GDN_OK) return rc;
     VerifyArgs a = make_args(shape, p, q, k, v, alpha, beta, state, state_slot, out, persist, final_state, status);
+    const long long grid = (long long)shape->batch * shape->h_v * p.slices;
+    if (grid > 0x7fffffffLL) return GDN_ERR_SHAPE;
+    hipError_t e = launch_verify(a, nullptr, shape->d_k, p.m_groups, persist_mode(shape, persist), p.waves,
+                                 p.lds, (int)grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_commit_verify_chain(const gdn_shape* shape, const int32_t* accepted_prev, const void* persist_prev,
+                            const float* final_prev, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, float* state, const int32_t* state_slot,
+                            void* out, void* persist, float* final_state, int32_t* status, void* stream) {
+    int rc = check_verify(shape, q, k, v, alpha, beta, state, state_slot, out, persist, final_state);
+    if (rc != GDN_OK || shape->batch == 0) return rc;
+    if (accepted_prev == nullptr || persist_prev == nullptr) return GDN_ERR_NULL;
+    if (shape->persist_dtype != GDN_F16 && shape->persist_dtype != GDN_F32) return GDN_ERR_DTYPE;
+    if (!aligned(accepted_prev, 4) || !aligned(persist_prev, 16) || !aligned(final_prev, 16)) return GDN_ERR_ALIGN;
+    if (final_state != nullptr && final_state == state) return GDN_ERR_SHAPE;
+    VerifyPlan p;
+    if ((rc = plan_verify(shape, 0, &p)) != GDN_OK) return rc;
+    VerifyArgs a = make_args(shape, p, q, k, v, alpha, beta, state, state_slot, out, persist, final_state, status);
+    a.accepted_prev = accepted_prev;
+    a.persist_prev = persist_prev;
+    a.final_prev = final_prev;
+    a.state_w = state;
+    a.persist_prev_f16 = shape->persist_dtype == GDN_F16;
     const long long grid = (long long)shape->batch * shape->h_v * p.slices;
     if (grid > 0x7fffffffLL) return GDN_ERR_SHAPE;
     hipError_t e = launch_verify(a, nullptr, shape->d_k, p.m_groups, persist_mode(shape, persist), p.waves,
@@ -298,9 +329,8 @@ int gdn_prefill_chunked(const gdn_shape* shape, const void* q, const void* k, co
     if (state_slot != nullptr && sh->n_slots < 1) return GDN_ERR_SHAPE;
     if (sh->batch == 0 || sh->n_nodes == 0) return GDN_OK;
     if (!q || !k || !v || !alpha || !beta || !state || !out) return GDN_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return GDN_ERR_ALIGN;
-    if (!aligned(alpha, 4) || !aligned(beta, 4) || !aligned(state, 4) || !aligned(out, 4) ||
-        !aligned(state_slot, 4))
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return GDN_ERR_ALIGN;
+    if (!aligned(alpha, 4) || !aligned(beta, 4) || !aligned(state, 4) || !aligned(state_slot, 4))
         return GDN_ERR_ALIGN;
     const size_t need = prefill_workspace_bytes(sh->batch, sh->n_nodes, sh->h_qk, sh->h_v, sh->d_k);
     if (workspace == nullptr || workspace_bytes < need) return GDN_ERR_WORKSPACE;

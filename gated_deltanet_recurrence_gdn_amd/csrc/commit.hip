@@ -16,7 +16,7 @@
 namespace gdn {
 namespace {
 
-template <bool F16>
+template <bool F16, bool NT>
 __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a) {
     int blk = blockIdx.x;
     const int tile = blk % a.tiles_per_head;
@@ -57,17 +57,22 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a) {
             x1 = *reinterpret_cast<const f32x4*>(src + 4);
         }
     }
-    *reinterpret_cast<f32x4*>(dst) = x0;
-    *reinterpret_cast<f32x4*>(dst + 4) = x1;
+    store_stream<NT>(x0, reinterpret_cast<f32x4*>(dst));
+    store_stream<NT>(x1, reinterpret_cast<f32x4*>(dst + 4));
 }
 
 }  // namespace
 
 hipError_t launch_commit(const CommitArgs& a, bool persist_f16, int grid, int block, hipStream_t stream) {
-    if (persist_f16)
-        hipLaunchKernelGGL(commit_kernel<true>, dim3(grid), dim3(block), 0, stream, a);
-    else
-        hipLaunchKernelGGL(commit_kernel<false>, dim3(grid), dim3(block), 0, stream, a);
+    // non-temporal stores for small commits (shorter drain), plain ones for large (faster streaming)
+    const bool nt = (double)a.batch * a.h_v * a.head_elems * 4 < 256.0 * (1 << 20);
+    if (persist_f16) {
+        if (nt) hipLaunchKernelGGL((commit_kernel<true, true>), dim3(grid), dim3(block), 0, stream, a);
+        else hipLaunchKernelGGL((commit_kernel<true, false>), dim3(grid), dim3(block), 0, stream, a);
+    } else {
+        if (nt) hipLaunchKernelGGL((commit_kernel<false, true>), dim3(grid), dim3(block), 0, stream, a);
+        else hipLaunchKernelGGL((commit_kernel<false, false>), dim3(grid), dim3(block), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -78,6 +78,16 @@ __device__ __forceinline__ float load1_as_f32(const void* base, size_t idx, bool
     return static_cast<const float*>(base)[idx];
 }
 
+// Store of write-once data: non-temporal when NT (small launches, where it
+// shortens the end-of-kernel drain), plain otherwise (large streaming launches,
+// where plain stores measured faster).  A compile-time choice: with a runtime
+// branch the compiler merges both stores and drops the non-temporal hint.
+template <bool NT, typename T>
+__device__ __forceinline__ void store_stream(T v, T* p) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 __device__ __forceinline__ void store_out(void* out, size_t idx, float o, int dtype) {
     if (dtype == 0) static_cast<float*>(out)[idx] = o;
     else if (dtype == 2) static_cast<_Float16*>(out)[idx] = (_Float16)o;

@@ -54,6 +54,13 @@ struct VerifyArgs {
     int32_t fork_slots;  // fork slots reserved in LDS (tree walks)
     int32_t per_seq_tree;// 0: tree 0 for every sequence; 1: tree b - seq0
     float scale;
+    // fused commit of the previous step (chain launches only; accepted_prev == nullptr: off)
+    const int32_t* accepted_prev;
+    const void* persist_prev;
+    const float* final_prev;
+    float* state_w;      // the state cache written by the fused commit (same buffer as `state`)
+    int32_t persist_prev_f16;
+    int32_t nt_stores;   // 1: write-once outputs with non-temporal stores
 };
 
 // Depth-first walk of up to kTreesPerLaunch trees (tree launches only).

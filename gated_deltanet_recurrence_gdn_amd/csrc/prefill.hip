@@ -62,22 +62,26 @@ __device__ __forceinline__ h8 to_h8(const float (&x)[8]) {
     return r;
 }
 
-// Raw 16-byte loads of 8 elements (bf16 or fp32 source) kept in registers
-// until they are converted into LDS; fp32 sources need two.
+// Raw 16-byte loads of 8 elements (bf16 or fp32 source, BF16 fixed at compile
+// time) kept in registers until they are converted into LDS; fp32 needs two.
+// Loads are unconditional (callers clamp the index), so no load waits on a
+// branch merge.
 struct Raw8 {
     u32x4 w0, w1;
 };
-__device__ __forceinline__ void raw_load(Raw8& r, const void* base, size_t idx, bool bf16) {
-    if (bf16) {
+template <bool BF16>
+__device__ __forceinline__ void raw_load(Raw8& r, const void* base, size_t idx) {
+    if constexpr (BF16) {
         r.w0 = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + idx);
     } else {
         r.w0 = *reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + idx);
         r.w1 = *reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + idx + 4);
     }
 }
-__device__ __forceinline__ h8 raw_to_h8(const Raw8& r, bool bf16) {
+template <bool BF16>
+__device__ __forceinline__ h8 raw_to_h8(const Raw8& r, bool valid) {
     float x[8];
-    if (bf16) {
+    if constexpr (BF16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             x[2 * i] = bf16_lo(r.w0[i]);
@@ -93,19 +97,18 @@ __device__ __forceinline__ h8 raw_to_h8(const Raw8& r, bool bf16) {
             x[4 + i] = hi[i];
         }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = valid ? x[i] : 0.f;
     return to_h8(x);
-}
-__device__ __forceinline__ void raw_zero(Raw8& r) {
-    r.w0 = u32x4{0u, 0u, 0u, 0u};
-    r.w1 = u32x4{0u, 0u, 0u, 0u};
 }
 
 // Workspace layout (bytes), per sequence b and chunk c:
 //   T, P   [B][nch][h_v][C][C]     f16
 //   gates  [B][nch][h_v][3][C]     fp32: gamma_t, beta_t, Gamma_{C,t}
-//   KT     [B][nch][h_qk][d_k][C]  f16
+//   KT     [B][nch][h_qk][d_k][C]  f16   (K transposed)
+//   K, Q   [B][nch][h_qk][C][d_k]  f16   (converted once, read by every slice)
 struct WsLayout {
-    size_t T, P, G, KT, total;
+    size_t T, P, G, KT, K, Q, total;
 };
 __host__ __device__ inline WsLayout ws_layout(int B, int nch, int h_qk, int h_v, int d_k) {
     WsLayout w;
@@ -114,7 +117,9 @@ __host__ __device__ inline WsLayout ws_layout(int B, int nch, int h_qk, int h_v,
     w.P = w.T + units * h_v * kC * kC * 2;
     w.G = w.P + units * h_v * kC * kC * 2;
     w.KT = w.G + units * h_v * 3 * kC * 4;
-    w.total = w.KT + units * h_qk * (size_t)d_k * kC * 2;
+    w.K = w.KT + units * h_qk * (size_t)d_k * kC * 2;
+    w.Q = w.K + units * h_qk * (size_t)d_k * kC * 2;
+    w.total = w.Q + units * h_qk * (size_t)d_k * kC * 2;
     return w;
 }
 
@@ -139,7 +144,7 @@ struct PrepLds {
     float ell[kC], al[kC], be[kC];
 };
 
-template <int DK>
+template <int DK, bool BF16>
 __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs a) {
     constexpr int kLdK = DK + 8;
     constexpr int KSD = DK / 32;
@@ -154,31 +159,41 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
     const int b = blk / nch;
     const int g = h / a.group;
     const int t0 = ck * kC;
-    const bool bf16 = a.qkv_bf16 != 0;
     const WsLayout ws = ws_layout(a.batch, nch, a.h_qk, a.h_v, DK);
     unsigned char* wsb = static_cast<unsigned char*>(a.workspace);
     const size_t unit_v = ((size_t)b * nch + ck) * a.h_v + h;
     const size_t unit_q = ((size_t)b * nch + ck) * a.h_qk + g;
 
-    // 1. K, Q chunk -> LDS (f16); gates -> LDS
-    for (int e = tid; e < kC * (DK / 8); e += 256) {
-        const int t = e / (DK / 8), d = 8 * (e % (DK / 8));
-        float kf[8], qf[8];
-        if (t0 + t < a.T) {
-            const size_t src = (((size_t)b * a.T + t0 + t) * a.h_qk + g) * DK + d;
-            load8_as_f32(a.k, src, bf16, kf);
-            load8_as_f32(a.q, src, bf16, qf);
-        } else {
+    // 1. K, Q chunk -> LDS (f16); gates -> LDS.  All loads are issued first
+    //    (token index clamped into the sequence), then converted and stored.
+    {
+        constexpr int NK = kC * DK / 8 / 256;  // 8-element chunks per thread
+        Raw8 rk[NK], rq[NK];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) kf[i] = qf[i] = 0.f;
+        for (int n = 0; n < NK; ++n) {
+            const int e = tid + 256 * n;
+            const int t = e / (DK / 8), d = 8 * (e % (DK / 8));
+            const int tc = t0 + t < a.T ? t0 + t : a.T - 1;
+            const size_t src = (((size_t)b * a.T + tc) * a.h_qk + g) * DK + d;
+            raw_load<BF16>(rk[n], a.k, src);
+            raw_load<BF16>(rq[n], a.q, src);
         }
-        *reinterpret_cast<h8*>(&L.u.in.Kf[t * kLdK + d]) = to_h8(kf);
-        *reinterpret_cast<h8*>(&L.u.in.Qf[t * kLdK + d]) = to_h8(qf);
-    }
-    if (tid < kC) {
-        const bool in = t0 + tid < a.T;
-        L.al[tid] = in ? a.alpha[((size_t)b * a.T + t0 + tid) * a.h_v + h] : 1.f;
-        L.be[tid] = in ? a.beta[((size_t)b * a.T + t0 + tid) * a.h_v + h] : 0.f;
+        const int tg = t0 + (tid & 63) < a.T ? t0 + (tid & 63) : a.T - 1;
+        const float al = a.alpha[((size_t)b * a.T + tg) * a.h_v + h];
+        const float be = a.beta[((size_t)b * a.T + tg) * a.h_v + h];
+#pragma unroll
+        for (int n = 0; n < NK; ++n) {
+            const int e = tid + 256 * n;
+            const int t = e / (DK / 8), d = 8 * (e % (DK / 8));
+            const bool valid = t0 + t < a.T;
+            *reinterpret_cast<h8*>(&L.u.in.Kf[t * kLdK + d]) = raw_to_h8<BF16>(rk[n], valid);
+            *reinterpret_cast<h8*>(&L.u.in.Qf[t * kLdK + d]) = raw_to_h8<BF16>(rq[n], valid);
+        }
+        if (tid < kC) {
+            const bool in = t0 + tid < a.T;
+            L.al[tid] = in ? al : 1.f;
+            L.be[tid] = in ? be : 0.f;
+        }
     }
     __syncthreads();
 
@@ -199,12 +214,17 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         gw[2 * kC + lane] = expf(lC - x);
     } else if (h % a.group == 0) {
         _Float16* kt = reinterpret_cast<_Float16*>(wsb + ws.KT) + unit_q * DK * kC;
+        _Float16* kw = reinterpret_cast<_Float16*>(wsb + ws.K) + unit_q * kC * DK;
+        _Float16* qw = reinterpret_cast<_Float16*>(wsb + ws.Q) + unit_q * kC * DK;
         for (int e = tid - 64; e < DK * (kC / 8); e += 192) {
             const int d = e / (kC / 8), tt = 8 * (e % (kC / 8));
             h8 v;
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = L.u.in.Kf[(tt + i) * kLdK + d];
             *reinterpret_cast<h8*>(kt + d * kC + tt) = v;
+            const int t = e / (DK / 8), dd = 8 * (e % (DK / 8));
+            *reinterpret_cast<h8*>(kw + t * DK + dd) = *reinterpret_cast<const h8*>(&L.u.in.Kf[t * kLdK + dd]);
+            *reinterpret_cast<h8*>(qw + t * DK + dd) = *reinterpret_cast<const h8*>(&L.u.in.Qf[t * kLdK + dd]);
         }
     }
     __syncthreads();
@@ -339,42 +359,38 @@ struct ScanLds {
     _Float16 UT[kDVS * kLdT];  // U^T
     _Float16 UG[kDVS * kLdT];  // (Gamma_{C,t} U)^T
     _Float16 Sf[kDVS * kLdK];  // state slice (f16) [value col][d_k]
+    float Os[kC * (kDVS + 4)]; // this chunk's outputs (fp32) [token][value col]
     float gam[kC], bet[kC], gC[kC];
 };
 
 template <int DK>
 struct ScanRegs {
     static constexpr int NK = kC * DK / 8 / 256;  // 16-byte chunks per thread of K (and Q, K^T)
-    Raw8 k[NK], q[NK];
-    u32x4 kt[NK], tt[2], pp[2];
+    u32x4 k[NK], q[NK], kt[NK], tt[2], pp[2];
     Raw8 v;
     float g0, g1, g2;
 };
 
-template <int DK>
+// Issue every global load of chunk ck (token indices clamped into the
+// sequence; the invalid rows are zeroed when stored).
+template <int DK, bool BF16>
 __device__ __forceinline__ void scan_load(ScanRegs<DK>& R, const PrefillArgs& a, const unsigned char* wsb,
                                           const WsLayout& ws, int b, int h, int g, int ck, int nch, int col0,
-                                          int tid, bool bf16) {
+                                          int tid) {
     constexpr int NK = ScanRegs<DK>::NK;
     const int t0 = ck * kC;
-#pragma unroll
-    for (int n = 0; n < NK; ++n) {
-        const int e = tid + 256 * n;
-        const int t = e / (DK / 8), d = 8 * (e % (DK / 8));
-        if (t0 + t < a.T) {
-            const size_t src = (((size_t)b * a.T + t0 + t) * a.h_qk + g) * DK + d;
-            raw_load(R.k[n], a.k, src, bf16);
-            raw_load(R.q[n], a.q, src, bf16);
-        } else {
-            raw_zero(R.k[n]);
-            raw_zero(R.q[n]);
-        }
-    }
+    const int tmax = a.T - 1;
     const size_t unit_v = ((size_t)b * nch + ck) * a.h_v + h;
     const size_t unit_q = ((size_t)b * nch + ck) * a.h_qk + g;
     const uint16_t* ktw = reinterpret_cast<const uint16_t*>(wsb + ws.KT) + unit_q * DK * kC;
+    const uint16_t* kw = reinterpret_cast<const uint16_t*>(wsb + ws.K) + unit_q * kC * DK;
+    const uint16_t* qw = reinterpret_cast<const uint16_t*>(wsb + ws.Q) + unit_q * kC * DK;
 #pragma unroll
-    for (int n = 0; n < NK; ++n) R.kt[n] = *reinterpret_cast<const u32x4*>(ktw + 8 * (tid + 256 * n));
+    for (int n = 0; n < NK; ++n) {
+        R.k[n] = *reinterpret_cast<const u32x4*>(kw + 8 * (tid + 256 * n));
+        R.q[n] = *reinterpret_cast<const u32x4*>(qw + 8 * (tid + 256 * n));
+        R.kt[n] = *reinterpret_cast<const u32x4*>(ktw + 8 * (tid + 256 * n));
+    }
     const uint16_t* tw = reinterpret_cast<const uint16_t*>(wsb + ws.T) + unit_v * kC * kC;
     const uint16_t* pw = reinterpret_cast<const uint16_t*>(wsb + ws.P) + unit_v * kC * kC;
 #pragma unroll
@@ -384,27 +400,25 @@ __device__ __forceinline__ void scan_load(ScanRegs<DK>& R, const PrefillArgs& a,
     }
     {
         const int t = tid / (kDVS / 8), j = 8 * (tid % (kDVS / 8));
-        if (t0 + t < a.T) raw_load(R.v, a.v, (((size_t)b * a.T + t0 + t) * a.h_v + h) * a.d_v + col0 + j, bf16);
-        else raw_zero(R.v);
+        const int tc = t0 + t < tmax ? t0 + t : tmax;
+        raw_load<BF16>(R.v, a.v, (((size_t)b * a.T + tc) * a.h_v + h) * a.d_v + col0 + j);
     }
-    if (tid < kC) {
-        const float* gw = reinterpret_cast<const float*>(wsb + ws.G) + unit_v * 3 * kC;
-        R.g0 = gw[tid];
-        R.g1 = gw[kC + tid];
-        R.g2 = gw[2 * kC + tid];
-    }
+    const float* gw = reinterpret_cast<const float*>(wsb + ws.G) + unit_v * 3 * kC;
+    R.g0 = gw[tid & 63];
+    R.g1 = gw[kC + (tid & 63)];
+    R.g2 = gw[2 * kC + (tid & 63)];
 }
 
-template <int DK>
-__device__ __forceinline__ void scan_store(const ScanRegs<DK>& R, ScanLds<DK>& L, int tid, bool bf16) {
+template <int DK, bool BF16>
+__device__ __forceinline__ void scan_store(const ScanRegs<DK>& R, ScanLds<DK>& L, int tid, int t0, int T) {
     constexpr int NK = ScanRegs<DK>::NK;
     constexpr int kLdK = DK + 8;
 #pragma unroll
     for (int n = 0; n < NK; ++n) {
         const int e = tid + 256 * n;
         const int t = e / (DK / 8), d = 8 * (e % (DK / 8));
-        *reinterpret_cast<h8*>(&L.Kf[t * kLdK + d]) = raw_to_h8(R.k[n], bf16);
-        *reinterpret_cast<h8*>(&L.Qf[t * kLdK + d]) = raw_to_h8(R.q[n], bf16);
+        *reinterpret_cast<u32x4*>(&L.Kf[t * kLdK + d]) = R.k[n];  // zero rows past T come from prepare
+        *reinterpret_cast<u32x4*>(&L.Qf[t * kLdK + d]) = R.q[n];
         const int dd = e / (kC / 8), tt = 8 * (e % (kC / 8));
         *reinterpret_cast<u32x4*>(&L.KT[dd * kLdT + tt]) = R.kt[n];
     }
@@ -417,7 +431,7 @@ __device__ __forceinline__ void scan_store(const ScanRegs<DK>& R, ScanLds<DK>& L
     }
     {
         const int t = tid / (kDVS / 8), j = 8 * (tid % (kDVS / 8));
-        *reinterpret_cast<h8*>(&L.Vs[t * (kDVS + 8) + j]) = raw_to_h8(R.v, bf16);
+        *reinterpret_cast<h8*>(&L.Vs[t * (kDVS + 8) + j]) = raw_to_h8<BF16>(R.v, t0 + t < T);
     }
     if (tid < kC) {
         L.gam[tid] = R.g0;
@@ -426,7 +440,36 @@ __device__ __forceinline__ void scan_store(const ScanRegs<DK>& R, ScanLds<DK>& L
     }
 }
 
-template <int DK, int OUT>
+// One chunk's outputs, staged in LDS as fp32 [token][value col] and written
+// out as 16-byte rows of the output dtype.
+template <int OUT>
+__device__ __forceinline__ void write_out(const float* Os, const PrefillArgs& a, int b, int h, int col0, int t0,
+                                          int tid) {
+    constexpr int EPT = OUT == 0 ? 4 : 8;  // elements per 16-byte store
+    constexpr int PER_ROW = kDVS / EPT;
+    for (int e = tid; e < kC * PER_ROW; e += 256) {
+        const int t = e / PER_ROW, j = EPT * (e % PER_ROW);
+        if (t0 + t >= a.T) continue;
+        const float* src = Os + t * (kDVS + 4) + j;
+        const size_t idx = (((size_t)b * a.T + t0 + t) * a.h_v + h) * a.d_v + col0 + j;
+        if constexpr (OUT == 0) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + idx) = *reinterpret_cast<const f32x4*>(src);
+        } else if constexpr (OUT == 2) {
+            h8 v;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = (_Float16)src[i];
+            *reinterpret_cast<h8*>(static_cast<_Float16*>(a.out) + idx) = v;
+        } else {
+            u32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[i] = (uint32_t)f32_to_bf16(src[2 * i]) | ((uint32_t)f32_to_bf16(src[2 * i + 1]) << 16);
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + idx) = v;
+        }
+    }
+}
+
+template <int DK, int OUT, bool BF16>
 __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs a) {
     constexpr int kLdK = DK + 8;
     constexpr int NT = DK / 16;      // d_k tiles
@@ -443,7 +486,6 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs a) 
     const int g = h / a.group;
     const int col0 = slice * kDVS;
     const int nch = (a.T + kC - 1) / kC;
-    const bool bf16 = a.qkv_bf16 != 0;
     const WsLayout ws = ws_layout(a.batch, nch, a.h_qk, a.h_v, DK);
     const unsigned char* wsb = static_cast<const unsigned char*>(a.workspace);
 
@@ -476,46 +518,59 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs a) 
     }
 
     ScanRegs<DK> R;
-    scan_load<DK>(R, a, wsb, ws, b, h, g, 0, nch, col0, tid, bf16);
+    scan_load<DK, BF16>(R, a, wsb, ws, b, h, g, 0, nch, col0, tid);
     const int it = wave;            // row block of the per-token products
     const int ksmax = it / 2;       // T and P are lower triangular
     const int tb = 16 * it + 4 * (lane >> 4);  // first token row held by this lane
     for (int ck = 0; ck < nch; ++ck) {
         const int t0 = ck * kC;
-        scan_store<DK>(R, L, tid, bf16);
-        if (ck + 1 < nch) scan_load<DK>(R, a, wsb, ws, b, h, g, ck + 1, nch, col0, tid, bf16);
+        scan_store<DK, BF16>(R, L, tid, t0, a.T);
+        if (ck + 1 < nch) scan_load<DK, BF16>(R, a, wsb, ws, b, h, g, ck + 1, nch, col0, tid);
+        // the previous chunk's outputs leave after this chunk's loads are issued, so the wait
+        // for this chunk's prefetched operands never waits on output stores
+        if (ck > 0) write_out<OUT>(L.Os, a, b, h, col0, t0 - kC, tid);
         __syncthreads();
 
         // K H and Q H for rows 16 it, both value tiles; R = beta V - beta gamma K H
-        f32x4 oacc[2];
+        f32x4 oacc[2], kh[2];
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) kh[vt] = oacc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+            const h8 ak = frag(L.Kf, kLdK, 16 * it, 32 * ks, lane);
+            const h8 aq = frag(L.Qf, kLdK, 16 * it, 32 * ks, lane);
+#pragma unroll
+            for (int vt = 0; vt < 2; ++vt) {
+                const h8 sb = frag(L.Sf, kLdK, 16 * vt, 32 * ks, lane);
+                kh[vt] = mfma16(ak, sb, kh[vt]);
+                oacc[vt] = mfma16(aq, sb, oacc[vt]);
+            }
+        }
 #pragma unroll
         for (int vt = 0; vt < 2; ++vt) {
-            f32x4 kh = {0.f, 0.f, 0.f, 0.f}, qh = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-                const h8 sb = frag(L.Sf, kLdK, 16 * vt, 32 * ks, lane);
-                kh = mfma16(frag(L.Kf, kLdK, 16 * it, 32 * ks, lane), sb, kh);
-                qh = mfma16(frag(L.Qf, kLdK, 16 * it, 32 * ks, lane), sb, qh);
-            }
             const int col = 16 * vt + (lane & 15);
             h4 r4;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float bt = L.bet[tb + r], gt = L.gam[tb + r];
                 const float vv = (float)L.Vs[(tb + r) * (kDVS + 8) + col];
-                r4[r] = (_Float16)(bt * (vv - gt * kh[r]));
-                oacc[vt][r] = gt * qh[r];
+                r4[r] = (_Float16)(bt * (vv - gt * kh[vt][r]));
+                oacc[vt][r] *= gt;
             }
             *reinterpret_cast<h4*>(&L.RT[col * kLdT + tb]) = r4;
         }
         __syncthreads();
 
         // U = T R
+        f32x4 uacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        for (int ks = 0; ks <= ksmax; ++ks) {
+            const h8 at = frag(L.Tt, kLdT, 16 * it, 32 * ks, lane);
+#pragma unroll
+            for (int vt = 0; vt < 2; ++vt) uacc[vt] = mfma16(at, frag(L.RT, kLdT, 16 * vt, 32 * ks, lane), uacc[vt]);
+        }
 #pragma unroll
         for (int vt = 0; vt < 2; ++vt) {
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
-            for (int ks = 0; ks <= ksmax; ++ks)
-                u = mfma16(frag(L.Tt, kLdT, 16 * it, 32 * ks, lane), frag(L.RT, kLdT, 16 * vt, 32 * ks, lane), u);
+            const f32x4 u = uacc[vt];
             const int col = 16 * vt + (lane & 15);
             h4 u4, g4;
 #pragma unroll
@@ -528,35 +583,34 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs a) 
         }
         __syncthreads();
 
-        // O = scale (gamma Q H + P U) -> global
+        // O = scale (gamma Q H + P U) -> LDS (written out with the next chunk's staging)
+        for (int ks = 0; ks <= ksmax; ++ks) {
+            const h8 ap = frag(L.P, kLdT, 16 * it, 32 * ks, lane);
+#pragma unroll
+            for (int vt = 0; vt < 2; ++vt) oacc[vt] = mfma16(ap, frag(L.UT, kLdT, 16 * vt, 32 * ks, lane), oacc[vt]);
+        }
 #pragma unroll
         for (int vt = 0; vt < 2; ++vt) {
-            for (int ks = 0; ks <= ksmax; ++ks)
-                oacc[vt] = mfma16(frag(L.P, kLdT, 16 * it, 32 * ks, lane), frag(L.UT, kLdT, 16 * vt, 32 * ks, lane),
-                                  oacc[vt]);
-            const int col = col0 + 16 * vt + (lane & 15);
+            const int col = 16 * vt + (lane & 15);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = t0 + tb + r;
-                if (t < a.T) {
-                    const size_t idx = (((size_t)b * a.T + t) * a.h_v + h) * a.d_v + col;
-                    const float o = a.scale * oacc[vt][r];
-                    if constexpr (OUT == 0) static_cast<float*>(a.out)[idx] = o;
-                    else if constexpr (OUT == 2) static_cast<_Float16*>(a.out)[idx] = (_Float16)o;
-                    else static_cast<uint16_t*>(a.out)[idx] = f32_to_bf16(o);
-                }
-            }
+            for (int r = 0; r < 4; ++r) L.Os[(tb + r) * (kDVS + 4) + col] = a.scale * oacc[vt][r];
         }
         // state: H_C = gamma_C H_0 + K^T diag(Gamma_C) U  (as S = H^T on the accumulators)
+        // a wave's state tiles share one value tile (STW <= NT), so one U fragment serves them all
         const float gc = L.gam[kC - 1];
+        const int vtw = (wave * STW) / NT;
 #pragma unroll
-        for (int y = 0; y < STW; ++y) {
-            const int x = wave * STW + y, vt = x / NT, dt = x % NT;
+        for (int y = 0; y < STW; ++y)
 #pragma unroll
             for (int r = 0; r < 4; ++r) st[y][r] *= gc;
 #pragma unroll
-            for (int ks = 0; ks < kC / 32; ++ks)
-                st[y] = mfma16(frag(L.UG, kLdT, 16 * vt, 32 * ks, lane), frag(L.KT, kLdT, 16 * dt, 32 * ks, lane), st[y]);
+        for (int ks = 0; ks < kC / 32; ++ks) {
+            const h8 au = frag(L.UG, kLdT, 16 * vtw, 32 * ks, lane);
+#pragma unroll
+            for (int y = 0; y < STW; ++y) {
+                const int dt = (wave * STW + y) % NT;
+                st[y] = mfma16(au, frag(L.KT, kLdT, 16 * dt, 32 * ks, lane), st[y]);
+            }
         }
         __syncthreads();  // every read of this chunk's LDS data is done
 #pragma unroll
@@ -568,6 +622,7 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs a) 
         }
     }
 
+    write_out<OUT>(L.Os, a, b, h, col0, (nch - 1) * kC, tid);  // last chunk's outputs
     // final state, in place
 #pragma unroll
     for (int y = 0; y < STW; ++y) {
@@ -584,28 +639,34 @@ hipError_t set_lds(K kernel, size_t lds) {
                                (int)lds);
 }
 
-template <int DK, int OUT>
+template <int DK, int OUT, bool BF16>
 hipError_t launch_scan(const PrefillArgs& a, int grid, hipStream_t st) {
     const size_t lds = sizeof(ScanLds<DK>);
-    hipError_t e = set_lds(&prefill_scan_kernel<DK, OUT>, lds);
+    hipError_t e = set_lds(&prefill_scan_kernel<DK, OUT, BF16>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT>), dim3(grid), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT, BF16>), dim3(grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
 
-template <int DK>
+template <int DK, bool BF16>
 hipError_t launch_dk(const PrefillArgs& a, int out_dtype, int prep_grid, int scan_grid, hipStream_t st) {
     const size_t lds = sizeof(PrepLds<DK>);
-    hipError_t e = set_lds(&prefill_prepare_kernel<DK>, lds);
+    hipError_t e = set_lds(&prefill_prepare_kernel<DK, BF16>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_prepare_kernel<DK>), dim3(prep_grid), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((prefill_prepare_kernel<DK, BF16>), dim3(prep_grid), dim3(256), lds, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     switch (out_dtype) {
-        case GDN_F32: return launch_scan<DK, 0>(a, scan_grid, st);
-        case GDN_BF16: return launch_scan<DK, 1>(a, scan_grid, st);
-        case GDN_F16: return launch_scan<DK, 2>(a, scan_grid, st);
+        case GDN_F32: return launch_scan<DK, 0, BF16>(a, scan_grid, st);
+        case GDN_BF16: return launch_scan<DK, 1, BF16>(a, scan_grid, st);
+        case GDN_F16: return launch_scan<DK, 2, BF16>(a, scan_grid, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <int DK>
+hipError_t launch_dk_any(const PrefillArgs& a, int out_dtype, int prep_grid, int scan_grid, hipStream_t st) {
+    return a.qkv_bf16 ? launch_dk<DK, true>(a, out_dtype, prep_grid, scan_grid, st)
+                      : launch_dk<DK, false>(a, out_dtype, prep_grid, scan_grid, st);
 }
 
 }  // namespace
@@ -621,9 +682,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int d_k, int out_dtype, hipStrea
     const long long scan = (long long)a.batch * a.h_v * a.slices;
     if (prep > 0x7fffffffLL || scan > 0x7fffffffLL) return hipErrorInvalidValue;
     switch (d_k) {
-        case 32: return launch_dk<32>(a, out_dtype, (int)prep, (int)scan, stream);
-        case 64: return launch_dk<64>(a, out_dtype, (int)prep, (int)scan, stream);
-        case 128: return launch_dk<128>(a, out_dtype, (int)prep, (int)scan, stream);
+        case 32: return launch_dk_any<32>(a, out_dtype, (int)prep, (int)scan, stream);
+        case 64: return launch_dk_any<64>(a, out_dtype, (int)prep, (int)scan, stream);
+        case 128: return launch_dk_any<128>(a, out_dtype, (int)prep, (int)scan, stream);
         default: return hipErrorInvalidValue;
     }
 }

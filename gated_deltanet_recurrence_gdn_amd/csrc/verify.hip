@@ -69,7 +69,7 @@ __device__ __forceinline__ void read_node(NodeOps<M>& x, const float* kL, const 
     for (int m = 0; m < M; ++m) x.vb[m] = vbL[node * rows + vr0 + m * RPG];
 }
 
-template <int DK, int M, bool TREE, int PMODE, int OUT>
+template <int DK, int M, bool TREE, int PMODE, int OUT, bool NT>
 __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t* walk) {
     constexpr int LPR = DK / 8;   // lanes per state row
     constexpr int RPG = 64 / LPR; // rows per row group
@@ -99,6 +99,15 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
             return;
         }
     }
+    // fused commit of the previous step: its accepted node must be in range
+    int acc = 0;
+    if (a.accepted_prev != nullptr) {
+        acc = a.accepted_prev[b];
+        if (acc < 0 || acc >= N) {
+            if (tid == 0 && a.status != nullptr) a.status[0] = GDN_ERR_NODE;
+            return;
+        }
+    }
 
     // LDS: k[N][DK], q[N][DK] (fp32), coef[N] (alpha, beta, q.k), beta*v[N][rows],
     // walk[N] (trees), then the fork slots.
@@ -115,8 +124,9 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
     const int wrow = wave * R;  // first row of this wave inside the slice
     const size_t head_elems = (size_t)DV * DK;
     float S[M][8];
-    {
-        const float* src = a.state + ((size_t)s * a.h_v + h) * head_elems + (size_t)(row0 + wrow + r) * DK + 8 * c;
+    const size_t my_rows = (size_t)(row0 + wrow + r) * DK + 8 * c;  // this lane's first element in a head
+    if (a.accepted_prev == nullptr) {
+        const float* src = a.state + ((size_t)s * a.h_v + h) * head_elems + my_rows;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (size_t)m * RPG * DK);
@@ -126,6 +136,52 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
                 S[m][e] = x0[e];
                 S[m][4 + e] = x1[e];
             }
+        }
+    } else {
+        // Commit while loading: the initial state is the previous step's accepted node
+        // (its exact fp32 final state when the whole block was accepted, else its persisted
+        // copy widened to fp32); it is also written back to the state cache.
+        if (a.final_prev != nullptr && acc == N - 1) {
+            const float* src = a.final_prev + ((size_t)b * a.h_v + h) * head_elems + my_rows;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (size_t)m * RPG * DK);
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + (size_t)m * RPG * DK + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    S[m][e] = x0[e];
+                    S[m][4 + e] = x1[e];
+                }
+            }
+        } else if (a.persist_prev_f16) {
+            const _Float16* src = static_cast<const _Float16*>(a.persist_prev) +
+                                  (((size_t)b * N + acc) * a.h_v + h) * head_elems + my_rows;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const f16x8 hv = *reinterpret_cast<const f16x8*>(src + (size_t)m * RPG * DK);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) S[m][e] = (float)hv[e];
+            }
+        } else {
+            const float* src = static_cast<const float*>(a.persist_prev) +
+                               (((size_t)b * N + acc) * a.h_v + h) * head_elems + my_rows;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (size_t)m * RPG * DK);
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + (size_t)m * RPG * DK + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    S[m][e] = x0[e];
+                    S[m][4 + e] = x1[e];
+                }
+            }
+        }
+        float* dst = a.state_w + ((size_t)s * a.h_v + h) * head_elems + my_rows;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            store_stream<NT>(f32x4{S[m][0], S[m][1], S[m][2], S[m][3]}, reinterpret_cast<f32x4*>(dst + (size_t)m * RPG * DK));
+            store_stream<NT>(f32x4{S[m][4], S[m][5], S[m][6], S[m][7]},
+                         reinterpret_cast<f32x4*>(dst + (size_t)m * RPG * DK + 4));
         }
     }
 
@@ -227,16 +283,17 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
             const float o = fmaf(sal, pq, sqk * u);   // scale (alpha S q + (q.k) u)
 #pragma unroll
             for (int e = 0; e < 8; ++e) S[m][e] = fmaf(al, S[m][e], u * x.k[e]);
+            // persisted states are written once and read later by commit, never by this kernel
             if constexpr (PMODE == 1) {
                 f16x8 hv;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) hv[e] = (_Float16)S[m][e];
-                *reinterpret_cast<f16x8*>(static_cast<_Float16*>(a.persist) + nbase * node_elems + prow +
-                                          (size_t)m * RPG * DK) = hv;
+                store_stream<NT>(hv, reinterpret_cast<f16x8*>(static_cast<_Float16*>(a.persist) + nbase * node_elems +
+                                                          prow + (size_t)m * RPG * DK));
             } else if constexpr (PMODE == 2) {
                 float* dst = static_cast<float*>(a.persist) + nbase * node_elems + prow + (size_t)m * RPG * DK;
-                *reinterpret_cast<f32x4*>(dst) = f32x4{S[m][0], S[m][1], S[m][2], S[m][3]};
-                *reinterpret_cast<f32x4*>(dst + 4) = f32x4{S[m][4], S[m][5], S[m][6], S[m][7]};
+                store_stream<NT>(f32x4{S[m][0], S[m][1], S[m][2], S[m][3]}, reinterpret_cast<f32x4*>(dst));
+                store_stream<NT>(f32x4{S[m][4], S[m][5], S[m][6], S[m][7]}, reinterpret_cast<f32x4*>(dst + 4));
             }
             if (a.out != nullptr && c == 0)
                 put_out<OUT>(a.out, (nbase * a.h_v + h) * DV + row0 + vr0 + m * RPG, o);
@@ -276,30 +333,32 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 float* d = dst + (size_t)m * RPG * DK;
-                *reinterpret_cast<f32x4*>(d) = f32x4{S[m][0], S[m][1], S[m][2], S[m][3]};
-                *reinterpret_cast<f32x4*>(d + 4) = f32x4{S[m][4], S[m][5], S[m][6], S[m][7]};
+                store_stream<NT>(f32x4{S[m][0], S[m][1], S[m][2], S[m][3]}, reinterpret_cast<f32x4*>(d));
+                store_stream<NT>(f32x4{S[m][4], S[m][5], S[m][6], S[m][7]}, reinterpret_cast<f32x4*>(d + 4));
             }
         }
     }
 }
 
-template <int DK, int M, int PMODE, int OUT>
+template <int DK, int M, int PMODE, int OUT, bool NT>
 __global__ __launch_bounds__(256) void verify_chain_kernel(const VerifyArgs a) {
-    verify_body<DK, M, false, PMODE, OUT>(a, nullptr);
+    verify_body<DK, M, false, PMODE, OUT, NT>(a, nullptr);
 }
 
 template <int DK, int M, int PMODE, int OUT>
 __global__ __launch_bounds__(256) void verify_tree_kernel(const VerifyArgs a, const TreeSched t) {
     const int bl = xcd_logical_block(blockIdx.x, gridDim.x) / (a.slices * a.h_v);
-    verify_body<DK, M, true, PMODE, OUT>(a, t.step[a.per_seq_tree ? bl : 0]);
+    verify_body<DK, M, true, PMODE, OUT, true>(a, t.step[a.per_seq_tree ? bl : 0]);
 }
 
 template <int DK, int M, int PMODE, int OUT>
 hipError_t launch_one(const VerifyArgs& a, const TreeSched* t, int waves, size_t lds, int grid, hipStream_t st) {
     if (t != nullptr)
         hipLaunchKernelGGL((verify_tree_kernel<DK, M, PMODE, OUT>), dim3(grid), dim3(64 * waves), lds, st, a, *t);
+    else if (a.nt_stores)
+        hipLaunchKernelGGL((verify_chain_kernel<DK, M, PMODE, OUT, true>), dim3(grid), dim3(64 * waves), lds, st, a);
     else
-        hipLaunchKernelGGL((verify_chain_kernel<DK, M, PMODE, OUT>), dim3(grid), dim3(64 * waves), lds, st, a);
+        hipLaunchKernelGGL((verify_chain_kernel<DK, M, PMODE, OUT, false>), dim3(grid), dim3(64 * waves), lds, st, a);
     return hipGetLastError();
 }
 

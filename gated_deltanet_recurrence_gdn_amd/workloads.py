@@ -197,4 +197,8 @@ def algorithmic_bytes_verify(w: Workload, out_bytes: int = 4) -> dict:
     }
     items["verify_total"] = sum(v for k, v in items.items() if k != "commit")
     items["total"] = items["verify_total"] + items["commit"]
+    # one launch per step: the previous step's accepted node is read (its f16/fp32
+    # copy) instead of the cached state, and written back as the committed state
+    items["fused_total"] = (items["verify_total"] - items["state_read"] + B * w.h_v * hs * p_b
+                            + B * w.h_v * hs * 4 + B * 4)
     return items

@@ -107,6 +107,31 @@ int gdn_verify_chain(const gdn_shape* shape, const void* q, const void* k, const
                      int32_t* status, void* stream);
 
 /*
+ * One launch for a decode step: commit the previous step's accepted node, then
+ * verify the next chain from the committed state.  Equivalent to
+ *     gdn_commit(shape, accepted_prev, persist_prev, final_prev, state, state_slot, status)
+ *     gdn_verify_chain(shape, q, k, v, alpha, beta, state, state_slot, out, persist,
+ *                      final_state, status)
+ * with the commit fused into the verify's state load, so the committed state is
+ * read once (as the f16 node copy, or final_prev on full acceptance), written to
+ * state[slot(b)] and used directly.  Page "400 tok/s with Qwen3.5", section
+ * "Handling recurrent state" (state set to the accepted boundary before the next
+ * verification).
+ *
+ * persist_prev and final_prev (nullable) are the previous step's persist and
+ * final_state: same layout, n_nodes and persist_dtype as this call's outputs.
+ * They may be the very buffers this call writes (each value is read before it
+ * is overwritten).  accepted_prev is a device array [B]; a node outside [0, N)
+ * skips the sequence entirely (state and outputs untouched) and sets *status to
+ * GDN_ERR_NODE.  Other arguments and errors as gdn_verify_chain; final_state
+ * may not be `state` here.
+ */
+int gdn_commit_verify_chain(const gdn_shape* shape, const int32_t* accepted_prev, const void* persist_prev,
+                            const float* final_prev, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, float* state, const int32_t* state_slot,
+                            void* out, void* persist, float* final_state, int32_t* status, void* stream);
+
+/*
  * Verify a tree of N draft nodes per sequence.
  * Page "Qwen3.6 27B: From 20 t/s to 184 t/s", section "Diffusion applied to
  * text": a best-first tree of up to 22 nodes is verified in one target pass.
@@ -151,7 +176,7 @@ int gdn_commit(const gdn_shape* shape, const int32_t* accepted_node, const void*
  * are converted to f16 for the matrix cores, so they must lie inside the f16
  * range, and magnitudes below 2^-14 keep an absolute precision of 2^-25);
  * alpha, beta [B][T][h_v] fp32; out [B][T][h_v][d_v] in out_dtype (F32, F16
- * or BF16).  state[slot(b)] holds the initial state on entry and the state
+ * or BF16), 16-byte aligned.  state[slot(b)] holds the initial state on entry and the state
  * after token T-1 on return (updated in place).  A zero alpha resets the state
  * up to a factor e^-80 (the log-gate is clamped at -80).  d_k must be 32, 64 or
  * 128 and d_v a multiple of 32.  persist_dtype is ignored.  T = 0 or batch = 0

@@ -196,11 +196,24 @@ def test_prefill_rejects_bad_requests():
     assert prefill(shape(**P), q=None) == E["GDN_ERR_NULL"]
     assert prefill(shape(**P), out=None) == E["GDN_ERR_NULL"]
     assert prefill(shape(**P), q=FAKE + 4) == E["GDN_ERR_ALIGN"]
+    assert prefill(shape(**P), out=FAKE + 4) == E["GDN_ERR_ALIGN"]
     assert prefill(shape(**P), ws=None) == E["GDN_ERR_WORKSPACE"]
     sh = shape(**P)
     need = gb.lib().gdn_prefill_workspace_bytes(ctypes.byref(sh))
-    # 64 chunks x (48 heads x (T + P) f16 + 48 x 3 x 64 fp32 gates + 16 q/k heads x K^T f16)
-    assert need == 64 * (48 * 2 * 64 * 64 * 2 + 48 * 3 * 64 * 4 + 16 * 128 * 64 * 2)
+    # 64 chunks x (48 heads x (T + P) f16 + 48 x 3 x 64 fp32 gates + 16 q/k heads x (K^T, K, Q) f16)
+    assert need == 64 * (48 * 2 * 64 * 64 * 2 + 48 * 3 * 64 * 4 + 16 * 3 * 128 * 64 * 2)
     assert prefill(sh, ws_bytes=need - 1) == E["GDN_ERR_WORKSPACE"]
     assert prefill(shape(**{**P, "n_nodes": 0}), q=None, ws=None) == 0
     assert prefill(shape(**{**P, "batch": 0}), q=None, ws=None) == 0
+
+
+def test_fused_commit_verify_rejects_bad_requests():
+    L = gb.lib()
+    f = lambda sh, acc=FAKE, per_prev=FAKE, fin_prev=None, st=FAKE, fin=None: L.gdn_commit_verify_chain(  # noqa: E731
+        ctypes.byref(sh), acc, per_prev, fin_prev, FAKE, FAKE, FAKE, FAKE, FAKE, st, None, FAKE, FAKE, fin, None, None)
+    assert f(shape(), acc=None) == E["GDN_ERR_NULL"]
+    assert f(shape(), per_prev=None) == E["GDN_ERR_NULL"]
+    assert f(shape(), per_prev=FAKE + 8) == E["GDN_ERR_ALIGN"]
+    assert f(shape(), acc=FAKE + 2) == E["GDN_ERR_ALIGN"]
+    assert f(shape(), fin=FAKE) == E["GDN_ERR_SHAPE"]  # final_state == state
+    assert f(shape(d_k=96)) == E["GDN_ERR_SHAPE"]

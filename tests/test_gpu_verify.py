@@ -350,3 +350,79 @@ def test_runs_on_a_side_stream():
                             final_state=fin)
     s.synchronize()
     assert torch.equal(out, ref_out) and torch.equal(persist, ref_p) and torch.equal(fin, ref_f)
+
+
+# --------------------------------------------------------------------------
+# fused commit + verify (one launch per decode step)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("persist_dtype", [torch.float16, torch.float32])
+@pytest.mark.parametrize("same_buffers", [False, True])
+def test_fused_commit_verify_equals_commit_then_verify(persist_dtype, same_buffers):
+    w, d1 = small_inputs(21, 3, 16, 2, 6, 128, 128)
+    _, d2 = small_inputs(22, 3, 16, 2, 6, 128, 128)
+    t1, t2 = dev_inputs(d1), dev_inputs(d2)
+    out1, per1, fin1 = run_chain(t1, 16, persist_dtype=persist_dtype)
+    acc = torch.tensor([3, 15, 0], dtype=torch.int32, device=DEV)
+    st_ref = t1["state0"].clone()
+    assert _commit(acc, per1, st_ref, final=fin1) == 0
+    out_r, per_r, fin_r = run_chain(t2, 16, persist_dtype=persist_dtype, state=st_ref)
+    st = t1["state0"].clone()
+    if same_buffers:  # the step writes over the very buffers it commits from
+        out, per, fin = out1.clone(), per1.clone(), fin1.clone()
+        per_prev, fin_prev = per, fin
+    else:
+        out, per, fin = alloc_outputs(t2, 16, persist_dtype)
+        per_prev, fin_prev = per1, fin1
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gb.gdn_commit_verify_chain(acc, per_prev, t2["q"], t2["k"], t2["v"], t2["alpha"], t2["beta"], st,
+                               final_prev=fin_prev, out=out, persist=per, final_state=fin, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(st, st_ref)
+    assert torch.equal(out, out_r) and torch.equal(per, per_r) and torch.equal(fin, fin_r)
+
+
+def test_fused_decode_loop_matches_oracle():
+    """Three fused steps (accepted lengths 5, 16, 1) against the oracle applied step by step."""
+    B, N = 2, 16
+    steps = [small_inputs(31 + i, B, N, 2, 4, 128, 128)[1] for i in range(3)]
+    accs = [np.array([4, 9], np.int32), np.array([15, 15], np.int32), np.array([0, 7], np.int32)]
+    st = dev_inputs(steps[0])["state0"].clone()
+    ref_state = steps[0]["state0"].astype(np.float64)
+    per_prev = fin_prev = acc_prev = None
+    for i, d in enumerate(steps):
+        t = dev_inputs(d)
+        out, per, fin = alloc_outputs(t, N)
+        if i == 0:
+            gb.gdn_verify_chain(t["q"], t["k"], t["v"], t["alpha"], t["beta"], st, out=out, persist=per,
+                                final_state=fin)
+        else:
+            gb.gdn_commit_verify_chain(acc_prev, per_prev, t["q"], t["k"], t["v"], t["alpha"], t["beta"], st,
+                                       final_prev=fin_prev, out=out, persist=per, final_state=fin)
+        torch.cuda.synchronize()
+        ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], ref_state)
+        assert max_rel(to_host(out), ref["out"]) <= OUT_TOL
+        assert max_rel(to_host(per), ref["nodes"]) <= PERSIST_TOL
+        ref_state, _ = oracle.commit(ref_state, ref["nodes"], accs[i], final=ref["final"])
+        # the committed state the next step reads comes from the f16 copy unless fully accepted
+        acc_prev = torch.from_numpy(accs[i]).to(DEV)
+        per_prev, fin_prev = per, fin
+    assert _commit(acc_prev, per_prev, st, final=fin_prev) == 0
+    assert max_rel(to_host(st), ref_state) <= STATE_TOL
+
+
+def test_fused_bad_accepted_node_skips_sequence():
+    w, d = small_inputs(41, 3, 8, 1, 2, 64, 64)
+    t = dev_inputs(d)
+    out1, per1, fin1 = run_chain(t, 8)
+    st = t["state0"].clone()
+    out, per, fin = alloc_outputs(t, 8)
+    out.zero_(); per.zero_(); fin.zero_()
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    acc = torch.tensor([2, 8, 5], dtype=torch.int32, device=DEV)
+    gb.gdn_commit_verify_chain(acc, per1, t["q"], t["k"], t["v"], t["alpha"], t["beta"], st, final_prev=fin1,
+                               out=out, persist=per, final_state=fin, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == gb.CODES["GDN_ERR_NODE"]
+    assert torch.equal(st[1], t["state0"][1]) and torch.count_nonzero(per[1]) == 0
+    assert torch.equal(st[0], per1[0, 2].float()) and torch.equal(st[2], per1[2, 5].float())
