@@ -208,7 +208,7 @@ def main() -> int:
                                 "verify_gbs": ledger["verify_total"] / (verify_ms * 1e-3) / 1e9},
         },
         "roofline": {
-            "kernel": "verify_chain_kernel<128,1,f16 persist,f32 out> with the fused commit",
+            "kernel": "commit_verify_chain_kernel<128,1,f16 persist,f32 out,nt>",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

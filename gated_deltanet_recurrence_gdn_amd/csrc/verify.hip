@@ -345,6 +345,13 @@ __global__ __launch_bounds__(256) void verify_chain_kernel(const VerifyArgs a) {
     verify_body<DK, M, false, PMODE, OUT, NT>(a, nullptr);
 }
 
+// The fused commit + verify launch: the same body, under its own symbol so kernel
+// traces and counters tell it apart from a plain verify.
+template <int DK, int M, int PMODE, int OUT, bool NT>
+__global__ __launch_bounds__(256) void commit_verify_chain_kernel(const VerifyArgs a) {
+    verify_body<DK, M, false, PMODE, OUT, NT>(a, nullptr);
+}
+
 template <int DK, int M, int PMODE, int OUT>
 __global__ __launch_bounds__(256) void verify_tree_kernel(const VerifyArgs a, const TreeSched t) {
     const int bl = xcd_logical_block(blockIdx.x, gridDim.x) / (a.slices * a.h_v);
@@ -355,6 +362,12 @@ template <int DK, int M, int PMODE, int OUT>
 hipError_t launch_one(const VerifyArgs& a, const TreeSched* t, int waves, size_t lds, int grid, hipStream_t st) {
     if (t != nullptr)
         hipLaunchKernelGGL((verify_tree_kernel<DK, M, PMODE, OUT>), dim3(grid), dim3(64 * waves), lds, st, a, *t);
+    else if (a.accepted_prev != nullptr && a.nt_stores)
+        hipLaunchKernelGGL((commit_verify_chain_kernel<DK, M, PMODE, OUT, true>), dim3(grid), dim3(64 * waves), lds,
+                           st, a);
+    else if (a.accepted_prev != nullptr)
+        hipLaunchKernelGGL((commit_verify_chain_kernel<DK, M, PMODE, OUT, false>), dim3(grid), dim3(64 * waves), lds,
+                           st, a);
     else if (a.nt_stores)
         hipLaunchKernelGGL((verify_chain_kernel<DK, M, PMODE, OUT, true>), dim3(grid), dim3(64 * waves), lds, st, a);
     else
