@@ -102,11 +102,24 @@ __device__ __forceinline__ h8 raw_to_h8(const Raw8& r, bool valid) {
     return to_h8(x);
 }
 
+// Row order of the scan's 16-row tiles (see the scan kernel): row c of tile
+// `tile` when tiles (2u, 2u+1) form one 32-wide contraction block.
+__device__ __forceinline__ int pair_row(int tile, int c) {
+    return 32 * (tile >> 1) + 8 * (c >> 2) + 4 * (tile & 1) + (c & 3);
+}
+
 // Workspace layout (bytes), per sequence b and chunk c:
-//   T, P   [B][nch][h_v][C][C]     f16
-//   gates  [B][nch][h_v][3][C]     fp32: gamma_t, beta_t, Gamma_{C,t}
-//   KT     [B][nch][h_qk][d_k][C]  f16   (K transposed)
-//   K, Q   [B][nch][h_qk][C][d_k]  f16   (converted once, read by every slice)
+//   T', P  [B][nch][h_v][C x C]     f16, T' = T diag(beta)
+//   gates  [B][nch][h_v][3][C]      fp32: gamma_t, beta_t, Gamma_{C,t}
+//   KT     [B][nch][h_qk][d_k x C]  f16   (K transposed)
+//   K, Q   [B][nch][h_qk][C x d_k]  f16
+// The matrices are stored in the scan's operand-fragment order: fragment f
+// (1 KB) holds, for lane l = 16 g + c, the 8 contraction-consecutive values of
+// row pair_row(tile, c) starting at column 32 (block) + 8 g, at f * 1 KB + 16 l.
+// K and Q: f = tile * (d_k / 32) + block over the C x d_k matrix; KT:
+// f = tile * 2 + block over the d_k x C matrix; T' and P: the six
+// lower-triangular (tile, block) pairs in the order (0,0) (1,0) (2,0) (2,1)
+// (3,0) (3,1).  So every load of the scan is one contiguous kilobyte.
 struct WsLayout {
     size_t T, P, G, KT, K, Q, total;
 };
@@ -213,18 +226,24 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         gw[kC + lane] = L.be[lane];
         gw[2 * kC + lane] = expf(lC - x);
     } else if (h % a.group == 0) {
+        // K^T, K, Q in fragment order, one 16-byte piece (fragment f, lane l) per step
         _Float16* kt = reinterpret_cast<_Float16*>(wsb + ws.KT) + unit_q * DK * kC;
         _Float16* kw = reinterpret_cast<_Float16*>(wsb + ws.K) + unit_q * kC * DK;
         _Float16* qw = reinterpret_cast<_Float16*>(wsb + ws.Q) + unit_q * kC * DK;
-        for (int e = tid - 64; e < DK * (kC / 8); e += 192) {
-            const int d = e / (kC / 8), tt = 8 * (e % (kC / 8));
+        constexpr int PIECES = DK * kC / 8;
+        for (int e = tid - 64; e < 3 * PIECES; e += 192) {
+            const int m = e / PIECES, i = e % PIECES;
+            const int f = i / 64, l = i % 64, c = l & 15, lg = l >> 4;
             h8 v;
+            if (m == 0) {
+                const int dk = pair_row(f / 2, c), t0 = 32 * (f % 2) + 8 * lg;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = L.u.in.Kf[(tt + i) * kLdK + d];
-            *reinterpret_cast<h8*>(kt + d * kC + tt) = v;
-            const int t = e / (DK / 8), dd = 8 * (e % (DK / 8));
-            *reinterpret_cast<h8*>(kw + t * DK + dd) = *reinterpret_cast<const h8*>(&L.u.in.Kf[t * kLdK + dd]);
-            *reinterpret_cast<h8*>(qw + t * DK + dd) = *reinterpret_cast<const h8*>(&L.u.in.Qf[t * kLdK + dd]);
+                for (int x = 0; x < 8; ++x) v[x] = L.u.in.Kf[(t0 + x) * kLdK + dk];
+            } else {
+                const int row = pair_row(f / KSD, c), col = 32 * (f % KSD) + 8 * lg;
+                v = *reinterpret_cast<const h8*>(&(m == 1 ? L.u.in.Kf : L.u.in.Qf)[row * kLdK + col]);
+            }
+            *reinterpret_cast<h8*>((m == 0 ? kt : m == 1 ? kw : qw) + 8 * i) = v;
         }
     }
     __syncthreads();
@@ -330,307 +349,455 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         __syncthreads();
     }
 
-    // 5. T (f16, zero above the diagonal) and P -> workspace, 16-byte stores
+    // 5. T' = T diag(beta) (f16, zero above the diagonal) and P -> workspace in
+    //    fragment order (the six lower-triangular fragments), 16-byte stores
     _Float16* Tw = reinterpret_cast<_Float16*>(wsb + ws.T) + unit_v * kC * kC;
     _Float16* Pw = reinterpret_cast<_Float16*>(wsb + ws.P) + unit_v * kC * kC;
-    for (int e = tid; e < kC * kC / 8; e += 256) {
-        const int t = e / (kC / 8), i0 = 8 * (e % (kC / 8));
-        h8 tv;
+    for (int e = tid; e < 2 * 6 * 64; e += 256) {
+        const int m = e / (6 * 64), i = e % (6 * 64);
+        const int f = i / 64, l = i % 64;
+        const int tile = f < 2 ? f : 2 + (f - 2) / 2, blk = f < 2 ? 0 : (f - 2) % 2;
+        const int t = pair_row(tile, l & 15), i0 = 32 * blk + 8 * (l >> 4);
+        h8 v;
+        if (m == 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) tv[i] = (_Float16)((i0 + i <= t) ? L.u.ut.Tm[t * kLdF + i0 + i] : 0.f);
-        *reinterpret_cast<h8*>(Tw + t * kC + i0) = tv;
-        *reinterpret_cast<h8*>(Pw + t * kC + i0) = *reinterpret_cast<const h8*>(&L.P[t * kLdT + i0]);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// scan: one (sequence, value head, 32 value columns) per workgroup
-// ---------------------------------------------------------------------------
-template <int DK>
-struct ScanLds {
-    static constexpr int kLdK = DK + 8;
-    _Float16 Kf[kC * kLdK];    // K chunk [token][d_k]
-    _Float16 Qf[kC * kLdK];    // Q chunk [token][d_k]
-    _Float16 KT[DK * kLdT];    // K^T [d_k][token]
-    _Float16 Tt[kC * kLdT];    // T [token][token]
-    _Float16 P[kC * kLdT];     // Gamma o tril(Q K^T)
-    _Float16 Vs[kC * (kDVS + 8)];  // V slice [token][value col]
-    _Float16 RT[kDVS * kLdT];  // R^T [value col][token]
-    _Float16 UT[kDVS * kLdT];  // U^T
-    _Float16 UG[kDVS * kLdT];  // (Gamma_{C,t} U)^T
-    _Float16 Sf[kDVS * kLdK];  // state slice (f16) [value col][d_k]
-    float Os[kC * (kDVS + 4)]; // this chunk's outputs (fp32) [token][value col]
-    float gam[kC], bet[kC], gC[kC];
-};
-
-template <int DK>
-struct ScanRegs {
-    static constexpr int NK = kC * DK / 8 / 256;  // 16-byte chunks per thread of K (and Q, K^T)
-    u32x4 k[NK], q[NK], kt[NK], tt[2], pp[2];
-    Raw8 v;
-    float g0, g1, g2;
-};
-
-// Issue every global load of chunk ck (token indices clamped into the
-// sequence; the invalid rows are zeroed when stored).
-template <int DK, bool BF16>
-__device__ __forceinline__ void scan_load(ScanRegs<DK>& R, const PrefillArgs& a, const unsigned char* wsb,
-                                          const WsLayout& ws, int b, int h, int g, int ck, int nch, int col0,
-                                          int tid) {
-    constexpr int NK = ScanRegs<DK>::NK;
-    const int t0 = ck * kC;
-    const int tmax = a.T - 1;
-    const size_t unit_v = ((size_t)b * nch + ck) * a.h_v + h;
-    const size_t unit_q = ((size_t)b * nch + ck) * a.h_qk + g;
-    const uint16_t* ktw = reinterpret_cast<const uint16_t*>(wsb + ws.KT) + unit_q * DK * kC;
-    const uint16_t* kw = reinterpret_cast<const uint16_t*>(wsb + ws.K) + unit_q * kC * DK;
-    const uint16_t* qw = reinterpret_cast<const uint16_t*>(wsb + ws.Q) + unit_q * kC * DK;
-#pragma unroll
-    for (int n = 0; n < NK; ++n) {
-        R.k[n] = *reinterpret_cast<const u32x4*>(kw + 8 * (tid + 256 * n));
-        R.q[n] = *reinterpret_cast<const u32x4*>(qw + 8 * (tid + 256 * n));
-        R.kt[n] = *reinterpret_cast<const u32x4*>(ktw + 8 * (tid + 256 * n));
-    }
-    const uint16_t* tw = reinterpret_cast<const uint16_t*>(wsb + ws.T) + unit_v * kC * kC;
-    const uint16_t* pw = reinterpret_cast<const uint16_t*>(wsb + ws.P) + unit_v * kC * kC;
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        R.tt[n] = *reinterpret_cast<const u32x4*>(tw + 8 * (tid + 256 * n));
-        R.pp[n] = *reinterpret_cast<const u32x4*>(pw + 8 * (tid + 256 * n));
-    }
-    {
-        const int t = tid / (kDVS / 8), j = 8 * (tid % (kDVS / 8));
-        const int tc = t0 + t < tmax ? t0 + t : tmax;
-        raw_load<BF16>(R.v, a.v, (((size_t)b * a.T + tc) * a.h_v + h) * a.d_v + col0 + j);
-    }
-    const float* gw = reinterpret_cast<const float*>(wsb + ws.G) + unit_v * 3 * kC;
-    R.g0 = gw[tid & 63];
-    R.g1 = gw[kC + (tid & 63)];
-    R.g2 = gw[2 * kC + (tid & 63)];
-}
-
-template <int DK, bool BF16>
-__device__ __forceinline__ void scan_store(const ScanRegs<DK>& R, ScanLds<DK>& L, int tid, int t0, int T) {
-    constexpr int NK = ScanRegs<DK>::NK;
-    constexpr int kLdK = DK + 8;
-#pragma unroll
-    for (int n = 0; n < NK; ++n) {
-        const int e = tid + 256 * n;
-        const int t = e / (DK / 8), d = 8 * (e % (DK / 8));
-        *reinterpret_cast<u32x4*>(&L.Kf[t * kLdK + d]) = R.k[n];  // zero rows past T come from prepare
-        *reinterpret_cast<u32x4*>(&L.Qf[t * kLdK + d]) = R.q[n];
-        const int dd = e / (kC / 8), tt = 8 * (e % (kC / 8));
-        *reinterpret_cast<u32x4*>(&L.KT[dd * kLdT + tt]) = R.kt[n];
-    }
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int e = tid + 256 * n;
-        const int t = e / (kC / 8), i0 = 8 * (e % (kC / 8));
-        *reinterpret_cast<u32x4*>(&L.Tt[t * kLdT + i0]) = R.tt[n];
-        *reinterpret_cast<u32x4*>(&L.P[t * kLdT + i0]) = R.pp[n];
-    }
-    {
-        const int t = tid / (kDVS / 8), j = 8 * (tid % (kDVS / 8));
-        *reinterpret_cast<h8*>(&L.Vs[t * (kDVS + 8) + j]) = raw_to_h8<BF16>(R.v, t0 + t < T);
-    }
-    if (tid < kC) {
-        L.gam[tid] = R.g0;
-        L.bet[tid] = R.g1;
-        L.gC[tid] = R.g2;
-    }
-}
-
-// One chunk's outputs, staged in LDS as fp32 [token][value col] and written
-// out as 16-byte rows of the output dtype.
-template <int OUT>
-__device__ __forceinline__ void write_out(const float* Os, const PrefillArgs& a, int b, int h, int col0, int t0,
-                                          int tid) {
-    constexpr int EPT = OUT == 0 ? 4 : 8;  // elements per 16-byte store
-    constexpr int PER_ROW = kDVS / EPT;
-    for (int e = tid; e < kC * PER_ROW; e += 256) {
-        const int t = e / PER_ROW, j = EPT * (e % PER_ROW);
-        if (t0 + t >= a.T) continue;
-        const float* src = Os + t * (kDVS + 4) + j;
-        const size_t idx = (((size_t)b * a.T + t0 + t) * a.h_v + h) * a.d_v + col0 + j;
-        if constexpr (OUT == 0) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + idx) = *reinterpret_cast<const f32x4*>(src);
-        } else if constexpr (OUT == 2) {
-            h8 v;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = (_Float16)src[i];
-            *reinterpret_cast<h8*>(static_cast<_Float16*>(a.out) + idx) = v;
+            for (int x = 0; x < 8; ++x)
+                v[x] = (_Float16)((i0 + x <= t) ? L.u.ut.Tm[t * kLdF + i0 + x] * L.be[i0 + x] : 0.f);
         } else {
-            u32x4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                v[i] = (uint32_t)f32_to_bf16(src[2 * i]) | ((uint32_t)f32_to_bf16(src[2 * i + 1]) << 16);
-            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + idx) = v;
+            v = *reinterpret_cast<const h8*>(&L.P[t * kLdT + i0]);
         }
+        *reinterpret_cast<h8*>((m == 0 ? Tw : Pw) + 8 * i) = v;
     }
+}
+
+// ---------------------------------------------------------------------------
+// scan: one workgroup of two waves per (sequence, value head, 32 value columns)
+// ---------------------------------------------------------------------------
+// Value columns never mix in the recurrence (R, U, O and the state update act
+// on each column of H separately), so each wave owns 16 columns of one head
+// for the whole prompt.  The state slice H[:, j0 .. j0+16) stays in
+// accumulators, and every product's result feeds the next product from the
+// lane that produced it, because 16-row tiles are paired into 32-wide
+// contraction blocks with a matching row order:
+//   the accumulator of a 16 x 16 x 32 product gives lane (c, g) = (lane % 16,
+//   lane / 16) rows 4g .. 4g+3; the B operand wants rows 8g .. 8g+7 of a
+//   32-row block.  Tile pair (2u, 2u+1) therefore covers rows
+//   32u + 8g + 4h + r of the block (h = tile & 1, r = 0..3), and the A operand
+//   of the producing product reads its row c from pair_row(tile, c).
+// So K H and Q H take the state as B straight from the accumulators, U = T' R
+// takes R = V - gamma K H, and O and the state update take U, all without
+// moving data between lanes.
+//
+// The two waves read the same A operands (K, Q, K^T, T', P of their head), so
+// the workgroup brings each chunk's operands into LDS once: buffer loads that
+// write LDS directly (no registers), split between the waves, one chunk
+// ahead into the other half of a double buffer.  The LDS copy is in fragment
+// order -- fragment f, lane l at f * 1 KB + 16 l -- so every operand read is
+// one conflict-free 16-byte LDS read.  One barrier per chunk: each wave waits
+// for its own loads of the chunk, then the barrier publishes both halves and
+// also tells each wave that the other has finished with the buffer about to
+// be refilled.
+__device__ __forceinline__ h8 pack_h8(const f32x4& lo, const f32x4& hi) {
+    h8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = (_Float16)lo[i];
+        r[4 + i] = (_Float16)hi[i];
+    }
+    return r;
+}
+
+// Buffer resources: a uniform base per matrix and chunk, bounded by its size,
+// so a load past it returns zero and a store past it is dropped (the rows of a
+// ragged last chunk past T).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// One chunk's block in LDS.  Fragments (1 KB each): K [p][u], Q [p][u],
+// K^T [t][v], then T' and P over the lower-triangular (p, v <= p / 2) pairs;
+// then V rows [64][32 columns] in the input dtype, then gamma_t and Gamma_{C,t}.
+template <int DK, bool BF16>
+struct ChunkBlock {
+    static constexpr int NT = DK / 16, KB = DK / 32, NP = kC / 16, VB = kC / 32;
+    static constexpr int NTRI = 6;  // (p, v): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+    static constexpr int K0 = 0, Q0 = K0 + NP * KB, KT0 = Q0 + NP * KB, T0 = KT0 + NT * VB, P0 = T0 + NTRI;
+    static constexpr int NFRAG = P0 + NTRI;
+    static constexpr int VROW = 32 * (BF16 ? 2 : 4);  // bytes of one V row (32 columns)
+    static constexpr int NVI = kC * VROW / 1024;      // V loads
+    static constexpr int V0 = NFRAG * 1024;
+    static constexpr int G0 = V0 + kC * VROW;         // gamma [64], Gamma_C [64] (fp32)
+    static constexpr int BYTES = G0 + 2 * kC * 4;
+    static constexpr int NLOAD = NFRAG + NVI + 2;     // load instructions per chunk
+};
+__device__ __forceinline__ constexpr int tri(int p, int v) { return p < 2 ? p : 2 * p - 2 + v; }
+
+template <int DK>
+struct ScanCtx {
+    static constexpr int NT = DK / 16, NP = kC / 16;
+    const PrefillArgs* a;
+    const unsigned char* wsb;
+    WsLayout ws;
+    int b, h, g, nch, col0;   // col0: first value column of the workgroup
+    __device__ int clamp_ck(int ck) const { return ck < nch ? ck : nch - 1; }
+    __device__ rsrc_t ws_v(size_t arr, uint32_t per_unit, int ck) const {
+        return make_rsrc(wsb + arr + (((size_t)b * nch + clamp_ck(ck)) * a->h_v + h) * per_unit, per_unit);
+    }
+    __device__ rsrc_t ws_q(size_t arr, uint32_t per_unit, int ck) const {
+        return make_rsrc(wsb + arr + (((size_t)b * nch + clamp_ck(ck)) * a->h_qk + g) * per_unit, per_unit);
+    }
+    // the workgroup's columns of the rows of chunk ck of a [B][T][h_v][d_v]
+    // tensor, bounded at the sequence's last token
+    __device__ rsrc_t rows(const void* base, int esz, int ck) const {
+        const int t0 = clamp_ck(ck) * kC;
+        const int n = a->T - t0 < kC ? a->T - t0 : kC;
+        const size_t row = (size_t)a->h_v * a->d_v;
+        return make_rsrc(static_cast<const unsigned char*>(base) +
+                             (((size_t)b * a->T + t0) * row + (size_t)h * a->d_v + col0) * esz,
+                         (uint32_t)(((size_t)(n - 1) * row + 32) * esz));
+    }
+};
+
+// Loads of one chunk into an LDS block.  ChunkBlock's load instructions are
+// split between the two waves: wave w issues instruction i = 2 k + w for slot
+// k.  Every matrix boundary in that list is even, so both instructions of a
+// slot read the same matrix and the slot's code is the same for both waves;
+// the wave enters only through per-lane offsets and a uniform LDS base.
+struct DmaCtx {
+    rsrc_t kw, qw, ktw, tw, pw, gw, vw;
+    uint32_t vf, vv, vg;  // per-lane source offsets of fragment, V and gate loads (this wave's)
+    uint32_t vstep;       // source bytes between V loads n and n + 1
+    unsigned char* dst;   // LDS block + 1 KB w
+    unsigned char* gdst;  // LDS gate area + 256 B w
+};
+
+template <int DK, bool BF16>
+__device__ __forceinline__ DmaCtx dma_ctx(const ScanCtx<DK>& X, int ck, unsigned char* blk, int w) {
+    using CB = ChunkBlock<DK, BF16>;
+    const PrefillArgs& a = *X.a;
+    constexpr int VSZ = BF16 ? 2 : 4;
+    constexpr int RPL = 1024 / CB::VROW;  // V rows per load
+    const int lane = threadIdx.x & 63;
+    const uint32_t rowb = (uint32_t)(a.h_v * a.d_v * VSZ);
+    DmaCtx d;
+    d.kw = X.ws_q(X.ws.K, kC * DK * 2, ck);
+    d.qw = X.ws_q(X.ws.Q, kC * DK * 2, ck);
+    d.ktw = X.ws_q(X.ws.KT, DK * kC * 2, ck);
+    d.tw = X.ws_v(X.ws.T, kC * kC * 2, ck);
+    d.pw = X.ws_v(X.ws.P, kC * kC * 2, ck);
+    d.gw = X.ws_v(X.ws.G, 3 * kC * 4, ck);
+    d.vw = X.rows(a.v, VSZ, ck);
+    // fragments are stored in load order: lane l of fragment f at f KB + 16 l
+    d.vf = 16 * lane + 1024 * w;
+    // V load n, lane l: row n RPL + 16 l / VROW, byte (16 l) % VROW of the workgroup's columns
+    d.vv = (uint32_t)((16 * lane / CB::VROW + RPL * w) * rowb + (16 * lane) % CB::VROW);
+    d.vstep = RPL * rowb;
+    // gamma (wave 0) and Gamma_C (wave 1), 64 fp32 each
+    d.vg = 4 * lane + 2 * kC * 4 * w;
+    d.dst = blk + 1024 * w;
+    d.gdst = blk + CB::G0 + kC * 4 * w;
+    return d;
+}
+
+template <int DK, bool BF16, int K>
+__device__ __forceinline__ void dma_slot(const DmaCtx& d) {
+    using CB = ChunkBlock<DK, BF16>;
+    constexpr int i0 = 2 * K;
+    if constexpr (i0 < CB::NFRAG) {
+        constexpr int base = i0 < CB::Q0 ? CB::K0 : i0 < CB::KT0 ? CB::Q0 : i0 < CB::T0 ? CB::KT0 : i0 < CB::P0 ? CB::T0 : CB::P0;
+        const rsrc_t r = i0 < CB::Q0 ? d.kw : i0 < CB::KT0 ? d.qw : i0 < CB::T0 ? d.ktw : i0 < CB::P0 ? d.tw : d.pw;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(d.dst + 1024 * i0), 16, d.vf, 1024 * (i0 - base), 0, 0);
+    } else if constexpr (i0 < CB::NFRAG + CB::NVI) {
+        constexpr int n0 = i0 - CB::NFRAG;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.vw, (lds_void*)(d.dst + 1024 * i0), 16, d.vv, n0 * d.vstep, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.gw, (lds_void*)d.gdst, 4, d.vg, 0, 0, 0);
+    }
+}
+
+template <int DK, bool BF16, int K, int KEND>
+__device__ __forceinline__ void dma_slots(const DmaCtx& d) {
+    if constexpr (K < KEND) {
+        dma_slot<DK, BF16, K>(d);
+        dma_slots<DK, BF16, K + 1, KEND>(d);
+    }
+}
+
+__device__ __forceinline__ h8 frag_at(const unsigned char* blk, int f) {
+    return *reinterpret_cast<const h8*>(blk + f * 1024 + 16 * (threadIdx.x & 63));
+}
+
+// Output rows staged in LDS per wave: row t at t * RB + (t / 8) * 32 (the skew
+// keeps the four rows one store instruction touches on different banks).
+template <int OUT>
+struct OStage {
+    static constexpr int ESZ = OUT == 0 ? 4 : 2;
+    static constexpr int RB = 16 * ESZ;
+    static constexpr int BYTES = kC * RB + (kC / 8) * 32;
+    __device__ static int at(int t) { return t * RB + (t >> 3) * 32; }
+};
+
+// The staged outputs of chunk ck -> HBM, 16-byte stores of whole row pieces.
+template <int DK, int OUT>
+__device__ __forceinline__ void write_out(const ScanCtx<DK>& X, const unsigned char* ost, int ck, int w) {
+    using OS = OStage<OUT>;
+    const PrefillArgs& a = *X.a;
+    const int lane = threadIdx.x & 63;
+    const rsrc_t ow = X.rows(a.out, OS::ESZ, ck);
+    const uint32_t rstride = (uint32_t)(a.h_v * a.d_v * OS::ESZ);
+    constexpr int PER_ROW = OS::RB / 16;  // 16-byte pieces per row
+#pragma unroll
+    for (int n = 0; n < PER_ROW; ++n) {
+        const int t = lane, piece = n;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ost + OS::at(t) + 16 * piece);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ow, t * rstride + (16 * w) * OS::ESZ + 16 * piece, 0, 0);
+    }
+}
+
+template <int OUT>
+__device__ __forceinline__ void stage_o(unsigned char* ost, int t, int c, float o) {
+    unsigned char* p = ost + OStage<OUT>::at(t) + c * OStage<OUT>::ESZ;
+    if constexpr (OUT == 0) *reinterpret_cast<float*>(p) = o;
+    else if constexpr (OUT == 2) *reinterpret_cast<_Float16*>(p) = (_Float16)o;
+    else *reinterpret_cast<uint16_t*>(p) = f32_to_bf16(o);
+}
+
+// The products of one chunk as one static sequence of MFMA steps, each with
+// its A fragment from LDS:
+//   K H (u-major, 4 independent accumulators) | first half of Q H |
+//   U = T' R | second half of Q H | state update (v-major) | O += P U
+// The Q H steps, which only need the chunk's starting state, fill the
+// latency between K H and R and between U and its f16 copies.  Fragment reads
+// run D steps ahead of their MFMA; the next chunk's loads into the other LDS
+// block are spread over the steps; the order is pinned with scheduling
+// barriers.
+template <int DK>
+struct Plan {
+    static constexpr int NT = DK / 16, KB = DK / 32, NP = kC / 16, VB = kC / 32;
+    static constexpr int NKH = NP * KB, NQ = NP * KB, NQ1 = NQ / 2, NU = 6, NST = NT * VB, NPU = 6;
+    static constexpr int S_QH1 = NKH, S_U = S_QH1 + NQ1, S_QH2 = S_U + NU, S_ST = S_QH2 + (NQ - NQ1);
+    static constexpr int S_PU = S_ST + NST, S_END = S_PU + NPU;
+    static constexpr int D = 6;        // fragment reads in flight ahead of the MFMAs
+    static constexpr int NEXTRA = 25;  // V (16), gamma (4), Gamma_C (4), gamma_C (1) reads
+};
+// the (tile, block) pairs of U = T' R and O += P U, block-major
+__device__ __forceinline__ constexpr int tri_p(int k) { return k < 4 ? k : k - 2; }
+__device__ __forceinline__ constexpr int tri_v(int k) { return k < 4 ? 0 : 1; }
+
+template <int DK>
+__device__ __forceinline__ constexpr int frag_of(int s) {
+    using PL = Plan<DK>;
+    using CB = ChunkBlock<DK, true>;  // fragment indices do not depend on the V dtype
+    if (s < PL::S_QH1) return CB::K0 + (s % PL::NP) * PL::KB + s / PL::NP;
+    if (s < PL::S_U) return CB::Q0 + ((s - PL::S_QH1) % PL::NP) * PL::KB + (s - PL::S_QH1) / PL::NP;
+    if (s < PL::S_QH2) return CB::T0 + tri(tri_p(s - PL::S_U), tri_v(s - PL::S_U));
+    if (s < PL::S_ST) {
+        const int q = s - PL::S_QH2 + PL::NQ1;
+        return CB::Q0 + (q % PL::NP) * PL::KB + q / PL::NP;
+    }
+    if (s < PL::S_PU) return CB::KT0 + ((s - PL::S_ST) % PL::NT) * PL::VB + (s - PL::S_ST) / PL::NT;
+    return CB::P0 + tri(tri_p(s - PL::S_PU), tri_v(s - PL::S_PU));
+}
+
+template <int DK>
+struct ChunkRegs {
+    using PL = Plan<DK>;
+    h8 sb[PL::KB];
+    f32x4 kh[PL::NP], uu[PL::NP], o[PL::NP];
+    h8 rb[PL::VB], ub[PL::VB], ug[PL::VB];
+    h8 fa[PL::S_END];
+    float vx[PL::NP][4];
+    f32x4 gp[PL::NP], gq[PL::NP];
+    float gC;
+};
+
+template <int DK, bool BF16, int E>
+__device__ __forceinline__ void extra_read(ChunkRegs<DK>& x, const unsigned char* blk, int w) {
+    using CB = ChunkBlock<DK, BF16>;
+    const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
+    const float* gam = reinterpret_cast<const float*>(blk + CB::G0);
+    if constexpr (E < 16) {
+        constexpr int p = E / 4, r = E % 4;
+        const unsigned char* vp = blk + CB::V0 + (pair_row(p, 4 * lg) + r) * CB::VROW + (16 * w + c) * (BF16 ? 2 : 4);
+        if constexpr (BF16) x.vx[p][r] = bf16_lo(*reinterpret_cast<const uint16_t*>(vp));
+        else x.vx[p][r] = *reinterpret_cast<const float*>(vp);
+    } else if constexpr (E < 20) {
+        x.gp[E - 16] = *reinterpret_cast<const f32x4*>(gam + pair_row(E - 16, 4 * lg));
+    } else if constexpr (E < 24) {
+        x.gq[E - 20] = *reinterpret_cast<const f32x4*>(gam + kC + pair_row(E - 20, 4 * lg));
+    } else {
+        x.gC = gam[kC - 1];
+    }
+}
+template <int DK, bool BF16, int E, int EEND>
+__device__ __forceinline__ void extra_reads(ChunkRegs<DK>& x, const unsigned char* blk, int w) {
+    if constexpr (E < EEND) {
+        extra_read<DK, BF16, E>(x, blk, w);
+        extra_reads<DK, BF16, E + 1, EEND>(x, blk, w);
+    }
+}
+
+template <int DK, int OUT, bool BF16, int S>
+__device__ __forceinline__ void chunk_step(ChunkRegs<DK>& x, f32x4 (&st)[DK / 16], const unsigned char* blk,
+                                           unsigned char* ost, float scale, int w, const DmaCtx& d) {
+    using PL = Plan<DK>;
+    using CB = ChunkBlock<DK, BF16>;
+    constexpr int NP = PL::NP, NT = PL::NT, VB = PL::VB, KB = PL::KB;
+    constexpr int NSLOT = CB::NLOAD / 2;
+    if constexpr (S < PL::S_END) {
+        // the next chunk's loads due at this step
+        dma_slots<DK, BF16, S * NSLOT / PL::S_END, (S + 1) * NSLOT / PL::S_END>(d);
+        // A fragment D steps ahead; V and gate reads during the K H steps
+        if constexpr (S + PL::D < PL::S_END) x.fa[S + PL::D] = frag_at(blk, frag_of<DK>(S + PL::D));
+        if constexpr (S < PL::NKH)
+            extra_reads<DK, BF16, S * PL::NEXTRA / PL::NKH, (S + 1) * PL::NEXTRA / PL::NKH>(x, blk, w);
+
+        if constexpr (S == PL::S_U) {
+            // R = V - gamma K H at this lane's rows pair_row(p, 4 lg) + r
+#pragma unroll
+            for (int v = 0; v < VB; ++v)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int p = 2 * v + hh;
+                        x.rb[v][4 * hh + r] = (_Float16)fmaf(-x.gp[p][r], x.kh[p][r], x.vx[p][r]);
+                    }
+        }
+        if constexpr (S == PL::S_ST) {
+            // U in f16, plain and scaled by Gamma_{C,t}; the state decays by gamma_C
+#pragma unroll
+            for (int v = 0; v < VB; ++v) {
+                x.ub[v] = pack_h8(x.uu[2 * v], x.uu[2 * v + 1]);
+                x.ug[v] = pack_h8(x.gq[2 * v] * x.uu[2 * v], x.gq[2 * v + 1] * x.uu[2 * v + 1]);
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) st[t] = x.gC * st[t];
+        }
+        if constexpr (S == PL::S_PU) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) x.o[p] = x.gp[p] * x.o[p];  // gamma Q H
+        }
+
+        if constexpr (S < PL::S_QH1) {
+            constexpr int p = S % NP, u = S / NP;
+            x.kh[p] = mfma16(x.fa[S], x.sb[u], x.kh[p]);
+        } else if constexpr (S < PL::S_U) {
+            constexpr int q = S - PL::S_QH1, p = q % NP, u = q / NP;
+            x.o[p] = mfma16(x.fa[S], x.sb[u], x.o[p]);
+        } else if constexpr (S < PL::S_QH2) {
+            constexpr int p = tri_p(S - PL::S_U), v = tri_v(S - PL::S_U);
+            x.uu[p] = mfma16(x.fa[S], x.rb[v], x.uu[p]);
+        } else if constexpr (S < PL::S_ST) {
+            constexpr int q = S - PL::S_QH2 + PL::NQ1, p = q % NP, u = q / NP;
+            x.o[p] = mfma16(x.fa[S], x.sb[u], x.o[p]);
+        } else if constexpr (S < PL::S_PU) {
+            constexpr int t = (S - PL::S_ST) % NT, v = (S - PL::S_ST) / NT;
+            st[t] = mfma16(x.fa[S], x.ug[v], st[t]);
+        } else {
+            constexpr int p = tri_p(S - PL::S_PU), v = tri_v(S - PL::S_PU);
+            x.o[p] = mfma16(x.fa[S], x.ub[v], x.o[p]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        chunk_step<DK, OUT, BF16, S + 1>(x, st, blk, ost, scale, w, d);
+    } else {
+        // O -> staging (written out at the start of the next chunk)
+        const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) stage_o<OUT>(ost, pair_row(p, 4 * lg) + r, c, scale * x.o[p][r]);
+    }
+}
+
+// One chunk from its LDS block: state update in place, outputs staged, and the
+// next chunk's loads issued (d) along the way.
+template <int DK, int OUT, bool BF16>
+__device__ __forceinline__ void scan_chunk(f32x4 (&st)[DK / 16], const unsigned char* blk, unsigned char* ost,
+                                           float scale, int w, const DmaCtx& d) {
+    using PL = Plan<DK>;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    ChunkRegs<DK> x;
+    // the state as B operand straight from the accumulators
+#pragma unroll
+    for (int u = 0; u < PL::KB; ++u) x.sb[u] = pack_h8(st[2 * u], st[2 * u + 1]);
+#pragma unroll
+    for (int p = 0; p < PL::NP; ++p) x.kh[p] = x.uu[p] = x.o[p] = z;
+#pragma unroll
+    for (int s = 0; s < PL::D; ++s) x.fa[s] = frag_at(blk, frag_of<DK>(s));
+    chunk_step<DK, OUT, BF16, 0>(x, st, blk, ost, scale, w, d);
 }
 
 template <int DK, int OUT, bool BF16>
-__global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs a) {
-    constexpr int kLdK = DK + 8;
-    constexpr int NT = DK / 16;      // d_k tiles
-    constexpr int KSD = DK / 32;     // contraction steps over d_k
-    constexpr int STW = 2 * NT / 4;  // state tiles per wave
+struct ScanLayout {
+    static constexpr int BLK = ChunkBlock<DK, BF16>::BYTES;
+    static constexpr int OST = OStage<OUT>::BYTES;
+    static constexpr int BYTES = 2 * BLK + 2 * OST;
+};
+
+template <int DK, int OUT, bool BF16>
+__global__ __launch_bounds__(128) void prefill_scan_kernel(const PrefillArgs a) {
+    using L = ScanLayout<DK, OUT, BF16>;
+    constexpr int NT = DK / 16;
     extern __shared__ __align__(16) unsigned char lds_raw[];
-    ScanLds<DK>& L = *reinterpret_cast<ScanLds<DK>*>(lds_raw);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int c = lane & 15, lg = lane >> 4;
     int blk = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int slice = blk % a.slices;
+    const int pair = blk % a.slices;
     blk /= a.slices;
-    const int h = blk % a.h_v;
-    const int b = blk / a.h_v;
-    const int g = h / a.group;
-    const int col0 = slice * kDVS;
-    const int nch = (a.T + kC - 1) / kC;
-    const WsLayout ws = ws_layout(a.batch, nch, a.h_qk, a.h_v, DK);
-    const unsigned char* wsb = static_cast<const unsigned char*>(a.workspace);
+    ScanCtx<DK> X;
+    X.a = &a;
+    X.wsb = static_cast<const unsigned char*>(a.workspace);
+    X.h = blk % a.h_v;
+    X.b = blk / a.h_v;
+    X.g = X.h / a.group;
+    X.nch = (a.T + kC - 1) / kC;
+    X.ws = ws_layout(a.batch, X.nch, a.h_qk, a.h_v, DK);
+    X.col0 = 32 * pair;
 
-    int s = b;
+    int s = X.b;
     if (a.state_slot != nullptr) {
-        s = a.state_slot[b];
+        s = a.state_slot[X.b];
         if (s < 0 || s >= a.n_slots) {
-            if (tid == 0 && a.status != nullptr) a.status[0] = GDN_ERR_SLOT;
-            return;
+            if (threadIdx.x == 0 && a.status != nullptr) a.status[0] = GDN_ERR_SLOT;
+            return;  // uniform over the workgroup: both waves leave before any barrier
         }
     }
-    float* stp = a.state + ((size_t)s * a.h_v + h) * (size_t)a.d_v * DK;
+    // lane (c, g) holds H[d_k][j] = S[j][d_k] for d_k = pair_row(t, 4g + r), r = 0..3
+    const int j = X.col0 + 16 * w + c;
+    float* stp = a.state + (((size_t)s * a.h_v + X.h) * a.d_v + j) * DK;
+    f32x4 st[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[t][r] = stp[pair_row(t, 4 * lg) + r];
 
-    // state tiles: x = wave * STW + y -> value tile x / NT, d_k tile x % NT;
-    // lane holds S[col0 + 16 vt + 4 (lane / 16) + r][16 dt + lane % 16]
-    f32x4 st[STW];
-#pragma unroll
-    for (int y = 0; y < STW; ++y) {
-        const int x = wave * STW + y, vt = x / NT, dt = x % NT;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            st[y][r] = stp[(size_t)(col0 + 16 * vt + 4 * (lane >> 4) + r) * DK + 16 * dt + (lane & 15)];
+    unsigned char* ost = lds_raw + 2 * L::BLK + w * L::OST;
+    {
+        const DmaCtx d0 = dma_ctx<DK, BF16>(X, 0, lds_raw, w);
+        dma_slots<DK, BF16, 0, ChunkBlock<DK, BF16>::NLOAD / 2>(d0);
     }
-#pragma unroll
-    for (int y = 0; y < STW; ++y) {
-        const int x = wave * STW + y, vt = x / NT, dt = x % NT;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            L.Sf[(16 * vt + 4 * (lane >> 4) + r) * kLdK + 16 * dt + (lane & 15)] = (_Float16)st[y][r];
-    }
-
-    ScanRegs<DK> R;
-    scan_load<DK, BF16>(R, a, wsb, ws, b, h, g, 0, nch, col0, tid);
-    const int it = wave;            // row block of the per-token products
-    const int ksmax = it / 2;       // T and P are lower triangular
-    const int tb = 16 * it + 4 * (lane >> 4);  // first token row held by this lane
-    for (int ck = 0; ck < nch; ++ck) {
-        const int t0 = ck * kC;
-        scan_store<DK, BF16>(R, L, tid, t0, a.T);
-        if (ck + 1 < nch) scan_load<DK, BF16>(R, a, wsb, ws, b, h, g, ck + 1, nch, col0, tid);
-        // the previous chunk's outputs leave after this chunk's loads are issued, so the wait
-        // for this chunk's prefetched operands never waits on output stores
-        if (ck > 0) write_out<OUT>(L.Os, a, b, h, col0, t0 - kC, tid);
+    for (int ck = 0; ck < X.nch; ++ck) {
+        // this wave's loads of chunk ck have landed (the wait: loads into LDS count as
+        // vector-memory operations, which the barrier alone does not wait for), the other
+        // wave's too (the barrier); both waves are done with the other half of the buffer
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-
-        // K H and Q H for rows 16 it, both value tiles; R = beta V - beta gamma K H
-        f32x4 oacc[2], kh[2];
-#pragma unroll
-        for (int vt = 0; vt < 2; ++vt) kh[vt] = oacc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-            const h8 ak = frag(L.Kf, kLdK, 16 * it, 32 * ks, lane);
-            const h8 aq = frag(L.Qf, kLdK, 16 * it, 32 * ks, lane);
-#pragma unroll
-            for (int vt = 0; vt < 2; ++vt) {
-                const h8 sb = frag(L.Sf, kLdK, 16 * vt, 32 * ks, lane);
-                kh[vt] = mfma16(ak, sb, kh[vt]);
-                oacc[vt] = mfma16(aq, sb, oacc[vt]);
-            }
-        }
-#pragma unroll
-        for (int vt = 0; vt < 2; ++vt) {
-            const int col = 16 * vt + (lane & 15);
-            h4 r4;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float bt = L.bet[tb + r], gt = L.gam[tb + r];
-                const float vv = (float)L.Vs[(tb + r) * (kDVS + 8) + col];
-                r4[r] = (_Float16)(bt * (vv - gt * kh[vt][r]));
-                oacc[vt][r] *= gt;
-            }
-            *reinterpret_cast<h4*>(&L.RT[col * kLdT + tb]) = r4;
-        }
-        __syncthreads();
-
-        // U = T R
-        f32x4 uacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        for (int ks = 0; ks <= ksmax; ++ks) {
-            const h8 at = frag(L.Tt, kLdT, 16 * it, 32 * ks, lane);
-#pragma unroll
-            for (int vt = 0; vt < 2; ++vt) uacc[vt] = mfma16(at, frag(L.RT, kLdT, 16 * vt, 32 * ks, lane), uacc[vt]);
-        }
-#pragma unroll
-        for (int vt = 0; vt < 2; ++vt) {
-            const f32x4 u = uacc[vt];
-            const int col = 16 * vt + (lane & 15);
-            h4 u4, g4;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                u4[r] = (_Float16)u[r];
-                g4[r] = (_Float16)(L.gC[tb + r] * u[r]);
-            }
-            *reinterpret_cast<h4*>(&L.UT[col * kLdT + tb]) = u4;
-            *reinterpret_cast<h4*>(&L.UG[col * kLdT + tb]) = g4;
-        }
-        __syncthreads();
-
-        // O = scale (gamma Q H + P U) -> LDS (written out with the next chunk's staging)
-        for (int ks = 0; ks <= ksmax; ++ks) {
-            const h8 ap = frag(L.P, kLdT, 16 * it, 32 * ks, lane);
-#pragma unroll
-            for (int vt = 0; vt < 2; ++vt) oacc[vt] = mfma16(ap, frag(L.UT, kLdT, 16 * vt, 32 * ks, lane), oacc[vt]);
-        }
-#pragma unroll
-        for (int vt = 0; vt < 2; ++vt) {
-            const int col = 16 * vt + (lane & 15);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) L.Os[(tb + r) * (kDVS + 4) + col] = a.scale * oacc[vt][r];
-        }
-        // state: H_C = gamma_C H_0 + K^T diag(Gamma_C) U  (as S = H^T on the accumulators)
-        // a wave's state tiles share one value tile (STW <= NT), so one U fragment serves them all
-        const float gc = L.gam[kC - 1];
-        const int vtw = (wave * STW) / NT;
-#pragma unroll
-        for (int y = 0; y < STW; ++y)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) st[y][r] *= gc;
-#pragma unroll
-        for (int ks = 0; ks < kC / 32; ++ks) {
-            const h8 au = frag(L.UG, kLdT, 16 * vtw, 32 * ks, lane);
-#pragma unroll
-            for (int y = 0; y < STW; ++y) {
-                const int dt = (wave * STW + y) % NT;
-                st[y] = mfma16(au, frag(L.KT, kLdT, 16 * dt, 32 * ks, lane), st[y]);
-            }
-        }
-        __syncthreads();  // every read of this chunk's LDS data is done
-#pragma unroll
-        for (int y = 0; y < STW; ++y) {
-            const int x = wave * STW + y, vt = x / NT, dt = x % NT;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                L.Sf[(16 * vt + 4 * (lane >> 4) + r) * kLdK + 16 * dt + (lane & 15)] = (_Float16)st[y][r];
-        }
+        if (ck > 0) write_out<DK, OUT>(X, ost, ck - 1, w);
+        const unsigned char* cur = lds_raw + (ck & 1) * L::BLK;
+        unsigned char* nxt = lds_raw + ((ck + 1) & 1) * L::BLK;
+        // the next chunk (the last chunk loads itself again into the idle block: harmless)
+        const DmaCtx d = dma_ctx<DK, BF16>(X, ck + 1, nxt, w);
+        scan_chunk<DK, OUT, BF16>(st, cur, ost, a.scale, w, d);
     }
-
-    write_out<OUT>(L.Os, a, b, h, col0, (nch - 1) * kC, tid);  // last chunk's outputs
-    // final state, in place
+    write_out<DK, OUT>(X, ost, X.nch - 1, w);
 #pragma unroll
-    for (int y = 0; y < STW; ++y) {
-        const int x = wave * STW + y, vt = x / NT, dt = x % NT;
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            stp[(size_t)(col0 + 16 * vt + 4 * (lane >> 4) + r) * DK + 16 * dt + (lane & 15)] = st[y][r];
-    }
+        for (int r = 0; r < 4; ++r) stp[pair_row(t, 4 * lg) + r] = st[t][r];
 }
 
 template <typename K>
@@ -641,10 +808,10 @@ hipError_t set_lds(K kernel, size_t lds) {
 
 template <int DK, int OUT, bool BF16>
 hipError_t launch_scan(const PrefillArgs& a, int grid, hipStream_t st) {
-    const size_t lds = sizeof(ScanLds<DK>);
+    const size_t lds = ScanLayout<DK, OUT, BF16>::BYTES;
     hipError_t e = set_lds(&prefill_scan_kernel<DK, OUT, BF16>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT, BF16>), dim3(grid), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT, BF16>), dim3(grid), dim3(128), lds, st, a);
     return hipGetLastError();
 }
 
