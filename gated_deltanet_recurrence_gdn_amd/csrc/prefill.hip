@@ -44,6 +44,13 @@ constexpr int kDVS = 32;               // value columns per scan workgroup
 constexpr int kLdT = kC + 8;           // row length (halves) of token-contiguous matrices
 constexpr int kLdF = kC + 4;           // row length (floats) of the fp32 A and T matrices
 constexpr float kLogFloor = -80.f;     // log alpha is clamped here (a zero gate -> e^-80)
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Gate arithmetic runs in base 2 on the hardware's v_log_f32 / v_exp_f32
+// (about 1 ulp each): l2_t = sum log2 alpha_s, clamped per token at
+// kLogFloor / ln 2, and every factor is 2^(difference of l2).
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ f32x4 mfma16(const h8& a, const h8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -210,10 +217,10 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
     }
     __syncthreads();
 
-    // 2. gates (wave 0): l_t by a wave prefix sum; gamma_t, Gamma_{C,t} -> workspace.
+    // 2. gates (wave 0): l_t (base 2) by a wave prefix sum; gamma_t, Gamma_{C,t} -> workspace.
     //    K^T -> workspace (waves 1-3, once per q/k head).
     if (wave == 0) {
-        float x = fmaxf(logf(L.al[lane]), kLogFloor);
+        float x = fmaxf(log2_fast(L.al[lane]), kLogFloor * kLog2e);
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(x, off, 64);
@@ -222,9 +229,9 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         L.ell[lane] = x;
         const float lC = __shfl(x, 63, 64);
         float* gw = reinterpret_cast<float*>(wsb + ws.G) + unit_v * 3 * kC;
-        gw[lane] = expf(x);
+        gw[lane] = exp2_fast(x);
         gw[kC + lane] = L.be[lane];
-        gw[2 * kC + lane] = expf(lC - x);
+        gw[2 * kC + lane] = exp2_fast(lC - x);
     } else if (h % a.group == 0) {
         // K^T, K, Q in fragment order, one 16-byte piece (fragment f, lane l) per step
         _Float16* kt = reinterpret_cast<_Float16*>(wsb + ws.KT) + unit_q * DK * kC;
@@ -275,17 +282,10 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * it + 4 * (lane >> 4) + r;
-            const float gm = expf(L.ell[t] - li);
+            const float gm = exp2_fast(L.ell[t] - li);
             if (mat == 0) L.u.ut.A[t * kLdF + i] = (t > i) ? L.be[t] * gm * gram[jj][r] : 0.f;
             else L.P[t * kLdT + i] = (_Float16)((t >= i) ? gm * gram[jj][r] : 0.f);
         }
-    }
-    // the upper tiles of P are zero
-    for (int e = tid; e < 6 * 256; e += 256) {
-        const int ut = e / 256, w = e % 256;
-        const int it = ut < 3 ? 0 : ut < 5 ? 1 : 2;
-        const int jt = ut < 3 ? 1 + ut : ut < 5 ? ut - 1 : 3;
-        L.P[(16 * it + w / 16) * kLdT + 16 * jt + w % 16] = (_Float16)0.f;
     }
     __syncthreads();
 
@@ -358,13 +358,22 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         const int f = i / 64, l = i % 64;
         const int tile = f < 2 ? f : 2 + (f - 2) / 2, blk = f < 2 ? 0 : (f - 2) % 2;
         const int t = pair_row(tile, l & 15), i0 = 32 * blk + 8 * (l >> 4);
+        // entries above the diagonal are zero (the LDS there holds stale values)
         h8 v;
         if (m == 0) {
+            const f32x4 t0 = *reinterpret_cast<const f32x4*>(&L.u.ut.Tm[t * kLdF + i0]);
+            const f32x4 t1 = *reinterpret_cast<const f32x4*>(&L.u.ut.Tm[t * kLdF + i0 + 4]);
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(&L.be[i0]);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(&L.be[i0 + 4]);
 #pragma unroll
-            for (int x = 0; x < 8; ++x)
-                v[x] = (_Float16)((i0 + x <= t) ? L.u.ut.Tm[t * kLdF + i0 + x] * L.be[i0 + x] : 0.f);
+            for (int x = 0; x < 4; ++x) {
+                v[x] = (_Float16)((i0 + x <= t) ? t0[x] * b0[x] : 0.f);
+                v[4 + x] = (_Float16)((i0 + 4 + x <= t) ? t1[x] * b1[x] : 0.f);
+            }
         } else {
-            v = *reinterpret_cast<const h8*>(&L.P[t * kLdT + i0]);
+            const h8 pv = *reinterpret_cast<const h8*>(&L.P[t * kLdT + i0]);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) v[x] = (i0 + x <= t) ? pv[x] : (_Float16)0.f;
         }
         *reinterpret_cast<h8*>((m == 0 ? Tw : Pw) + 8 * i) = v;
     }
