@@ -5,11 +5,11 @@
 // chunk algebra here is derived from the rule.  With H = S^T (d_k x d_v) and
 // a chunk of C = 64 tokens starting from H_0:
 //   l_t = sum_{s<=t} log alpha_s,  gamma_t = e^{l_t},  Gamma_{t,i} = e^{l_t - l_i}
-//   A   = strict_lower(beta_t Gamma_{t,i} k_t.k_i),  T = (I + A)^{-1}
-//   R   = diag(beta) V - diag(beta gamma) K H_0,     U = T R
+//   A   = strict_lower(beta_t Gamma_{t,i} k_t.k_i),  T = (I + A)^{-1},  T' = T diag(beta)
+//   R   = V - diag(gamma) K H_0,                   U = T' R
 //   O   = scale [diag(gamma) Q H_0 + (Gamma o tril(Q K^T)) U]
 //   H_C = gamma_C H_0 + K^T diag(Gamma_{C,.}) U
-// (U = T R is the usual W / U' form, T diag(beta) V - T diag(beta gamma) K H_0,
+// (U = T' R is the usual W / U' form, T diag(beta) V - T diag(beta gamma) K H_0,
 // with the product by T applied once to the combined right-hand side.)
 //
 // Two kernels.
@@ -18,18 +18,17 @@
 //    K K^T and Q K^T on the matrix cores, the masked matrices, and the UT
 //    transform T = (I + A)^{-1} in fp32 (16 x 16 diagonal blocks by forward
 //    substitution, off-diagonal blocks by v_mfma_f32_16x16x4_f32).  It writes
-//    T and P = Gamma o tril(Q K^T) in f16, the per-token gate factors, and
-//    K^T in f16 (once per q/k head) to the workspace.
-//  * scan (one workgroup per (sequence, value head, 32 value columns),
-//    sequential over chunks): the state slice stays in MFMA accumulators for
-//    the whole prompt; per chunk it forms K H, Q H, R, U = T R, O and the
-//    state update with v_mfma_f32_16x16x32_f16, while the next chunk's
-//    operands are already being loaded into registers.
+//    T' and P = Gamma o tril(Q K^T) in f16, the per-token gate factors, and
+//    K, Q, K^T in f16 (once per q/k head) to the workspace, every matrix in the
+//    scan's operand-fragment order.
+//  * scan (one workgroup of two waves per (sequence, value head, 32 value
+//    columns), sequential over chunks): each wave keeps its 16 columns of the
+//    state in accumulators for the whole prompt; per chunk it forms K H, Q H,
+//    R, U = T' R, O and the state update with v_mfma_f32_16x16x32_f16 from
+//    operands that buffer-to-LDS loads brought in during the previous chunk.
 // All matrix-core operands are f16 with fp32 accumulation: the bf16 inputs are
-// exact in f16 within the f16 range, and the derived operands (T, R, P, U, H)
+// exact in f16 within the f16 range, and the derived operands (T', R, P, U, H)
 // keep f16's 11-bit significand, enough for the parity bar where bf16 is not.
-// Every matrix in LDS keeps its contraction index contiguous, so an operand
-// fragment is one 16-byte LDS read per lane.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -37,10 +36,8 @@ namespace gdn {
 namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = GDN_PREFILL_CHUNK;  // tokens per chunk
-constexpr int kDVS = 32;               // value columns per scan workgroup
 constexpr int kLdT = kC + 8;           // row length (halves) of token-contiguous matrices
 constexpr int kLdF = kC + 4;           // row length (floats) of the fp32 A and T matrices
 constexpr float kLogFloor = -80.f;     // log alpha is clamped here (a zero gate -> e^-80)
