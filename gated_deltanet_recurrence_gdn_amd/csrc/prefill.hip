@@ -448,11 +448,16 @@ struct ScanCtx {
     WsLayout ws;
     int b, h, g, nch, col0;   // col0: first value column of the workgroup
     __device__ int clamp_ck(int ck) const { return ck < nch ? ck : nch - 1; }
+    // the chunk's block of a per-value-head array (per_unit bytes per head and chunk)
     __device__ rsrc_t ws_v(size_t arr, uint32_t per_unit, int ck) const {
-        return make_rsrc(wsb + arr + (((size_t)b * nch + clamp_ck(ck)) * a->h_v + h) * per_unit, per_unit);
+        return make_rsrc(wsb + arr + ((size_t)b * nch * a->h_v + h) * per_unit +
+                             (size_t)(uint32_t)clamp_ck(ck) * (uint32_t)(a->h_v * per_unit),
+                         per_unit);
     }
     __device__ rsrc_t ws_q(size_t arr, uint32_t per_unit, int ck) const {
-        return make_rsrc(wsb + arr + (((size_t)b * nch + clamp_ck(ck)) * a->h_qk + g) * per_unit, per_unit);
+        return make_rsrc(wsb + arr + ((size_t)b * nch * a->h_qk + g) * per_unit +
+                             (size_t)(uint32_t)clamp_ck(ck) * (uint32_t)(a->h_qk * per_unit),
+                         per_unit);
     }
     // the workgroup's columns of the rows of chunk ck of a [B][T][h_v][d_v]
     // tensor, bounded at the sequence's last token
@@ -514,7 +519,11 @@ __device__ __forceinline__ void dma_slot(const DmaCtx& d) {
     if constexpr (i0 < CB::NFRAG) {
         constexpr int base = i0 < CB::Q0 ? CB::K0 : i0 < CB::KT0 ? CB::Q0 : i0 < CB::T0 ? CB::KT0 : i0 < CB::P0 ? CB::T0 : CB::P0;
         const rsrc_t r = i0 < CB::Q0 ? d.kw : i0 < CB::KT0 ? d.qw : i0 < CB::T0 ? d.ktw : i0 < CB::P0 ? d.tw : d.pw;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(d.dst + 1024 * i0), 16, d.vf, 1024 * (i0 - base), 0, 0);
+        // slots pair up inside a matrix and share one LDS base: the instruction offset
+        // (2 KB for the second of a pair) moves the source and the LDS address alike
+        constexpr int pb = base + 4 * ((i0 - base) / 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(d.dst + 1024 * pb), 16, d.vf, 1024 * (pb - base),
+                                                 1024 * (i0 - pb), 0);
     } else if constexpr (i0 < CB::NFRAG + CB::NVI) {
         constexpr int n0 = i0 - CB::NFRAG;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.vw, (lds_void*)(d.dst + 1024 * i0), 16, d.vv, n0 * d.vstep, 0, 0);
