@@ -579,63 +579,80 @@ __device__ __forceinline__ void stage_o(unsigned char* ost, int t, int c, float 
     else *reinterpret_cast<uint16_t*>(p) = f32_to_bf16(o);
 }
 
-// The products of one chunk as one static sequence of MFMA steps, each with
-// its A fragment from LDS:
-//   K H (u-major, 4 independent accumulators) | first half of Q H |
-//   U = T' R | second half of Q H | state update (v-major) | O += P U
-// The Q H steps, which only need the chunk's starting state, fill the
-// latency between K H and R and between U and its f16 copies.  Fragment reads
-// run D steps ahead of their MFMA; the next chunk's loads into the other LDS
-// block are spread over the steps; the order is pinned with scheduling
-// barriers.
+// The products of one chunk, split between two waves per 16-column slice so
+// that each runs on its own SIMD:
+//   chain wave:  K H (u-major) | R = V - gamma K H | U = T' R | U -> LDS |
+//                barrier | state update (v-major) | next state -> LDS
+//   output wave: Q H (from the state in LDS) | barrier | U <- LDS | O += P U |
+//                outputs staged; it also issues the next chunk's loads.
+// Each wave's steps are one static sequence, each MFMA with its A fragment
+// from LDS read D steps ahead; the order is pinned with scheduling barriers.
 template <int DK>
 struct Plan {
     static constexpr int NT = DK / 16, KB = DK / 32, NP = kC / 16, VB = kC / 32;
-    static constexpr int NKH = NP * KB, NQ = NP * KB, NQ1 = NQ / 2, NU = 6, NST = NT * VB, NPU = 6;
-    static constexpr int S_QH1 = NKH, S_U = S_QH1 + NQ1, S_QH2 = S_U + NU, S_ST = S_QH2 + (NQ - NQ1);
-    static constexpr int S_PU = S_ST + NST, S_END = S_PU + NPU;
+    static constexpr int NKH = NP * KB, NU = 6, NST = NT * VB, NQ = NP * KB, NPU = 6;
+    // chain wave
+    static constexpr int A_U = NKH, A_ST = A_U + NU, A_END = A_ST + NST;
+    // output wave
+    static constexpr int B_PU = NQ, B_END = B_PU + NPU;
     static constexpr int D = 6;        // fragment reads in flight ahead of the MFMAs
-    static constexpr int NEXTRA = 25;  // V (16), gamma (4), Gamma_C (4), gamma_C (1) reads
+    static constexpr int NEXTRA = 25;  // chain wave: V (16), gamma (4), Gamma_C (4), gamma_C (1)
 };
 // the (tile, block) pairs of U = T' R and O += P U, block-major
 __device__ __forceinline__ constexpr int tri_p(int k) { return k < 4 ? k : k - 2; }
 __device__ __forceinline__ constexpr int tri_v(int k) { return k < 4 ? 0 : 1; }
 
 template <int DK>
-__device__ __forceinline__ constexpr int frag_of(int s) {
+__device__ __forceinline__ constexpr int frag_a(int s) {  // chain wave, step s
     using PL = Plan<DK>;
     using CB = ChunkBlock<DK, true>;  // fragment indices do not depend on the V dtype
-    if (s < PL::S_QH1) return CB::K0 + (s % PL::NP) * PL::KB + s / PL::NP;
-    if (s < PL::S_U) return CB::Q0 + ((s - PL::S_QH1) % PL::NP) * PL::KB + (s - PL::S_QH1) / PL::NP;
-    if (s < PL::S_QH2) return CB::T0 + tri(tri_p(s - PL::S_U), tri_v(s - PL::S_U));
-    if (s < PL::S_ST) {
-        const int q = s - PL::S_QH2 + PL::NQ1;
-        return CB::Q0 + (q % PL::NP) * PL::KB + q / PL::NP;
-    }
-    if (s < PL::S_PU) return CB::KT0 + ((s - PL::S_ST) % PL::NT) * PL::VB + (s - PL::S_ST) / PL::NT;
-    return CB::P0 + tri(tri_p(s - PL::S_PU), tri_v(s - PL::S_PU));
+    if (s < PL::A_U) return CB::K0 + (s % PL::NP) * PL::KB + s / PL::NP;
+    if (s < PL::A_ST) return CB::T0 + tri(tri_p(s - PL::A_U), tri_v(s - PL::A_U));
+    return CB::KT0 + ((s - PL::A_ST) % PL::NT) * PL::VB + (s - PL::A_ST) / PL::NT;
+}
+template <int DK>
+__device__ __forceinline__ constexpr int frag_b(int s) {  // output wave, step s
+    using PL = Plan<DK>;
+    using CB = ChunkBlock<DK, true>;
+    if (s < PL::B_PU) return CB::Q0 + (s % PL::NP) * PL::KB + s / PL::NP;
+    return CB::P0 + tri(tri_p(s - PL::B_PU), tri_v(s - PL::B_PU));
+}
+
+// The state (f16, as the products' B operand) and U (f16) handed from the
+// chain wave to the output wave of a slice, in operand order: 16 bytes per
+// lane per operand.
+template <int DK>
+struct Xchg {
+    static constexpr int KB = DK / 32, VB = kC / 32;
+    static constexpr int SB = 0, UB = KB * 1024, BYTES = UB + VB * 1024;
+};
+__device__ __forceinline__ void put_h8(unsigned char* base, int i, const h8& v) {
+    *reinterpret_cast<h8*>(base + i * 1024 + 16 * (threadIdx.x & 63)) = v;
+}
+__device__ __forceinline__ h8 get_h8(const unsigned char* base, int i) {
+    return *reinterpret_cast<const h8*>(base + i * 1024 + 16 * (threadIdx.x & 63));
 }
 
 template <int DK>
-struct ChunkRegs {
+struct ChainRegs {
     using PL = Plan<DK>;
     h8 sb[PL::KB];
-    f32x4 kh[PL::NP], uu[PL::NP], o[PL::NP];
-    h8 rb[PL::VB], ub[PL::VB], ug[PL::VB];
-    h8 fa[PL::S_END];
+    f32x4 kh[PL::NP], uu[PL::NP];
+    h8 rb[PL::VB], ug[PL::VB];
+    h8 fa[PL::A_END];
     float vx[PL::NP][4];
     f32x4 gp[PL::NP], gq[PL::NP];
     float gC;
 };
 
 template <int DK, bool BF16, int E>
-__device__ __forceinline__ void extra_read(ChunkRegs<DK>& x, const unsigned char* blk, int w) {
+__device__ __forceinline__ void extra_read(ChainRegs<DK>& x, const unsigned char* blk, int sl) {
     using CB = ChunkBlock<DK, BF16>;
     const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
     const float* gam = reinterpret_cast<const float*>(blk + CB::G0);
     if constexpr (E < 16) {
         constexpr int p = E / 4, r = E % 4;
-        const unsigned char* vp = blk + CB::V0 + (pair_row(p, 4 * lg) + r) * CB::VROW + (16 * w + c) * (BF16 ? 2 : 4);
+        const unsigned char* vp = blk + CB::V0 + (pair_row(p, 4 * lg) + r) * CB::VROW + (16 * sl + c) * (BF16 ? 2 : 4);
         if constexpr (BF16) x.vx[p][r] = bf16_lo(*reinterpret_cast<const uint16_t*>(vp));
         else x.vx[p][r] = *reinterpret_cast<const float*>(vp);
     } else if constexpr (E < 20) {
@@ -647,29 +664,23 @@ __device__ __forceinline__ void extra_read(ChunkRegs<DK>& x, const unsigned char
     }
 }
 template <int DK, bool BF16, int E, int EEND>
-__device__ __forceinline__ void extra_reads(ChunkRegs<DK>& x, const unsigned char* blk, int w) {
+__device__ __forceinline__ void extra_reads(ChainRegs<DK>& x, const unsigned char* blk, int sl) {
     if constexpr (E < EEND) {
-        extra_read<DK, BF16, E>(x, blk, w);
-        extra_reads<DK, BF16, E + 1, EEND>(x, blk, w);
+        extra_read<DK, BF16, E>(x, blk, sl);
+        extra_reads<DK, BF16, E + 1, EEND>(x, blk, sl);
     }
 }
 
-template <int DK, int OUT, bool BF16, int S>
-__device__ __forceinline__ void chunk_step(ChunkRegs<DK>& x, f32x4 (&st)[DK / 16], const unsigned char* blk,
-                                           unsigned char* ost, float scale, int w, const DmaCtx& d) {
+template <int DK, bool BF16, int S>
+__device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16], const unsigned char* blk,
+                                           unsigned char* xc, int sl) {
     using PL = Plan<DK>;
-    using CB = ChunkBlock<DK, BF16>;
     constexpr int NP = PL::NP, NT = PL::NT, VB = PL::VB, KB = PL::KB;
-    constexpr int NSLOT = CB::NLOAD / 2;
-    if constexpr (S < PL::S_END) {
-        // the next chunk's loads due at this step
-        dma_slots<DK, BF16, S * NSLOT / PL::S_END, (S + 1) * NSLOT / PL::S_END>(d);
-        // A fragment D steps ahead; V and gate reads during the K H steps
-        if constexpr (S + PL::D < PL::S_END) x.fa[S + PL::D] = frag_at(blk, frag_of<DK>(S + PL::D));
+    if constexpr (S < PL::A_END) {
+        if constexpr (S + PL::D < PL::A_END) x.fa[S + PL::D] = frag_at(blk, frag_a<DK>(S + PL::D));
         if constexpr (S < PL::NKH)
-            extra_reads<DK, BF16, S * PL::NEXTRA / PL::NKH, (S + 1) * PL::NEXTRA / PL::NKH>(x, blk, w);
-
-        if constexpr (S == PL::S_U) {
+            extra_reads<DK, BF16, S * PL::NEXTRA / PL::NKH, (S + 1) * PL::NEXTRA / PL::NKH>(x, blk, sl);
+        if constexpr (S == PL::A_U) {
             // R = V - gamma K H at this lane's rows pair_row(p, 4 lg) + r
 #pragma unroll
             for (int v = 0; v < VB; ++v)
@@ -681,42 +692,77 @@ __device__ __forceinline__ void chunk_step(ChunkRegs<DK>& x, f32x4 (&st)[DK / 16
                         x.rb[v][4 * hh + r] = (_Float16)fmaf(-x.gp[p][r], x.kh[p][r], x.vx[p][r]);
                     }
         }
-        if constexpr (S == PL::S_ST) {
-            // U in f16, plain and scaled by Gamma_{C,t}; the state decays by gamma_C
+        if constexpr (S == PL::A_ST) {
+            // U in f16 to the output wave; U scaled by Gamma_{C,t} here; the state decays
 #pragma unroll
             for (int v = 0; v < VB; ++v) {
-                x.ub[v] = pack_h8(x.uu[2 * v], x.uu[2 * v + 1]);
+                put_h8(xc + Xchg<DK>::UB, v, pack_h8(x.uu[2 * v], x.uu[2 * v + 1]));
                 x.ug[v] = pack_h8(x.gq[2 * v] * x.uu[2 * v], x.gq[2 * v + 1] * x.uu[2 * v + 1]);
             }
+            __syncthreads();  // U published (the output wave waits here for it)
 #pragma unroll
             for (int t = 0; t < NT; ++t) st[t] = x.gC * st[t];
         }
-        if constexpr (S == PL::S_PU) {
-#pragma unroll
-            for (int p = 0; p < NP; ++p) x.o[p] = x.gp[p] * x.o[p];  // gamma Q H
-        }
-
-        if constexpr (S < PL::S_QH1) {
+        if constexpr (S < PL::A_U) {
             constexpr int p = S % NP, u = S / NP;
             x.kh[p] = mfma16(x.fa[S], x.sb[u], x.kh[p]);
-        } else if constexpr (S < PL::S_U) {
-            constexpr int q = S - PL::S_QH1, p = q % NP, u = q / NP;
-            x.o[p] = mfma16(x.fa[S], x.sb[u], x.o[p]);
-        } else if constexpr (S < PL::S_QH2) {
-            constexpr int p = tri_p(S - PL::S_U), v = tri_v(S - PL::S_U);
+        } else if constexpr (S < PL::A_ST) {
+            constexpr int p = tri_p(S - PL::A_U), v = tri_v(S - PL::A_U);
             x.uu[p] = mfma16(x.fa[S], x.rb[v], x.uu[p]);
-        } else if constexpr (S < PL::S_ST) {
-            constexpr int q = S - PL::S_QH2 + PL::NQ1, p = q % NP, u = q / NP;
-            x.o[p] = mfma16(x.fa[S], x.sb[u], x.o[p]);
-        } else if constexpr (S < PL::S_PU) {
-            constexpr int t = (S - PL::S_ST) % NT, v = (S - PL::S_ST) / NT;
-            st[t] = mfma16(x.fa[S], x.ug[v], st[t]);
         } else {
-            constexpr int p = tri_p(S - PL::S_PU), v = tri_v(S - PL::S_PU);
+            constexpr int t = (S - PL::A_ST) % NT, v = (S - PL::A_ST) / NT;
+            st[t] = mfma16(x.fa[S], x.ug[v], st[t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        chain_step<DK, BF16, S + 1>(x, st, blk, xc, sl);
+    } else {
+        // the next chunk's starting state as the products' B operand, for both waves
+#pragma unroll
+        for (int u = 0; u < KB; ++u) put_h8(xc + Xchg<DK>::SB, u, pack_h8(st[2 * u], st[2 * u + 1]));
+    }
+}
+
+template <int DK>
+struct OutRegs {
+    using PL = Plan<DK>;
+    h8 sb[PL::KB], ub[PL::VB];
+    f32x4 o[PL::NP];
+    h8 fa[PL::B_END];
+    f32x4 gp[PL::NP];
+};
+
+template <int DK, int OUT, bool BF16, int S>
+__device__ __forceinline__ void out_step(OutRegs<DK>& x, const unsigned char* blk, const unsigned char* xc,
+                                         unsigned char* ost, float scale, const DmaCtx& d) {
+    using PL = Plan<DK>;
+    using CB = ChunkBlock<DK, BF16>;
+    constexpr int NP = PL::NP, VB = PL::VB;
+    constexpr int NSLOT = CB::NLOAD / 2;
+    if constexpr (S < PL::B_END) {
+        // the next chunk's loads due at this step
+        dma_slots<DK, BF16, S * NSLOT / PL::B_END, (S + 1) * NSLOT / PL::B_END>(d);
+        if constexpr (S + PL::D < PL::B_END) x.fa[S + PL::D] = frag_at(blk, frag_b<DK>(S + PL::D));
+        if constexpr (S == PL::B_PU) {
+            const int lg = (threadIdx.x & 63) >> 4;
+            const float* gam = reinterpret_cast<const float*>(blk + CB::G0);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                x.gp[p] = *reinterpret_cast<const f32x4*>(gam + pair_row(p, 4 * lg));
+                x.o[p] = x.gp[p] * x.o[p];  // gamma Q H
+            }
+            __syncthreads();  // U from the chain wave
+#pragma unroll
+            for (int v = 0; v < VB; ++v) x.ub[v] = get_h8(xc + Xchg<DK>::UB, v);
+        }
+        if constexpr (S < PL::B_PU) {
+            constexpr int p = S % NP, u = S / NP;
+            x.o[p] = mfma16(x.fa[S], x.sb[u], x.o[p]);
+        } else {
+            constexpr int p = tri_p(S - PL::B_PU), v = tri_v(S - PL::B_PU);
             x.o[p] = mfma16(x.fa[S], x.ub[v], x.o[p]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        chunk_step<DK, OUT, BF16, S + 1>(x, st, blk, ost, scale, w, d);
+        out_step<DK, OUT, BF16, S + 1>(x, blk, xc, ost, scale, d);
     } else {
         // O -> staging (written out at the start of the next chunk)
         const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
@@ -727,38 +773,56 @@ __device__ __forceinline__ void chunk_step(ChunkRegs<DK>& x, f32x4 (&st)[DK / 16
     }
 }
 
-// One chunk from its LDS block: state update in place, outputs staged, and the
-// next chunk's loads issued (d) along the way.
-template <int DK, int OUT, bool BF16>
-__device__ __forceinline__ void scan_chunk(f32x4 (&st)[DK / 16], const unsigned char* blk, unsigned char* ost,
-                                           float scale, int w, const DmaCtx& d) {
+template <int DK, bool BF16>
+__device__ __forceinline__ void chain_chunk(f32x4 (&st)[DK / 16], const unsigned char* blk, unsigned char* xc,
+                                            int sl) {
     using PL = Plan<DK>;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    ChunkRegs<DK> x;
-    // the state as B operand straight from the accumulators
+    ChainRegs<DK> x;
 #pragma unroll
     for (int u = 0; u < PL::KB; ++u) x.sb[u] = pack_h8(st[2 * u], st[2 * u + 1]);
 #pragma unroll
-    for (int p = 0; p < PL::NP; ++p) x.kh[p] = x.uu[p] = x.o[p] = z;
+    for (int p = 0; p < PL::NP; ++p) x.kh[p] = x.uu[p] = z;
 #pragma unroll
-    for (int s = 0; s < PL::D; ++s) x.fa[s] = frag_at(blk, frag_of<DK>(s));
-    chunk_step<DK, OUT, BF16, 0>(x, st, blk, ost, scale, w, d);
+    for (int s = 0; s < PL::D; ++s) x.fa[s] = frag_at(blk, frag_a<DK>(s));
+    chain_step<DK, BF16, 0>(x, st, blk, xc, sl);
+}
+
+template <int DK, int OUT, bool BF16>
+__device__ __forceinline__ void out_chunk(const unsigned char* blk, const unsigned char* xc, unsigned char* ost,
+                                          float scale, const DmaCtx& d) {
+    using PL = Plan<DK>;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    OutRegs<DK> x;
+#pragma unroll
+    for (int u = 0; u < PL::KB; ++u) x.sb[u] = get_h8(xc + Xchg<DK>::SB, u);
+#pragma unroll
+    for (int p = 0; p < PL::NP; ++p) x.o[p] = z;
+#pragma unroll
+    for (int s = 0; s < PL::D; ++s) x.fa[s] = frag_at(blk, frag_b<DK>(s));
+    out_step<DK, OUT, BF16, 0>(x, blk, xc, ost, scale, d);
 }
 
 template <int DK, int OUT, bool BF16>
 struct ScanLayout {
     static constexpr int BLK = ChunkBlock<DK, BF16>::BYTES;
+    static constexpr int XC = Xchg<DK>::BYTES;
     static constexpr int OST = OStage<OUT>::BYTES;
-    static constexpr int BYTES = 2 * BLK + 2 * OST;
+    static constexpr int BYTES = 2 * BLK + 2 * XC + 2 * OST;
 };
 
+// One workgroup of four waves per (sequence, value head, 32 value columns):
+// waves 0 and 1 are the chain waves of the two 16-column slices, waves 2 and 3
+// their output waves.
 template <int DK, int OUT, bool BF16>
-__global__ __launch_bounds__(128) void prefill_scan_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs a) {
     using L = ScanLayout<DK, OUT, BF16>;
     constexpr int NT = DK / 16;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int sl = w & 1;            // slice: value columns col0 + 16 sl ..
+    const bool chain = w < 2;
     const int c = lane & 15, lg = lane >> 4;
     int blk = xcd_logical_block(blockIdx.x, gridDim.x);
     const int pair = blk % a.slices;
@@ -778,41 +842,51 @@ __global__ __launch_bounds__(128) void prefill_scan_kernel(const PrefillArgs a) 
         s = a.state_slot[X.b];
         if (s < 0 || s >= a.n_slots) {
             if (threadIdx.x == 0 && a.status != nullptr) a.status[0] = GDN_ERR_SLOT;
-            return;  // uniform over the workgroup: both waves leave before any barrier
+            return;  // uniform over the workgroup: every wave leaves before any barrier
         }
     }
-    // lane (c, g) holds H[d_k][j] = S[j][d_k] for d_k = pair_row(t, 4g + r), r = 0..3
-    const int j = X.col0 + 16 * w + c;
-    float* stp = a.state + (((size_t)s * a.h_v + X.h) * a.d_v + j) * DK;
+    unsigned char* xc = lds_raw + 2 * L::BLK + sl * L::XC;
+    unsigned char* ost = lds_raw + 2 * L::BLK + 2 * L::XC + sl * L::OST;
+    // chain wave: lane (c, g) holds H[d_k][j] = S[j][d_k] for d_k = pair_row(t, 4g + r)
+    float* stp = a.state + (((size_t)s * a.h_v + X.h) * a.d_v + X.col0 + 16 * sl + c) * DK;
     f32x4 st[NT];
+    if (chain) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st[t][r] = stp[pair_row(t, 4 * lg) + r];
-
-    unsigned char* ost = lds_raw + 2 * L::BLK + w * L::OST;
-    {
-        const DmaCtx d0 = dma_ctx<DK, BF16>(X, 0, lds_raw, w);
+            for (int r = 0; r < 4; ++r) st[t][r] = stp[pair_row(t, 4 * lg) + r];
+#pragma unroll
+        for (int u = 0; u < DK / 32; ++u) put_h8(xc + Xchg<DK>::SB, u, pack_h8(st[2 * u], st[2 * u + 1]));
+    } else {
+        const DmaCtx d0 = dma_ctx<DK, BF16>(X, 0, lds_raw, sl);
         dma_slots<DK, BF16, 0, ChunkBlock<DK, BF16>::NLOAD / 2>(d0);
     }
     for (int ck = 0; ck < X.nch; ++ck) {
-        // this wave's loads of chunk ck have landed (the wait: loads into LDS count as
-        // vector-memory operations, which the barrier alone does not wait for), the other
-        // wave's too (the barrier); both waves are done with the other half of the buffer
+        // the output waves' loads of chunk ck have landed (the wait: loads into LDS count as
+        // vector-memory operations, which the barrier alone does not wait for) and are
+        // published by the barrier, with the chain waves' starting state; every wave is
+        // done with the other half of the double buffer
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (ck > 0) write_out<DK, OUT>(X, ost, ck - 1, w);
         const unsigned char* cur = lds_raw + (ck & 1) * L::BLK;
-        unsigned char* nxt = lds_raw + ((ck + 1) & 1) * L::BLK;
-        // the next chunk (the last chunk loads itself again into the idle block: harmless)
-        const DmaCtx d = dma_ctx<DK, BF16>(X, ck + 1, nxt, w);
-        scan_chunk<DK, OUT, BF16>(st, cur, ost, a.scale, w, d);
+        if (chain) {
+            chain_chunk<DK, BF16>(st, cur, xc, sl);
+        } else {
+            if (ck > 0) write_out<DK, OUT>(X, ost, ck - 1, sl);
+            unsigned char* nxt = lds_raw + ((ck + 1) & 1) * L::BLK;
+            // the next chunk (the last chunk loads itself again into the idle block: harmless)
+            const DmaCtx d = dma_ctx<DK, BF16>(X, ck + 1, nxt, sl);
+            out_chunk<DK, OUT, BF16>(cur, xc, ost, a.scale, d);
+        }
     }
-    write_out<DK, OUT>(X, ost, X.nch - 1, w);
+    if (chain) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) stp[pair_row(t, 4 * lg) + r] = st[t][r];
+            for (int r = 0; r < 4; ++r) stp[pair_row(t, 4 * lg) + r] = st[t][r];
+    } else {
+        write_out<DK, OUT>(X, ost, X.nch - 1, sl);
+    }
 }
 
 template <typename K>
@@ -826,7 +900,7 @@ hipError_t launch_scan(const PrefillArgs& a, int grid, hipStream_t st) {
     const size_t lds = ScanLayout<DK, OUT, BF16>::BYTES;
     hipError_t e = set_lds(&prefill_scan_kernel<DK, OUT, BF16>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT, BF16>), dim3(grid), dim3(128), lds, st, a);
+    hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT, BF16>), dim3(grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
 
