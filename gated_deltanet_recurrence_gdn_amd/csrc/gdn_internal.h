@@ -100,7 +100,7 @@ struct PrefillArgs {
     int32_t h_v;
     int32_t d_v;
     int32_t group;   // h_v / h_qk
-    int32_t slices;  // d_v / 32 (one scan workgroup of two waves per 32 value columns)
+    int32_t slices;  // scan workgroups per head (set by the launcher from d_v)
     int32_t n_slots;
     int32_t qkv_bf16;
     float scale;

@@ -19,13 +19,14 @@
 //    transform T = (I + A)^{-1} in fp32 (16 x 16 diagonal blocks by forward
 //    substitution, off-diagonal blocks by v_mfma_f32_16x16x4_f32).  It writes
 //    T' and P = Gamma o tril(Q K^T) in f16, the per-token gate factors, and
-//    K, Q, K^T in f16 (once per q/k head) to the workspace, every matrix in the
+//    K, Q in f16 (once per q/k head) to the workspace, every matrix in the
 //    scan's operand-fragment order.
-//  * scan (one workgroup of two waves per (sequence, value head, 32 value
-//    columns), sequential over chunks): each wave keeps its 16 columns of the
-//    state in accumulators for the whole prompt; per chunk it forms K H, Q H,
-//    R, U = T' R, O and the state update with v_mfma_f32_16x16x32_f16 from
-//    operands that buffer-to-LDS loads brought in during the previous chunk.
+//  * scan (one workgroup per (sequence, value head, 64 or 32 value columns),
+//    sequential over chunks): per 16 columns a chain wave keeps the state in
+//    accumulators for the whole prompt and forms K H, R, U = T' R and the
+//    state update, and an output wave forms Q H and O = gamma Q H + P U, all
+//    with v_mfma_f32_16x16x32_f16 from operands that buffer-to-LDS loads
+//    brought in during the previous chunk.
 // All matrix-core operands are f16 with fp32 accumulation: the bf16 inputs are
 // exact in f16 within the f16 range, and the derived operands (T', R, P, U, H)
 // keep f16's 11-bit significand, enough for the parity bar where bf16 is not.
@@ -115,17 +116,15 @@ __device__ __forceinline__ int pair_row(int tile, int c) {
 // Workspace layout (bytes), per sequence b and chunk c:
 //   T', P  [B][nch][h_v][C x C]     f16, T' = T diag(beta)
 //   gates  [B][nch][h_v][3][C]      fp32: gamma_t, beta_t, Gamma_{C,t}
-//   KT     [B][nch][h_qk][d_k x C]  f16   (K transposed)
 //   K, Q   [B][nch][h_qk][C x d_k]  f16
 // The matrices are stored in the scan's operand-fragment order: fragment f
 // (1 KB) holds, for lane l = 16 g + c, the 8 contraction-consecutive values of
 // row pair_row(tile, c) starting at column 32 (block) + 8 g, at f * 1 KB + 16 l.
-// K and Q: f = tile * (d_k / 32) + block over the C x d_k matrix; KT:
-// f = tile * 2 + block over the d_k x C matrix; T' and P: the six
+// K and Q: f = tile * (d_k / 32) + block over the C x d_k matrix; T' and P: the six
 // lower-triangular (tile, block) pairs in the order (0,0) (1,0) (2,0) (2,1)
 // (3,0) (3,1).  So every load of the scan is one contiguous kilobyte.
 struct WsLayout {
-    size_t T, P, G, KT, K, Q, total;
+    size_t T, P, G, K, Q, total;
 };
 __host__ __device__ inline WsLayout ws_layout(int B, int nch, int h_qk, int h_v, int d_k) {
     WsLayout w;
@@ -133,8 +132,7 @@ __host__ __device__ inline WsLayout ws_layout(int B, int nch, int h_qk, int h_v,
     w.T = 0;
     w.P = w.T + units * h_v * kC * kC * 2;
     w.G = w.P + units * h_v * kC * kC * 2;
-    w.KT = w.G + units * h_v * 3 * kC * 4;
-    w.K = w.KT + units * h_qk * (size_t)d_k * kC * 2;
+    w.K = w.G + units * h_v * 3 * kC * 4;
     w.Q = w.K + units * h_qk * (size_t)d_k * kC * 2;
     w.total = w.Q + units * h_qk * (size_t)d_k * kC * 2;
     return w;
@@ -215,7 +213,7 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
     __syncthreads();
 
     // 2. gates (wave 0): l_t (base 2) by a wave prefix sum; gamma_t, Gamma_{C,t} -> workspace.
-    //    K^T -> workspace (waves 1-3, once per q/k head).
+    //    K, Q -> workspace (waves 1-3, once per q/k head).
     if (wave == 0) {
         float x = fmaxf(log2_fast(L.al[lane]), kLogFloor * kLog2e);
 #pragma unroll
@@ -230,24 +228,16 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         gw[kC + lane] = L.be[lane];
         gw[2 * kC + lane] = exp2_fast(lC - x);
     } else if (h % a.group == 0) {
-        // K^T, K, Q in fragment order, one 16-byte piece (fragment f, lane l) per step
-        _Float16* kt = reinterpret_cast<_Float16*>(wsb + ws.KT) + unit_q * DK * kC;
+        // K, Q in fragment order, one 16-byte piece (fragment f, lane l) per step
         _Float16* kw = reinterpret_cast<_Float16*>(wsb + ws.K) + unit_q * kC * DK;
         _Float16* qw = reinterpret_cast<_Float16*>(wsb + ws.Q) + unit_q * kC * DK;
         constexpr int PIECES = DK * kC / 8;
-        for (int e = tid - 64; e < 3 * PIECES; e += 192) {
+        for (int e = tid - 64; e < 2 * PIECES; e += 192) {
             const int m = e / PIECES, i = e % PIECES;
             const int f = i / 64, l = i % 64, c = l & 15, lg = l >> 4;
-            h8 v;
-            if (m == 0) {
-                const int dk = pair_row(f / 2, c), t0 = 32 * (f % 2) + 8 * lg;
-#pragma unroll
-                for (int x = 0; x < 8; ++x) v[x] = L.u.in.Kf[(t0 + x) * kLdK + dk];
-            } else {
-                const int row = pair_row(f / KSD, c), col = 32 * (f % KSD) + 8 * lg;
-                v = *reinterpret_cast<const h8*>(&(m == 1 ? L.u.in.Kf : L.u.in.Qf)[row * kLdK + col]);
-            }
-            *reinterpret_cast<h8*>((m == 0 ? kt : m == 1 ? kw : qw) + 8 * i) = v;
+            const int row = pair_row(f / KSD, c), col = 32 * (f % KSD) + 8 * lg;
+            const h8 v = *reinterpret_cast<const h8*>(&(m == 0 ? L.u.in.Kf : L.u.in.Qf)[row * kLdK + col]);
+            *reinterpret_cast<h8*>((m == 0 ? kw : qw) + 8 * i) = v;
         }
     }
     __syncthreads();
@@ -377,11 +367,11 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
 }
 
 // ---------------------------------------------------------------------------
-// scan: one workgroup of two waves per (sequence, value head, 32 value columns)
+// scan: one workgroup per (sequence, value head, 16 NSL value columns)
 // ---------------------------------------------------------------------------
 // Value columns never mix in the recurrence (R, U, O and the state update act
-// on each column of H separately), so each wave owns 16 columns of one head
-// for the whole prompt.  The state slice H[:, j0 .. j0+16) stays in
+// on each column of H separately), so a pair of waves owns 16 columns of one
+// head for the whole prompt.  The state slice H[:, j0 .. j0+16) stays in
 // accumulators, and every product's result feeds the next product from the
 // lane that produced it, because 16-row tiles are paired into 32-wide
 // contraction blocks with a matching row order:
@@ -394,15 +384,16 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
 // takes R = V - gamma K H, and O and the state update take U, all without
 // moving data between lanes.
 //
-// The two waves read the same A operands (K, Q, K^T, T', P of their head), so
-// the workgroup brings each chunk's operands into LDS once: buffer loads that
-// write LDS directly (no registers), split between the waves, one chunk
-// ahead into the other half of a double buffer.  The LDS copy is in fragment
-// order -- fragment f, lane l at f * 1 KB + 16 l -- so every operand read is
-// one conflict-free 16-byte LDS read.  One barrier per chunk: each wave waits
-// for its own loads of the chunk, then the barrier publishes both halves and
-// also tells each wave that the other has finished with the buffer about to
-// be refilled.
+// All slices of a workgroup read the same A operands (K, Q, T', P of their
+// head), so the workgroup brings each chunk's operands into LDS once: buffer
+// loads that write LDS directly (no registers), split between the output
+// waves, one chunk ahead into the other half of a double buffer.  The LDS
+// copy is in fragment order -- fragment f, lane l at f * 1 KB + 16 l -- so
+// an operand read is one conflict-free 16-byte LDS read (K^T: two transposing
+// reads of the K fragments).  Two barriers per chunk: at the top, after each
+// output wave's wait for its own loads (publishing the chunk, and telling
+// every wave that the other half of the buffer is free), and in the middle,
+// where the chain waves hand U to the output waves.
 __device__ __forceinline__ h8 pack_h8(const f32x4& lo, const f32x4& hi) {
     h8 r;
 #pragma unroll
@@ -422,31 +413,37 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-// One chunk's block in LDS.  Fragments (1 KB each): K [p][u], Q [p][u],
-// K^T [t][v], then T' and P over the lower-triangular (p, v <= p / 2) pairs;
-// then V rows [64][32 columns] in the input dtype, then gamma_t and Gamma_{C,t}.
-template <int DK, bool BF16>
+// One chunk's block in LDS.  Fragments (1 KB each): K [p][u], Q [p][u], then
+// T' and P over the six lower-triangular (p, v <= p / 2) pairs (each rounded
+// up to a multiple of NSL fragments); then V rows [64][the workgroup's 16 NSL
+// columns] in the input dtype, then gamma_t and Gamma_{C,t}.  K^T is not stored: the chain
+// wave reads it from the K fragments with transposing LDS reads.
+template <int DK, bool BF16, int NSL>
 struct ChunkBlock {
     static constexpr int NT = DK / 16, KB = DK / 32, NP = kC / 16, VB = kC / 32;
-    static constexpr int NTRI = 6;  // (p, v): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-    static constexpr int K0 = 0, Q0 = K0 + NP * KB, KT0 = Q0 + NP * KB, T0 = KT0 + NT * VB, P0 = T0 + NTRI;
+    static constexpr int NTRI = (6 + NSL - 1) / NSL * NSL;
+    static constexpr int K0 = 0, Q0 = K0 + NP * KB, T0 = Q0 + NP * KB, P0 = T0 + NTRI;
     static constexpr int NFRAG = P0 + NTRI;
-    static constexpr int VROW = 32 * (BF16 ? 2 : 4);  // bytes of one V row (32 columns)
-    static constexpr int NVI = kC * VROW / 1024;      // V loads
+    static constexpr int COLS = 16 * NSL;              // value columns of the workgroup
+    static constexpr int VROW = COLS * (BF16 ? 2 : 4);  // bytes of one V row
+    static constexpr int NVI = kC * VROW / 1024;       // V loads
     static constexpr int V0 = NFRAG * 1024;
-    static constexpr int G0 = V0 + kC * VROW;         // gamma [64], Gamma_C [64] (fp32)
+    static constexpr int G0 = V0 + kC * VROW;          // gamma [64], Gamma_C [64] (fp32)
     static constexpr int BYTES = G0 + 2 * kC * 4;
-    static constexpr int NLOAD = NFRAG + NVI + 2;     // load instructions per chunk
+    // load instructions per chunk, NSL per slot (one per output wave): every
+    // boundary between matrices falls on a slot boundary
+    static constexpr int NLOAD = NFRAG + NVI + NSL;
+    static_assert(Q0 % NSL == 0 && T0 % NSL == 0 && P0 % NSL == 0 && NFRAG % NSL == 0 && NVI % NSL == 0,
+                  "slot boundaries");
 };
 __device__ __forceinline__ constexpr int tri(int p, int v) { return p < 2 ? p : 2 * p - 2 + v; }
 
 template <int DK>
 struct ScanCtx {
-    static constexpr int NT = DK / 16, NP = kC / 16;
     const PrefillArgs* a;
     const unsigned char* wsb;
     WsLayout ws;
-    int b, h, g, nch, col0;   // col0: first value column of the workgroup
+    int b, h, g, nch, col0, cols;  // the workgroup's first value column and column count
     __device__ int clamp_ck(int ck) const { return ck < nch ? ck : nch - 1; }
     // the chunk's block of a per-value-head array (per_unit bytes per head and chunk)
     __device__ rsrc_t ws_v(size_t arr, uint32_t per_unit, int ck) const {
@@ -467,26 +464,27 @@ struct ScanCtx {
         const size_t row = (size_t)a->h_v * a->d_v;
         return make_rsrc(static_cast<const unsigned char*>(base) +
                              (((size_t)b * a->T + t0) * row + (size_t)h * a->d_v + col0) * esz,
-                         (uint32_t)(((size_t)(n - 1) * row + 32) * esz));
+                         (uint32_t)(((size_t)(n - 1) * row + cols) * esz));
     }
 };
 
 // Loads of one chunk into an LDS block.  ChunkBlock's load instructions are
-// split between the two waves: wave w issues instruction i = 2 k + w for slot
-// k.  Every matrix boundary in that list is even, so both instructions of a
-// slot read the same matrix and the slot's code is the same for both waves;
-// the wave enters only through per-lane offsets and a uniform LDS base.
+// split between the NSL output waves: output wave sl issues instruction
+// i = NSL k + sl for slot k.  Every matrix boundary is a slot boundary, so all
+// instructions of a slot read the same matrix and the slot's code is the same
+// for every wave; the wave enters only through per-lane offsets and a uniform
+// LDS base.
 struct DmaCtx {
-    rsrc_t kw, qw, ktw, tw, pw, gw, vw;
+    rsrc_t kw, qw, tw, pw, gw, vw;
     uint32_t vf, vv, vg;  // per-lane source offsets of fragment, V and gate loads (this wave's)
-    uint32_t vstep;       // source bytes between V loads n and n + 1
-    unsigned char* dst;   // LDS block + 1 KB w
-    unsigned char* gdst;  // LDS gate area + 256 B w
+    uint32_t vstep;       // source bytes between this wave's consecutive V loads
+    unsigned char* dst;   // LDS block + 1 KB sl
+    unsigned char* gdst;  // LDS gate area: gamma (even sl) or Gamma_C (odd sl)
 };
 
-template <int DK, bool BF16>
-__device__ __forceinline__ DmaCtx dma_ctx(const ScanCtx<DK>& X, int ck, unsigned char* blk, int w) {
-    using CB = ChunkBlock<DK, BF16>;
+template <int DK, bool BF16, int NSL>
+__device__ __forceinline__ DmaCtx dma_ctx(const ScanCtx<DK>& X, int ck, unsigned char* blk, int sl) {
+    using CB = ChunkBlock<DK, BF16, NSL>;
     const PrefillArgs& a = *X.a;
     constexpr int VSZ = BF16 ? 2 : 4;
     constexpr int RPL = 1024 / CB::VROW;  // V rows per load
@@ -495,48 +493,52 @@ __device__ __forceinline__ DmaCtx dma_ctx(const ScanCtx<DK>& X, int ck, unsigned
     DmaCtx d;
     d.kw = X.ws_q(X.ws.K, kC * DK * 2, ck);
     d.qw = X.ws_q(X.ws.Q, kC * DK * 2, ck);
-    d.ktw = X.ws_q(X.ws.KT, DK * kC * 2, ck);
     d.tw = X.ws_v(X.ws.T, kC * kC * 2, ck);
     d.pw = X.ws_v(X.ws.P, kC * kC * 2, ck);
     d.gw = X.ws_v(X.ws.G, 3 * kC * 4, ck);
     d.vw = X.rows(a.v, VSZ, ck);
     // fragments are stored in load order: lane l of fragment f at f KB + 16 l
-    d.vf = 16 * lane + 1024 * w;
+    d.vf = 16 * lane + 1024 * sl;
     // V load n, lane l: row n RPL + 16 l / VROW, byte (16 l) % VROW of the workgroup's columns
-    d.vv = (uint32_t)((16 * lane / CB::VROW + RPL * w) * rowb + (16 * lane) % CB::VROW);
-    d.vstep = RPL * rowb;
-    // gamma (wave 0) and Gamma_C (wave 1), 64 fp32 each
-    d.vg = 4 * lane + 2 * kC * 4 * w;
-    d.dst = blk + 1024 * w;
-    d.gdst = blk + CB::G0 + kC * 4 * w;
+    d.vv = (uint32_t)((16 * lane / CB::VROW + RPL * sl) * rowb + (16 * lane) % CB::VROW);
+    d.vstep = NSL * RPL * rowb;
+    // gamma (even sl) and Gamma_C (odd sl), 64 fp32 each (with four waves, twice over)
+    d.vg = 4 * lane + 2 * kC * 4 * (sl & 1);
+    d.dst = blk + 1024 * sl;
+    d.gdst = blk + CB::G0 + kC * 4 * (sl & 1);
     return d;
 }
 
-template <int DK, bool BF16, int K>
+template <int DK, bool BF16, int NSL, int K>
 __device__ __forceinline__ void dma_slot(const DmaCtx& d) {
-    using CB = ChunkBlock<DK, BF16>;
-    constexpr int i0 = 2 * K;
+    using CB = ChunkBlock<DK, BF16, NSL>;
+    constexpr int i0 = NSL * K;  // this slot's first instruction
     if constexpr (i0 < CB::NFRAG) {
-        constexpr int base = i0 < CB::Q0 ? CB::K0 : i0 < CB::KT0 ? CB::Q0 : i0 < CB::T0 ? CB::KT0 : i0 < CB::P0 ? CB::T0 : CB::P0;
-        const rsrc_t r = i0 < CB::Q0 ? d.kw : i0 < CB::KT0 ? d.qw : i0 < CB::T0 ? d.ktw : i0 < CB::P0 ? d.tw : d.pw;
-        // slots pair up inside a matrix and share one LDS base: the instruction offset
-        // (2 KB for the second of a pair) moves the source and the LDS address alike
-        constexpr int pb = base + 4 * ((i0 - base) / 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(d.dst + 1024 * pb), 16, d.vf, 1024 * (pb - base),
-                                                 1024 * (i0 - pb), 0);
+        constexpr int base = i0 < CB::Q0 ? CB::K0 : i0 < CB::T0 ? CB::Q0 : i0 < CB::P0 ? CB::T0 : CB::P0;
+        const rsrc_t r = i0 < CB::Q0 ? d.kw : i0 < CB::T0 ? d.qw : i0 < CB::P0 ? d.tw : d.pw;
+        if constexpr (NSL * 1024 < 4096) {
+            // slots pair up inside a matrix and share one LDS base: the instruction offset
+            // (the second of a pair) moves the source and the LDS address alike
+            constexpr int pb = base + 2 * NSL * ((i0 - base) / (2 * NSL));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(d.dst + 1024 * pb), 16, d.vf,
+                                                     1024 * (pb - base), 1024 * (i0 - pb), 0);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(d.dst + 1024 * i0), 16, d.vf, 1024 * (i0 - base),
+                                                     0, 0);
+        }
     } else if constexpr (i0 < CB::NFRAG + CB::NVI) {
-        constexpr int n0 = i0 - CB::NFRAG;
+        constexpr int n0 = (i0 - CB::NFRAG) / NSL;  // this wave's V load index
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.vw, (lds_void*)(d.dst + 1024 * i0), 16, d.vv, n0 * d.vstep, 0, 0);
     } else {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.gw, (lds_void*)d.gdst, 4, d.vg, 0, 0, 0);
     }
 }
 
-template <int DK, bool BF16, int K, int KEND>
+template <int DK, bool BF16, int NSL, int K, int KEND>
 __device__ __forceinline__ void dma_slots(const DmaCtx& d) {
     if constexpr (K < KEND) {
-        dma_slot<DK, BF16, K>(d);
-        dma_slots<DK, BF16, K + 1, KEND>(d);
+        dma_slot<DK, BF16, NSL, K>(d);
+        dma_slots<DK, BF16, NSL, K + 1, KEND>(d);
     }
 }
 
@@ -544,8 +546,34 @@ __device__ __forceinline__ h8 frag_at(const unsigned char* blk, int f) {
     return *reinterpret_cast<const h8*>(blk + f * 1024 + 16 * (threadIdx.x & 63));
 }
 
-// Output rows staged in LDS per wave: row t at t * RB + (t / 8) * 32 (the skew
-// keeps the four rows one store instruction touches on different banks).
+// The state update's A operand K^T (tile t over d_k, block v over tokens),
+// read from the K fragments with two transposing reads.  ds_read_b64_tr_b16
+// gives lane c of a 16-lane group element e = value c % 4 of the 8 bytes that
+// lane 4 e + c / 4 of the group addressed.  Lane 4 e + q of group g therefore
+// addresses K[token 32 v + 8 g + 4 h + e][d_k 32 (t / 2) + 8 q + 4 (t % 2) ..+4]
+// for half h, and lane (c, g) receives K^T[pair_row(t, c)][32 v + 8 g + 4 h + e].
+template <int DK>
+__device__ __forceinline__ h8 kt_frag(const unsigned char* blk, int t, int v) {
+    typedef short s4v __attribute__((ext_vector_type(4)));
+    typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4v lds_s4;
+    constexpr int KB = DK / 32;
+    const int lane = threadIdx.x & 63, g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+    h8 r;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const unsigned char* p =
+            blk + ((2 * v + hh) * KB + (t >> 1)) * 1024 + (16 * q + 4 * g + e) * 16 + 8 * (t & 1);
+        const h4v x = __builtin_bit_cast(h4v, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[4 * hh + j] = x[j];
+    }
+    return r;
+}
+
+// Output rows staged in LDS per output wave: row t at t * RB + (t / 8) * 32
+// (the skew keeps the four rows one store instruction touches on different
+// banks).
 template <int OUT>
 struct OStage {
     static constexpr int ESZ = OUT == 0 ? 4 : 2;
@@ -556,7 +584,7 @@ struct OStage {
 
 // The staged outputs of chunk ck -> HBM, 16-byte stores of whole row pieces.
 template <int DK, int OUT>
-__device__ __forceinline__ void write_out(const ScanCtx<DK>& X, const unsigned char* ost, int ck, int w) {
+__device__ __forceinline__ void write_out(const ScanCtx<DK>& X, const unsigned char* ost, int ck, int sl) {
     using OS = OStage<OUT>;
     const PrefillArgs& a = *X.a;
     const int lane = threadIdx.x & 63;
@@ -565,9 +593,9 @@ __device__ __forceinline__ void write_out(const ScanCtx<DK>& X, const unsigned c
     constexpr int PER_ROW = OS::RB / 16;  // 16-byte pieces per row
 #pragma unroll
     for (int n = 0; n < PER_ROW; ++n) {
-        const int t = lane, piece = n;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(ost + OS::at(t) + 16 * piece);
-        __builtin_amdgcn_raw_buffer_store_b128(v, ow, t * rstride + (16 * w) * OS::ESZ + 16 * piece, 0, 0);
+        const int t = lane;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ost + OS::at(t) + 16 * n);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ow, t * rstride + (16 * sl) * OS::ESZ + 16 * n, 0, 0);
     }
 }
 
@@ -585,7 +613,7 @@ __device__ __forceinline__ void stage_o(unsigned char* ost, int t, int c, float 
 //                barrier | state update (v-major) | next state -> LDS
 //   output wave: Q H (from the state in LDS) | barrier | U <- LDS | O += P U |
 //                outputs staged; it also issues the next chunk's loads.
-// Each wave's steps are one static sequence, each MFMA with its A fragment
+// Each wave's steps are one static sequence, each MFMA with its A operand
 // from LDS read D steps ahead; the order is pinned with scheduling barriers.
 template <int DK>
 struct Plan {
@@ -595,25 +623,27 @@ struct Plan {
     static constexpr int A_U = NKH, A_ST = A_U + NU, A_END = A_ST + NST;
     // output wave
     static constexpr int B_PU = NQ, B_END = B_PU + NPU;
-    static constexpr int D = 6;        // fragment reads in flight ahead of the MFMAs
+    static constexpr int D = 6;        // operand reads in flight ahead of the MFMAs
     static constexpr int NEXTRA = 25;  // chain wave: V (16), gamma (4), Gamma_C (4), gamma_C (1)
 };
 // the (tile, block) pairs of U = T' R and O += P U, block-major
 __device__ __forceinline__ constexpr int tri_p(int k) { return k < 4 ? k : k - 2; }
 __device__ __forceinline__ constexpr int tri_v(int k) { return k < 4 ? 0 : 1; }
 
-template <int DK>
-__device__ __forceinline__ constexpr int frag_a(int s) {  // chain wave, step s
+// chain wave: the A operand of step s
+template <int DK, int S>
+__device__ __forceinline__ h8 chain_operand(const unsigned char* blk) {
     using PL = Plan<DK>;
-    using CB = ChunkBlock<DK, true>;  // fragment indices do not depend on the V dtype
-    if (s < PL::A_U) return CB::K0 + (s % PL::NP) * PL::KB + s / PL::NP;
-    if (s < PL::A_ST) return CB::T0 + tri(tri_p(s - PL::A_U), tri_v(s - PL::A_U));
-    return CB::KT0 + ((s - PL::A_ST) % PL::NT) * PL::VB + (s - PL::A_ST) / PL::NT;
+    using CB = ChunkBlock<DK, true, 2>;  // fragment indices depend on neither the V dtype nor NSL
+    if constexpr (S < PL::A_U) return frag_at(blk, CB::K0 + (S % PL::NP) * PL::KB + S / PL::NP);
+    else if constexpr (S < PL::A_ST) return frag_at(blk, CB::T0 + tri(tri_p(S - PL::A_U), tri_v(S - PL::A_U)));
+    else return kt_frag<DK>(blk, (S - PL::A_ST) % PL::NT, (S - PL::A_ST) / PL::NT);
 }
+// output wave: the A operand fragment of step s
 template <int DK>
-__device__ __forceinline__ constexpr int frag_b(int s) {  // output wave, step s
+__device__ __forceinline__ constexpr int frag_b(int s) {
     using PL = Plan<DK>;
-    using CB = ChunkBlock<DK, true>;
+    using CB = ChunkBlock<DK, true, 2>;
     if (s < PL::B_PU) return CB::Q0 + (s % PL::NP) * PL::KB + s / PL::NP;
     return CB::P0 + tri(tri_p(s - PL::B_PU), tri_v(s - PL::B_PU));
 }
@@ -645,9 +675,9 @@ struct ChainRegs {
     float gC;
 };
 
-template <int DK, bool BF16, int E>
+template <int DK, bool BF16, int NSL, int E>
 __device__ __forceinline__ void extra_read(ChainRegs<DK>& x, const unsigned char* blk, int sl) {
-    using CB = ChunkBlock<DK, BF16>;
+    using CB = ChunkBlock<DK, BF16, NSL>;
     const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
     const float* gam = reinterpret_cast<const float*>(blk + CB::G0);
     if constexpr (E < 16) {
@@ -663,23 +693,23 @@ __device__ __forceinline__ void extra_read(ChainRegs<DK>& x, const unsigned char
         x.gC = gam[kC - 1];
     }
 }
-template <int DK, bool BF16, int E, int EEND>
+template <int DK, bool BF16, int NSL, int E, int EEND>
 __device__ __forceinline__ void extra_reads(ChainRegs<DK>& x, const unsigned char* blk, int sl) {
     if constexpr (E < EEND) {
-        extra_read<DK, BF16, E>(x, blk, sl);
-        extra_reads<DK, BF16, E + 1, EEND>(x, blk, sl);
+        extra_read<DK, BF16, NSL, E>(x, blk, sl);
+        extra_reads<DK, BF16, NSL, E + 1, EEND>(x, blk, sl);
     }
 }
 
-template <int DK, bool BF16, int S>
+template <int DK, bool BF16, int NSL, int S>
 __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16], const unsigned char* blk,
                                            unsigned char* xc, int sl) {
     using PL = Plan<DK>;
     constexpr int NP = PL::NP, NT = PL::NT, VB = PL::VB, KB = PL::KB;
     if constexpr (S < PL::A_END) {
-        if constexpr (S + PL::D < PL::A_END) x.fa[S + PL::D] = frag_at(blk, frag_a<DK>(S + PL::D));
+        if constexpr (S + PL::D < PL::A_END) x.fa[S + PL::D] = chain_operand<DK, S + PL::D>(blk);
         if constexpr (S < PL::NKH)
-            extra_reads<DK, BF16, S * PL::NEXTRA / PL::NKH, (S + 1) * PL::NEXTRA / PL::NKH>(x, blk, sl);
+            extra_reads<DK, BF16, NSL, S * PL::NEXTRA / PL::NKH, (S + 1) * PL::NEXTRA / PL::NKH>(x, blk, sl);
         if constexpr (S == PL::A_U) {
             // R = V - gamma K H at this lane's rows pair_row(p, 4 lg) + r
 #pragma unroll
@@ -699,7 +729,7 @@ __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16
                 put_h8(xc + Xchg<DK>::UB, v, pack_h8(x.uu[2 * v], x.uu[2 * v + 1]));
                 x.ug[v] = pack_h8(x.gq[2 * v] * x.uu[2 * v], x.gq[2 * v + 1] * x.uu[2 * v + 1]);
             }
-            __syncthreads();  // U published (the output wave waits here for it)
+            __syncthreads();  // U published (the output waves wait here for it)
 #pragma unroll
             for (int t = 0; t < NT; ++t) st[t] = x.gC * st[t];
         }
@@ -714,9 +744,9 @@ __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16
             st[t] = mfma16(x.fa[S], x.ug[v], st[t]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        chain_step<DK, BF16, S + 1>(x, st, blk, xc, sl);
+        chain_step<DK, BF16, NSL, S + 1>(x, st, blk, xc, sl);
     } else {
-        // the next chunk's starting state as the products' B operand, for both waves
+        // the next chunk's starting state as the products' B operand, for the output wave
 #pragma unroll
         for (int u = 0; u < KB; ++u) put_h8(xc + Xchg<DK>::SB, u, pack_h8(st[2 * u], st[2 * u + 1]));
     }
@@ -731,16 +761,16 @@ struct OutRegs {
     f32x4 gp[PL::NP];
 };
 
-template <int DK, int OUT, bool BF16, int S>
+template <int DK, int OUT, bool BF16, int NSL, int S>
 __device__ __forceinline__ void out_step(OutRegs<DK>& x, const unsigned char* blk, const unsigned char* xc,
                                          unsigned char* ost, float scale, const DmaCtx& d) {
     using PL = Plan<DK>;
-    using CB = ChunkBlock<DK, BF16>;
+    using CB = ChunkBlock<DK, BF16, NSL>;
     constexpr int NP = PL::NP, VB = PL::VB;
-    constexpr int NSLOT = CB::NLOAD / 2;
+    constexpr int NSLOT = CB::NLOAD / NSL;
     if constexpr (S < PL::B_END) {
         // the next chunk's loads due at this step
-        dma_slots<DK, BF16, S * NSLOT / PL::B_END, (S + 1) * NSLOT / PL::B_END>(d);
+        dma_slots<DK, BF16, NSL, S * NSLOT / PL::B_END, (S + 1) * NSLOT / PL::B_END>(d);
         if constexpr (S + PL::D < PL::B_END) x.fa[S + PL::D] = frag_at(blk, frag_b<DK>(S + PL::D));
         if constexpr (S == PL::B_PU) {
             const int lg = (threadIdx.x & 63) >> 4;
@@ -762,7 +792,7 @@ __device__ __forceinline__ void out_step(OutRegs<DK>& x, const unsigned char* bl
             x.o[p] = mfma16(x.fa[S], x.ub[v], x.o[p]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        out_step<DK, OUT, BF16, S + 1>(x, blk, xc, ost, scale, d);
+        out_step<DK, OUT, BF16, NSL, S + 1>(x, blk, xc, ost, scale, d);
     } else {
         // O -> staging (written out at the start of the next chunk)
         const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
@@ -773,7 +803,7 @@ __device__ __forceinline__ void out_step(OutRegs<DK>& x, const unsigned char* bl
     }
 }
 
-template <int DK, bool BF16>
+template <int DK, bool BF16, int NSL>
 __device__ __forceinline__ void chain_chunk(f32x4 (&st)[DK / 16], const unsigned char* blk, unsigned char* xc,
                                             int sl) {
     using PL = Plan<DK>;
@@ -783,12 +813,17 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&st)[DK / 16], const unsigned
     for (int u = 0; u < PL::KB; ++u) x.sb[u] = pack_h8(st[2 * u], st[2 * u + 1]);
 #pragma unroll
     for (int p = 0; p < PL::NP; ++p) x.kh[p] = x.uu[p] = z;
-#pragma unroll
-    for (int s = 0; s < PL::D; ++s) x.fa[s] = frag_at(blk, frag_a<DK>(s));
-    chain_step<DK, BF16, 0>(x, st, blk, xc, sl);
+    x.fa[0] = chain_operand<DK, 0>(blk);
+    x.fa[1] = chain_operand<DK, 1>(blk);
+    x.fa[2] = chain_operand<DK, 2>(blk);
+    x.fa[3] = chain_operand<DK, 3>(blk);
+    x.fa[4] = chain_operand<DK, 4>(blk);
+    x.fa[5] = chain_operand<DK, 5>(blk);
+    static_assert(Plan<DK>::D == 6, "prologue reads D operands");
+    chain_step<DK, BF16, NSL, 0>(x, st, blk, xc, sl);
 }
 
-template <int DK, int OUT, bool BF16>
+template <int DK, int OUT, bool BF16, int NSL>
 __device__ __forceinline__ void out_chunk(const unsigned char* blk, const unsigned char* xc, unsigned char* ost,
                                           float scale, const DmaCtx& d) {
     using PL = Plan<DK>;
@@ -800,32 +835,32 @@ __device__ __forceinline__ void out_chunk(const unsigned char* blk, const unsign
     for (int p = 0; p < PL::NP; ++p) x.o[p] = z;
 #pragma unroll
     for (int s = 0; s < PL::D; ++s) x.fa[s] = frag_at(blk, frag_b<DK>(s));
-    out_step<DK, OUT, BF16, 0>(x, blk, xc, ost, scale, d);
+    out_step<DK, OUT, BF16, NSL, 0>(x, blk, xc, ost, scale, d);
 }
 
-template <int DK, int OUT, bool BF16>
+template <int DK, int OUT, bool BF16, int NSL>
 struct ScanLayout {
-    static constexpr int BLK = ChunkBlock<DK, BF16>::BYTES;
+    static constexpr int BLK = ChunkBlock<DK, BF16, NSL>::BYTES;
     static constexpr int XC = Xchg<DK>::BYTES;
     static constexpr int OST = OStage<OUT>::BYTES;
-    static constexpr int BYTES = 2 * BLK + 2 * XC + 2 * OST;
+    static constexpr int BYTES = 2 * BLK + NSL * (XC + OST);
 };
 
-// One workgroup of four waves per (sequence, value head, 32 value columns):
-// waves 0 and 1 are the chain waves of the two 16-column slices, waves 2 and 3
-// their output waves.
-template <int DK, int OUT, bool BF16>
-__global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs a) {
-    using L = ScanLayout<DK, OUT, BF16>;
+// One workgroup of 2 NSL waves per (sequence, value head, 16 NSL value
+// columns): waves 0 .. NSL-1 are the chain waves of the NSL 16-column slices,
+// waves NSL .. 2 NSL - 1 their output waves.
+template <int DK, int OUT, bool BF16, int NSL>
+__global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillArgs a) {
+    using L = ScanLayout<DK, OUT, BF16, NSL>;
     constexpr int NT = DK / 16;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int sl = w & 1;            // slice: value columns col0 + 16 sl ..
-    const bool chain = w < 2;
+    const bool chain = w < NSL;
+    const int sl = chain ? w : w - NSL;  // slice: value columns col0 + 16 sl ..
     const int c = lane & 15, lg = lane >> 4;
     int blk = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int pair = blk % a.slices;
+    const int grp = blk % a.slices;
     blk /= a.slices;
     ScanCtx<DK> X;
     X.a = &a;
@@ -835,7 +870,8 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs a) 
     X.g = X.h / a.group;
     X.nch = (a.T + kC - 1) / kC;
     X.ws = ws_layout(a.batch, X.nch, a.h_qk, a.h_v, DK);
-    X.col0 = 32 * pair;
+    X.cols = 16 * NSL;
+    X.col0 = X.cols * grp;
 
     int s = X.b;
     if (a.state_slot != nullptr) {
@@ -846,7 +882,7 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs a) 
         }
     }
     unsigned char* xc = lds_raw + 2 * L::BLK + sl * L::XC;
-    unsigned char* ost = lds_raw + 2 * L::BLK + 2 * L::XC + sl * L::OST;
+    unsigned char* ost = lds_raw + 2 * L::BLK + NSL * L::XC + sl * L::OST;
     // chain wave: lane (c, g) holds H[d_k][j] = S[j][d_k] for d_k = pair_row(t, 4g + r)
     float* stp = a.state + (((size_t)s * a.h_v + X.h) * a.d_v + X.col0 + 16 * sl + c) * DK;
     f32x4 st[NT];
@@ -858,8 +894,8 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs a) 
 #pragma unroll
         for (int u = 0; u < DK / 32; ++u) put_h8(xc + Xchg<DK>::SB, u, pack_h8(st[2 * u], st[2 * u + 1]));
     } else {
-        const DmaCtx d0 = dma_ctx<DK, BF16>(X, 0, lds_raw, sl);
-        dma_slots<DK, BF16, 0, ChunkBlock<DK, BF16>::NLOAD / 2>(d0);
+        const DmaCtx d0 = dma_ctx<DK, BF16, NSL>(X, 0, lds_raw, sl);
+        dma_slots<DK, BF16, NSL, 0, ChunkBlock<DK, BF16, NSL>::NLOAD / NSL>(d0);
     }
     for (int ck = 0; ck < X.nch; ++ck) {
         // the output waves' loads of chunk ck have landed (the wait: loads into LDS count as
@@ -870,13 +906,13 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs a) 
         __syncthreads();
         const unsigned char* cur = lds_raw + (ck & 1) * L::BLK;
         if (chain) {
-            chain_chunk<DK, BF16>(st, cur, xc, sl);
+            chain_chunk<DK, BF16, NSL>(st, cur, xc, sl);
         } else {
             if (ck > 0) write_out<DK, OUT>(X, ost, ck - 1, sl);
             unsigned char* nxt = lds_raw + ((ck + 1) & 1) * L::BLK;
             // the next chunk (the last chunk loads itself again into the idle block: harmless)
-            const DmaCtx d = dma_ctx<DK, BF16>(X, ck + 1, nxt, sl);
-            out_chunk<DK, OUT, BF16>(cur, xc, ost, a.scale, d);
+            const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + 1, nxt, sl);
+            out_chunk<DK, OUT, BF16, NSL>(cur, xc, ost, a.scale, d);
         }
     }
     if (chain) {
@@ -895,34 +931,45 @@ hipError_t set_lds(K kernel, size_t lds) {
                                (int)lds);
 }
 
-template <int DK, int OUT, bool BF16>
-hipError_t launch_scan(const PrefillArgs& a, int grid, hipStream_t st) {
-    const size_t lds = ScanLayout<DK, OUT, BF16>::BYTES;
-    hipError_t e = set_lds(&prefill_scan_kernel<DK, OUT, BF16>, lds);
+template <int DK, int OUT, bool BF16, int NSL>
+hipError_t launch_scan_nsl(const PrefillArgs& a, hipStream_t st) {
+    PrefillArgs s = a;
+    s.slices = a.d_v / (16 * NSL);
+    const long long grid = (long long)a.batch * a.h_v * s.slices;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    const size_t lds = ScanLayout<DK, OUT, BF16, NSL>::BYTES;
+    hipError_t e = set_lds(&prefill_scan_kernel<DK, OUT, BF16, NSL>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT, BF16>), dim3(grid), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT, BF16, NSL>), dim3((int)grid), dim3(128 * NSL), lds, st, s);
     return hipGetLastError();
 }
 
+// Two 16-column slices per workgroup: with four (one fetch of each chunk's
+// operands for 64 columns, two waves per SIMD) the chain waves shared their
+// SIMDs and the scan measured 25% slower.
+template <int DK, int OUT, bool BF16>
+hipError_t launch_scan(const PrefillArgs& a, hipStream_t st) {
+    return launch_scan_nsl<DK, OUT, BF16, 2>(a, st);
+}
+
 template <int DK, bool BF16>
-hipError_t launch_dk(const PrefillArgs& a, int out_dtype, int prep_grid, int scan_grid, hipStream_t st) {
+hipError_t launch_dk(const PrefillArgs& a, int out_dtype, int prep_grid, hipStream_t st) {
     const size_t lds = sizeof(PrepLds<DK>);
     hipError_t e = set_lds(&prefill_prepare_kernel<DK, BF16>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_prepare_kernel<DK, BF16>), dim3(prep_grid), dim3(256), lds, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     switch (out_dtype) {
-        case GDN_F32: return launch_scan<DK, 0, BF16>(a, scan_grid, st);
-        case GDN_BF16: return launch_scan<DK, 1, BF16>(a, scan_grid, st);
-        case GDN_F16: return launch_scan<DK, 2, BF16>(a, scan_grid, st);
+        case GDN_F32: return launch_scan<DK, 0, BF16>(a, st);
+        case GDN_BF16: return launch_scan<DK, 1, BF16>(a, st);
+        case GDN_F16: return launch_scan<DK, 2, BF16>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int DK>
-hipError_t launch_dk_any(const PrefillArgs& a, int out_dtype, int prep_grid, int scan_grid, hipStream_t st) {
-    return a.qkv_bf16 ? launch_dk<DK, true>(a, out_dtype, prep_grid, scan_grid, st)
-                      : launch_dk<DK, false>(a, out_dtype, prep_grid, scan_grid, st);
+hipError_t launch_dk_any(const PrefillArgs& a, int out_dtype, int prep_grid, hipStream_t st) {
+    return a.qkv_bf16 ? launch_dk<DK, true>(a, out_dtype, prep_grid, st) : launch_dk<DK, false>(a, out_dtype, prep_grid, st);
 }
 
 }  // namespace
@@ -935,12 +982,11 @@ size_t prefill_workspace_bytes(int batch, int T, int h_qk, int h_v, int d_k) {
 hipError_t launch_prefill(const PrefillArgs& a, int d_k, int out_dtype, hipStream_t stream) {
     const int nch = (a.T + kC - 1) / kC;
     const long long prep = (long long)a.batch * nch * a.h_v;
-    const long long scan = (long long)a.batch * a.h_v * a.slices;
-    if (prep > 0x7fffffffLL || scan > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (prep > 0x7fffffffLL) return hipErrorInvalidValue;
     switch (d_k) {
-        case 32: return launch_dk_any<32>(a, out_dtype, (int)prep, (int)scan, stream);
-        case 64: return launch_dk_any<64>(a, out_dtype, (int)prep, (int)scan, stream);
-        case 128: return launch_dk_any<128>(a, out_dtype, (int)prep, (int)scan, stream);
+        case 32: return launch_dk_any<32>(a, out_dtype, (int)prep, stream);
+        case 64: return launch_dk_any<64>(a, out_dtype, (int)prep, stream);
+        case 128: return launch_dk_any<128>(a, out_dtype, (int)prep, stream);
         default: return hipErrorInvalidValue;
     }
 }

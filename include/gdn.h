@@ -186,8 +186,8 @@ int gdn_commit(const gdn_shape* shape, const int32_t* accepted_node, const void*
  * gdn_prefill_workspace_bytes(shape) bytes (16-byte aligned), used during the
  * call for the per-chunk operands that do not depend on the state (the UT
  * transform and masked Q K^T per chunk and value head in f16, the gate factors,
- * K^T per chunk and q/k head); about 1 MB per 64 tokens at 48 value heads and
- * d_k = 128.  Its contents on entry are ignored.  A missing or short workspace
+ * K and Q in f16 per chunk and q/k head); about 1.3 MB per 64 tokens at 48 value
+ * heads, 16 q/k heads and d_k = 128.  Its contents on entry are ignored.  A missing or short workspace
  * returns GDN_ERR_WORKSPACE.  Calls sharing one workspace must be ordered on
  * one stream.
  */

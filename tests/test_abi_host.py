@@ -200,8 +200,8 @@ def test_prefill_rejects_bad_requests():
     assert prefill(shape(**P), ws=None) == E["GDN_ERR_WORKSPACE"]
     sh = shape(**P)
     need = gb.lib().gdn_prefill_workspace_bytes(ctypes.byref(sh))
-    # 64 chunks x (48 heads x (T + P) f16 + 48 x 3 x 64 fp32 gates + 16 q/k heads x (K^T, K, Q) f16)
-    assert need == 64 * (48 * 2 * 64 * 64 * 2 + 48 * 3 * 64 * 4 + 16 * 3 * 128 * 64 * 2)
+    # 64 chunks x (48 heads x (T', P) f16 + 48 x 3 x 64 fp32 gates + 16 q/k heads x (K, Q) f16)
+    assert need == 64 * (48 * 2 * 64 * 64 * 2 + 48 * 3 * 64 * 4 + 16 * 2 * 128 * 64 * 2)
     assert prefill(sh, ws_bytes=need - 1) == E["GDN_ERR_WORKSPACE"]
     assert prefill(shape(**{**P, "n_nodes": 0}), q=None, ws=None) == 0
     assert prefill(shape(**{**P, "batch": 0}), q=None, ws=None) == 0

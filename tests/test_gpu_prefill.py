@@ -147,8 +147,8 @@ def test_prefill_deterministic_and_workspace():
     b = run_prefill(t)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     need = gb.gdn_prefill_workspace_bytes(t["q"], t["v"], t["state0"], a[0])
-    # 2 chunks x (3 heads x (T + P) f16 + 3 heads x gates + 1 q/k head x (K^T, K, Q) f16)
-    assert need == 2 * (3 * 2 * 64 * 64 * 2 + 3 * 3 * 64 * 4 + 3 * 128 * 64 * 2)
+    # 2 chunks x (3 heads x (T', P) f16 + 3 heads x gates + 1 q/k head x (K, Q) f16)
+    assert need == 2 * (3 * 2 * 64 * 64 * 2 + 3 * 3 * 64 * 4 + 2 * 128 * 64 * 2)
     # a caller-provided workspace with stale contents gives the same result
     ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
     c = run_prefill(t, workspace=ws)
