@@ -13,10 +13,11 @@
 // with the product by T applied once to the combined right-hand side.)
 //
 // Two kernels.
-//  * prepare (one workgroup per (sequence, chunk, value head), all in
-//    parallel): everything that does not depend on the state -- the gates,
-//    K K^T and Q K^T on the matrix cores, the masked matrices, and the UT
-//    transform T = (I + A)^{-1} in fp32 (16 x 16 diagonal blocks by forward
+//  * prepare (one workgroup per (sequence, chunk, q/k head), all in
+//    parallel): everything that does not depend on the state -- K K^T and
+//    Q K^T on the matrix cores once per q/k head, then per value head on one
+//    wave the gates, the masked matrices, and the UT transform
+//    T = (I + A)^{-1} in fp32 (16 x 16 diagonal blocks by forward
 //    substitution, off-diagonal blocks by v_mfma_f32_16x16x4_f32).  It writes
 //    T' and P = Gamma o tril(Q K^T) in f16, the per-token gate factors, and
 //    K, Q in f16 (once per q/k head) to the workspace, every matrix in the
@@ -39,8 +40,6 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 constexpr int kC = GDN_PREFILL_CHUNK;  // tokens per chunk
-constexpr int kLdT = kC + 8;           // row length (halves) of token-contiguous matrices
-constexpr int kLdF = kC + 4;           // row length (floats) of the fp32 A and T matrices
 constexpr float kLogFloor = -80.f;     // log alpha is clamped here (a zero gate -> e^-80)
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -139,25 +138,181 @@ __host__ __device__ inline WsLayout ws_layout(int B, int nch, int h_qk, int h_v,
 }
 
 // ---------------------------------------------------------------------------
-// prepare: one (sequence, chunk, value head) per workgroup
+// prepare: one (sequence, chunk, q/k head) per workgroup
 // ---------------------------------------------------------------------------
+// K and Q are loaded and K K^T, Q K^T formed once per q/k head (on the matrix
+// cores, four waves); then each of the head's value heads is handled by one
+// wave on its own, with no further barrier: gates, the masked A, the UT
+// transform T = (I + A)^-1 and the T' and P fragments.  Lower 16 x 16 tiles
+// are kept tile-major: tile (it, jt), jt <= it, is tile number
+// it (it + 1) / 2 + jt, element (r, c) at r * 16 + c.
+__device__ __forceinline__ constexpr int tix(int it, int jt) { return it * (it + 1) / 2 + jt; }
+
+// One wave's working set for one value head.  The diagonal tiles of T
+// replace those of A (each is read in full before it is overwritten); the
+// off-diagonal tiles of T have their own slots.
+struct PrepWave {
+    float ell[kC];       // l2_t (base-2 log gates, prefix-summed)
+    float be[kC];        // beta_t
+    float A[10][256];    // strict lower beta Gamma K K^T, lower tiles; diagonal tiles then hold T
+    float To[6][256];    // off-diagonal tiles of T = (I + A)^-1
+    float Y[256];        // scratch tile
+    __device__ float* T(int it, int jt) { return it == jt ? A[tix(it, it)] : To[tix(it, jt) - it]; }
+};
+
 template <int DK>
 struct PrepLds {
     static constexpr int kLdK = DK + 8;
-    union {
-        struct {
-            _Float16 Kf[kC * kLdK];  // K chunk [token][d_k]
-            _Float16 Qf[kC * kLdK];  // Q chunk [token][d_k]
-        } in;
-        struct {
-            float A[kC * kLdF];   // strict lower beta Gamma K K^T
-            float Tm[kC * kLdF];  // (I + A)^-1
-        } ut;
-    } u;
-    _Float16 P[kC * kLdT];  // Gamma o tril(Q K^T)
-    float Y[4][16 * 16];    // per-wave scratch block
-    float ell[kC], al[kC], be[kC];
+    float KK[10][256];  // K K^T, lower tiles
+    float QK[10][256];  // Q K^T, lower tiles
+    // then the K, Q chunk [token][d_k] (f16) for the Gram products, and afterwards
+    // in the same bytes one PrepWave per wave that works on a value head
+    static constexpr size_t kIn = 2 * (size_t)kC * kLdK * 2;
+    static size_t bytes(int waves) {
+        const size_t w = (size_t)waves * sizeof(PrepWave);
+        return 2 * 10 * 256 * 4 + (w > kIn ? w : kIn);
+    }
+    __device__ _Float16* Kf() { return reinterpret_cast<_Float16*>(this + 1); }
+    __device__ _Float16* Qf() { return Kf() + kC * kLdK; }
+    __device__ PrepWave& w(int i) { return reinterpret_cast<PrepWave*>(this + 1)[i]; }
 };
+
+// Orders this wave's LDS accesses for the compiler where lanes exchange data
+// through LDS (the hardware keeps one wave's LDS operations in order).
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
+// One value head's UT transform and output fragments, on one wave.
+template <int DK>
+__device__ __forceinline__ void prepare_head(PrepLds<DK>& L, PrepWave& W, const PrefillArgs& a, unsigned char* wsb,
+                                             const WsLayout& ws, int b, int ck, int nch, int hv) {
+    const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
+    const int t0 = ck * kC;
+    const size_t unit_v = ((size_t)b * nch + ck) * a.h_v + hv;
+
+    // gates: lane = token; l2_t by a wave prefix sum of the clamped log2 alpha
+    {
+        const bool in = t0 + lane < a.T;
+        const size_t gi = ((size_t)b * a.T + (in ? t0 + lane : a.T - 1)) * a.h_v + hv;
+        const float al = in ? a.alpha[gi] : 1.f;
+        const float bt = in ? a.beta[gi] : 0.f;
+        float x = fmaxf(log2_fast(al), kLogFloor * kLog2e);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        const float lC = __shfl(x, 63, 64);
+        W.ell[lane] = x;
+        W.be[lane] = bt;
+        float* gw = reinterpret_cast<float*>(wsb + ws.G) + unit_v * 3 * kC;
+        gw[lane] = exp2_fast(x);
+        gw[kC + lane] = bt;
+        gw[2 * kC + lane] = exp2_fast(lC - x);
+    }
+    wave_lds_order();
+
+    // A = strict_lower(beta_t Gamma_{t,i} K K^T) on the lower tiles
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int jt = 0; jt <= it; ++jt) {
+            const int i = 16 * jt + c;
+            const float li = W.ell[i];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * it + 4 * lg + r;
+                const float kk = L.KK[tix(it, jt)][(4 * lg + r) * 16 + c];
+                W.A[tix(it, jt)][(4 * lg + r) * 16 + c] = t > i ? W.be[t] * exp2_fast(W.ell[t] - li) * kk : 0.f;
+            }
+        }
+    wave_lds_order();
+
+    // diagonal 16 x 16 blocks of T by forward substitution: lane = (block, column)
+    {
+        const int bb = lane >> 4, j = lane & 15;
+        const float* Ab = W.A[tix(bb, bb)];
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float arow[16];
+#pragma unroll
+            for (int m4 = 0; m4 < 4; ++m4) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(Ab + t * 16 + 4 * m4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) arow[4 * m4 + e] = v[e];
+            }
+            float sum = (t == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < t; ++m) sum = fmaf(-arow[m], x[m], sum);
+            x[t] = sum;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) W.T(bb, bb)[t * 16 + j] = x[t];  // after all reads of A_bb
+    }
+    wave_lds_order();
+
+    // off-diagonal blocks by distance: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+    // (v_mfma_f32_16x16x4_f32: A[i][4 s + lg], B[4 s + lg][c], D rows 4 lg + r)
+#pragma unroll
+    for (int dist = 1; dist < 4; ++dist)
+#pragma unroll
+        for (int jb = 0; jb + dist < 4; ++jb) {
+            const int ib = jb + dist;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = jb; kb < ib; ++kb) {
+                const float* Ab = W.A[tix(ib, kb)];
+                const float* Tb = W.T(kb, jb);
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ab[c * 16 + 4 * s + lg], Tb[(4 * s + lg) * 16 + c], acc,
+                                                               0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) W.Y[(4 * lg + r) * 16 + c] = acc[r];
+            wave_lds_order();
+            const float* Ti = W.T(ib, ib);
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(Ti[c * 16 + 4 * s + lg], W.Y[(4 * s + lg) * 16 + c], x, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) W.T(ib, jb)[(4 * lg + r) * 16 + c] = -x[r];
+            wave_lds_order();
+        }
+
+    // T' = T diag(beta) and P = Gamma o tril(Q K^T) -> workspace in fragment
+    // order (the six lower-triangular fragments); zero above the diagonal
+    _Float16* Tw = reinterpret_cast<_Float16*>(wsb + ws.T) + unit_v * kC * kC;
+    _Float16* Pw = reinterpret_cast<_Float16*>(wsb + ws.P) + unit_v * kC * kC;
+#pragma unroll
+    for (int f = 0; f < 6; ++f) {
+        const int tile = f < 2 ? f : 2 + (f - 2) / 2, blk = f < 2 ? 0 : (f - 2) % 2;
+        const int t = pair_row(tile, c), i0 = 32 * blk + 8 * lg;
+        const int it = t >> 4, jt = i0 >> 4;
+        h8 tv, pv;
+        if (jt <= it) {
+            const float* trow = W.T(it, jt) + (t & 15) * 16 + (i0 & 15);
+            const float* qrow = L.QK[tix(it, jt)] + (t & 15) * 16 + (i0 & 15);
+            const f32x4 ta = *reinterpret_cast<const f32x4*>(trow), tb = *reinterpret_cast<const f32x4*>(trow + 4);
+            const f32x4 qa = *reinterpret_cast<const f32x4*>(qrow), qb = *reinterpret_cast<const f32x4*>(qrow + 4);
+            const float lt = W.ell[t];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = i0 + e;
+                const float tval = e < 4 ? ta[e] : tb[e - 4];
+                const float qval = e < 4 ? qa[e] : qb[e - 4];
+                tv[e] = (_Float16)(i <= t ? tval * W.be[i] : 0.f);
+                pv[e] = (_Float16)(i <= t ? exp2_fast(lt - W.ell[i]) * qval : 0.f);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tv[e] = pv[e] = (_Float16)0.f;
+        }
+        *reinterpret_cast<h8*>(Tw + (f * 64 + lane) * 8) = tv;
+        *reinterpret_cast<h8*>(Pw + (f * 64 + lane) * 8) = pv;
+    }
+}
 
 template <int DK, bool BF16>
 __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs a) {
@@ -165,22 +320,21 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
     constexpr int KSD = DK / 32;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     PrepLds<DK>& L = *reinterpret_cast<PrepLds<DK>*>(lds_raw);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nch = (a.T + kC - 1) / kC;
     int blk = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int h = blk % a.h_v;
-    blk /= a.h_v;
+    const int g = blk % a.h_qk;
+    blk /= a.h_qk;
     const int ck = blk % nch;
     const int b = blk / nch;
-    const int g = h / a.group;
     const int t0 = ck * kC;
     const WsLayout ws = ws_layout(a.batch, nch, a.h_qk, a.h_v, DK);
     unsigned char* wsb = static_cast<unsigned char*>(a.workspace);
-    const size_t unit_v = ((size_t)b * nch + ck) * a.h_v + h;
     const size_t unit_q = ((size_t)b * nch + ck) * a.h_qk + g;
 
-    // 1. K, Q chunk -> LDS (f16); gates -> LDS.  All loads are issued first
-    //    (token index clamped into the sequence), then converted and stored.
+    // 1. K, Q chunk -> LDS (f16).  All loads are issued first (token index
+    //    clamped into the sequence), then converted and stored; rows past T are zero.
     {
         constexpr int NK = kC * DK / 8 / 256;  // 8-element chunks per thread
         Raw8 rk[NK], rq[NK];
@@ -193,177 +347,51 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
             raw_load<BF16>(rk[n], a.k, src);
             raw_load<BF16>(rq[n], a.q, src);
         }
-        const int tg = t0 + (tid & 63) < a.T ? t0 + (tid & 63) : a.T - 1;
-        const float al = a.alpha[((size_t)b * a.T + tg) * a.h_v + h];
-        const float be = a.beta[((size_t)b * a.T + tg) * a.h_v + h];
 #pragma unroll
         for (int n = 0; n < NK; ++n) {
             const int e = tid + 256 * n;
             const int t = e / (DK / 8), d = 8 * (e % (DK / 8));
             const bool valid = t0 + t < a.T;
-            *reinterpret_cast<h8*>(&L.u.in.Kf[t * kLdK + d]) = raw_to_h8<BF16>(rk[n], valid);
-            *reinterpret_cast<h8*>(&L.u.in.Qf[t * kLdK + d]) = raw_to_h8<BF16>(rq[n], valid);
-        }
-        if (tid < kC) {
-            const bool in = t0 + tid < a.T;
-            L.al[tid] = in ? al : 1.f;
-            L.be[tid] = in ? be : 0.f;
+            *reinterpret_cast<h8*>(&L.Kf()[t * kLdK + d]) = raw_to_h8<BF16>(rk[n], valid);
+            *reinterpret_cast<h8*>(&L.Qf()[t * kLdK + d]) = raw_to_h8<BF16>(rq[n], valid);
         }
     }
     __syncthreads();
 
-    // 2. gates (wave 0): l_t (base 2) by a wave prefix sum; gamma_t, Gamma_{C,t} -> workspace.
-    //    K, Q -> workspace (waves 1-3, once per q/k head).
-    if (wave == 0) {
-        float x = fmaxf(log2_fast(L.al[lane]), kLogFloor * kLog2e);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
-        }
-        L.ell[lane] = x;
-        const float lC = __shfl(x, 63, 64);
-        float* gw = reinterpret_cast<float*>(wsb + ws.G) + unit_v * 3 * kC;
-        gw[lane] = exp2_fast(x);
-        gw[kC + lane] = L.be[lane];
-        gw[2 * kC + lane] = exp2_fast(lC - x);
-    } else if (h % a.group == 0) {
-        // K, Q in fragment order, one 16-byte piece (fragment f, lane l) per step
-        _Float16* kw = reinterpret_cast<_Float16*>(wsb + ws.K) + unit_q * kC * DK;
-        _Float16* qw = reinterpret_cast<_Float16*>(wsb + ws.Q) + unit_q * kC * DK;
-        constexpr int PIECES = DK * kC / 8;
-        for (int e = tid - 64; e < 2 * PIECES; e += 192) {
-            const int m = e / PIECES, i = e % PIECES;
-            const int f = i / 64, l = i % 64, c = l & 15, lg = l >> 4;
-            const int row = pair_row(f / KSD, c), col = 32 * (f % KSD) + 8 * lg;
-            const h8 v = *reinterpret_cast<const h8*>(&(m == 0 ? L.u.in.Kf : L.u.in.Qf)[row * kLdK + col]);
-            *reinterpret_cast<h8*>((m == 0 ? kw : qw) + 8 * i) = v;
-        }
-    }
-    __syncthreads();
-
-    // 3. Gram products on the lower 16 x 16 tiles (job = matrix x tile), kept in registers
-    f32x4 gram[5];
+    // 2. K K^T and Q K^T on the lower 16 x 16 tiles (20 jobs over the four waves);
+    //    K and Q -> workspace in fragment order
 #pragma unroll
     for (int jj = 0; jj < 5; ++jj) {
         const int job = wave + 4 * jj;
-        const int mat = job / 10, tix = job % 10;
-        const int it = tix < 1 ? 0 : tix < 3 ? 1 : tix < 6 ? 2 : 3;
-        const int jt = tix - it * (it + 1) / 2;
+        const int mat = job / 10, tx = job % 10;
+        const int it = tx < 1 ? 0 : tx < 3 ? 1 : tx < 6 ? 2 : 3;
+        const int jt = tx - it * (it + 1) / 2;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks)
-            acc = mfma16(frag(mat ? L.u.in.Qf : L.u.in.Kf, kLdK, 16 * it, 32 * ks, lane),
-                         frag(L.u.in.Kf, kLdK, 16 * jt, 32 * ks, lane), acc);
-        gram[jj] = acc;
-    }
-    __syncthreads();  // K, Q are dead: A and T overwrite them
+            acc = mfma16(frag(mat ? L.Qf() : L.Kf(), kLdK, 16 * it, 32 * ks, lane),
+                         frag(L.Kf(), kLdK, 16 * jt, 32 * ks, lane), acc);
+        float* dst = (mat ? L.QK : L.KK)[tx];
 #pragma unroll
-    for (int jj = 0; jj < 5; ++jj) {
-        const int job = wave + 4 * jj;
-        const int mat = job / 10, tix = job % 10;
-        const int it = tix < 1 ? 0 : tix < 3 ? 1 : tix < 6 ? 2 : 3;
-        const int jt = tix - it * (it + 1) / 2;
-        const int i = 16 * jt + (lane & 15);
-        const float li = L.ell[i];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * it + 4 * (lane >> 4) + r;
-            const float gm = exp2_fast(L.ell[t] - li);
-            if (mat == 0) L.u.ut.A[t * kLdF + i] = (t > i) ? L.be[t] * gm * gram[jj][r] : 0.f;
-            else L.P[t * kLdT + i] = (_Float16)((t >= i) ? gm * gram[jj][r] : 0.f);
-        }
+        for (int r = 0; r < 4; ++r) dst[(4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[r];
     }
-    __syncthreads();
-
-    // 4. T = (I + A)^-1: diagonal 16 x 16 blocks, column j per lane (wave = block)
     {
-        const int bb = wave, j = lane & 15;
-        const float* Ab = L.u.ut.A + 16 * bb * kLdF + 16 * bb;
-        float x[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            float arow[16];
-#pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(Ab + t * kLdF + 4 * m4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) arow[4 * m4 + e] = v[e];
-            }
-            float sum = (t == j) ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < t; ++m) sum = fmaf(-arow[m], x[m], sum);
-            x[t] = sum;
-        }
-        if (lane < 16) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) L.u.ut.Tm[(16 * bb + t) * kLdF + 16 * bb + j] = x[t];
+        _Float16* kw = reinterpret_cast<_Float16*>(wsb + ws.K) + unit_q * kC * DK;
+        _Float16* qw = reinterpret_cast<_Float16*>(wsb + ws.Q) + unit_q * kC * DK;
+        constexpr int PIECES = DK * kC / 8;
+        for (int e = tid; e < 2 * PIECES; e += 256) {
+            const int m = e / PIECES, i = e % PIECES;
+            const int f = i / 64, l = i % 64, c = l & 15, lg = l >> 4;
+            const int row = pair_row(f / KSD, c), col = 32 * (f % KSD) + 8 * lg;
+            const h8 v = *reinterpret_cast<const h8*>(&(m == 0 ? L.Kf() : L.Qf())[row * kLdK + col]);
+            *reinterpret_cast<h8*>((m == 0 ? kw : qw) + 8 * i) = v;
         }
     }
-    __syncthreads();
-    // off-diagonal blocks, by distance: X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj
-#pragma unroll
-    for (int dist = 1; dist < 4; ++dist) {
-        const int j = wave, i = wave + dist;
-        const bool active = i < 4;
-        if (active) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int kk = j; kk < i; ++kk) {
-                const float* Lb = L.u.ut.A + 16 * i * kLdF + 16 * kk;
-                const float* Rb = L.u.ut.Tm + 16 * kk * kLdF + 16 * j;
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Lb[(lane & 15) * kLdF + 4 * s + (lane >> 4)],
-                                                               Rb[(4 * s + (lane >> 4)) * kLdF + (lane & 15)], acc,
-                                                               0, 0, 0);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) L.Y[wave][(4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[r];
-        }
-        __syncthreads();
-        if (active) {
-            const float* Xi = L.u.ut.Tm + 16 * i * kLdF + 16 * i;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Xi[(lane & 15) * kLdF + 4 * s + (lane >> 4)],
-                                                           L.Y[wave][(4 * s + (lane >> 4)) * 16 + (lane & 15)], acc,
-                                                           0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                L.u.ut.Tm[(16 * i + 4 * (lane >> 4) + r) * kLdF + 16 * j + (lane & 15)] = -acc[r];
-        }
-        __syncthreads();
-    }
+    __syncthreads();  // K, Q are dead: the per-wave working sets overwrite them
 
-    // 5. T' = T diag(beta) (f16, zero above the diagonal) and P -> workspace in
-    //    fragment order (the six lower-triangular fragments), 16-byte stores
-    _Float16* Tw = reinterpret_cast<_Float16*>(wsb + ws.T) + unit_v * kC * kC;
-    _Float16* Pw = reinterpret_cast<_Float16*>(wsb + ws.P) + unit_v * kC * kC;
-    for (int e = tid; e < 2 * 6 * 64; e += 256) {
-        const int m = e / (6 * 64), i = e % (6 * 64);
-        const int f = i / 64, l = i % 64;
-        const int tile = f < 2 ? f : 2 + (f - 2) / 2, blk = f < 2 ? 0 : (f - 2) % 2;
-        const int t = pair_row(tile, l & 15), i0 = 32 * blk + 8 * (l >> 4);
-        // entries above the diagonal are zero (the LDS there holds stale values)
-        h8 v;
-        if (m == 0) {
-            const f32x4 t0 = *reinterpret_cast<const f32x4*>(&L.u.ut.Tm[t * kLdF + i0]);
-            const f32x4 t1 = *reinterpret_cast<const f32x4*>(&L.u.ut.Tm[t * kLdF + i0 + 4]);
-            const f32x4 b0 = *reinterpret_cast<const f32x4*>(&L.be[i0]);
-            const f32x4 b1 = *reinterpret_cast<const f32x4*>(&L.be[i0 + 4]);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                v[x] = (_Float16)((i0 + x <= t) ? t0[x] * b0[x] : 0.f);
-                v[4 + x] = (_Float16)((i0 + 4 + x <= t) ? t1[x] * b1[x] : 0.f);
-            }
-        } else {
-            const h8 pv = *reinterpret_cast<const h8*>(&L.P[t * kLdT + i0]);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) v[x] = (i0 + x <= t) ? pv[x] : (_Float16)0.f;
-        }
-        *reinterpret_cast<h8*>((m == 0 ? Tw : Pw) + 8 * i) = v;
-    }
+    // 3. one value head per wave (waves past the head count only help with steps 1-2)
+    for (int j = wave; j < a.group; j += 4)
+        prepare_head<DK>(L, L.w(wave), a, wsb, ws, b, ck, nch, g * a.group + j);
 }
 
 // ---------------------------------------------------------------------------
@@ -954,7 +982,7 @@ hipError_t launch_scan(const PrefillArgs& a, hipStream_t st) {
 
 template <int DK, bool BF16>
 hipError_t launch_dk(const PrefillArgs& a, int out_dtype, int prep_grid, hipStream_t st) {
-    const size_t lds = sizeof(PrepLds<DK>);
+    const size_t lds = PrepLds<DK>::bytes(a.group < 4 ? a.group : 4);
     hipError_t e = set_lds(&prefill_prepare_kernel<DK, BF16>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_prepare_kernel<DK, BF16>), dim3(prep_grid), dim3(256), lds, st, a);
@@ -981,7 +1009,7 @@ size_t prefill_workspace_bytes(int batch, int T, int h_qk, int h_v, int d_k) {
 
 hipError_t launch_prefill(const PrefillArgs& a, int d_k, int out_dtype, hipStream_t stream) {
     const int nch = (a.T + kC - 1) / kC;
-    const long long prep = (long long)a.batch * nch * a.h_v;
+    const long long prep = (long long)a.batch * nch * a.h_qk;
     if (prep > 0x7fffffffLL) return hipErrorInvalidValue;
     switch (d_k) {
         case 32: return launch_dk_any<32>(a, out_dtype, (int)prep, stream);
