@@ -126,6 +126,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work of the oracle baseline")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-secondary", action="store_true")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run only the chunked prefill leg and print its measurement (for counter profiles)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reads and writes MIB MiB), to scale "
                          "memory counters in a profile")
@@ -151,6 +153,9 @@ def main() -> int:
             torch.mul(src, 1.0, out=dst)  # one elementwise kernel: n*4 bytes read, n*4 written
         torch.cuda.synchronize()
         del src, dst
+    if args.only_prefill:
+        print(json.dumps({"prefill": bench_prefill(torch, gb, wl, dev, max(5, args.steps // 25))}), flush=True)
+        return 0
     w = wl.WORKLOADS["chain"]
     ledger = wl.algorithmic_bytes_verify(w)
     sets = make_sets(torch, wl, w, args.sets, dev)
