@@ -292,9 +292,43 @@ def secondary(torch, gb, wl, dev, args):
     log("batched_chain", out["batched_chain"])
     del sets
     torch.cuda.empty_cache()
+    out["replay_chain"] = bench_replay(torch, gb, wl, dev, args)
+    log("replay_chain", out["replay_chain"])
     out["prefill"] = bench_prefill(torch, gb, wl, dev, max(5, args.steps // 25))
     log("prefill", out["prefill"])
     return out
+
+
+def bench_replay(torch, gb, wl, dev, args):
+    """Decode step with commit by replay at the chain workload: one launch
+    replays the previous block's accepted prefix from the cached fp32 state,
+    writes the committed state and verifies the next block (outputs only, no
+    persisted node states).  Same rotation over buffer sets as the headline."""
+    w = wl.WORKLOADS["chain"]
+    led = wl.algorithmic_bytes_replay(w)
+    sets = []
+    for i in range(args.sets):
+        base = wl.WORKLOAD_SEEDS[w.name] + 7919 * i
+        prev = dev_set(torch, wl.make_inputs(w, seed=base), dev)
+        cur = dev_set(torch, wl.make_inputs(w, seed=base + 1), dev)
+        cur["out"] = torch.empty(w.batch, w.n_nodes, w.h_v, w.d_v, device=dev)
+        cur["prev"] = prev
+        sets.append(cur)
+
+    def step(s):
+        p = s["prev"]
+        gb.gdn_replay_verify_chain(p["accepted"], p["q"], p["k"], p["v"], p["alpha"], p["beta"], s["q"], s["k"],
+                                   s["v"], s["alpha"], s["beta"], s["state0"], out=s["out"])
+
+    sm, km = time_steps(torch, sets, step, step, args.steps, args.warmup)
+    res = {"tokens_per_s_per_layer": w.batch * w.n_nodes / (sm * 1e-3), "ms_per_step": sm,
+           "kernel_us": km * 1e3, "step_bytes": led["total"],
+           "achieved_gbs": led["total"] / (km * 1e-3) / 1e9,
+           "hbm_frac": led["total"] / (km * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "kernel": "replay_verify_chain_kernel<128,1,no persist,f32 out,nt>"}
+    del sets
+    torch.cuda.empty_cache()
+    return res
 
 
 def prefill_flops(w) -> float:

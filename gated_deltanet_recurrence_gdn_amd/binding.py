@@ -49,6 +49,8 @@ _SIGS = {
     "gdn_verify_tree": [ctypes.POINTER(GdnShape), _vp, ctypes.c_int32] + [_vp] * 11,
     "gdn_commit_verify_chain": [ctypes.POINTER(GdnShape)] + [_vp] * 15,
     "gdn_commit": [ctypes.POINTER(GdnShape)] + [_vp] * 7,
+    "gdn_commit_replay": [ctypes.POINTER(GdnShape), _vp, ctypes.c_int32] + [_vp] * 10,
+    "gdn_replay_verify_chain": [ctypes.POINTER(GdnShape)] + [_vp] * 18,
     "gdn_status_string": [ctypes.c_int],
     "gdn_tree_walk": [_vp, ctypes.c_int32, _vp, _vp],
     "gdn_prefill_workspace_bytes": [ctypes.POINTER(GdnShape)],
@@ -189,6 +191,41 @@ def gdn_commit(accepted_node, persist, state, *, final_state=None, state_slot=No
                           _dev_ptr(state, "state"), _dev_ptr(state_slot, "state_slot"),
                           _dev_ptr(status, "status"), _stream(stream))
     _check(rc, "gdn_commit")
+
+
+def gdn_commit_replay(accepted_node, q, k, v, alpha, beta, state, *, parent=None, state_slot=None, status=None,
+                      stream=None) -> None:
+    """Commit by replay: state[slot(b)] <- the state after node accepted_node[b],
+    re-run from state[slot(b)] over the node's root path (chain when ``parent``
+    is None; else a host parent array [N] or [B][N])."""
+    sh = _verify_shape(q, v, state, None, None, 1.0)
+    par, n_trees = None, 0
+    if parent is not None:
+        par = _host_parent(parent)
+        n_trees = 1 if par.ndim == 1 else par.shape[0]
+    rc = lib().gdn_commit_replay(ctypes.byref(sh), par.ctypes.data if par is not None else None, n_trees,
+                                 _dev_ptr(accepted_node, "accepted_node"), _dev_ptr(q, "q"), _dev_ptr(k, "k"),
+                                 _dev_ptr(v, "v"), _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                 _dev_ptr(state, "state"), _dev_ptr(state_slot, "state_slot"),
+                                 _dev_ptr(status, "status"), _stream(stream))
+    _check(rc, "gdn_commit_replay")
+
+
+def gdn_replay_verify_chain(accepted_prev, q_prev, k_prev, v_prev, alpha_prev, beta_prev, q, k, v, alpha, beta,
+                            state, *, out=None, persist=None, final_state=None, state_slot=None, status=None,
+                            scale: float = 1.0, stream=None) -> None:
+    """Commit the previous chain block by replay and verify the next one, in one launch."""
+    sh = _verify_shape(q, v, state, out, persist, scale)
+    rc = lib().gdn_replay_verify_chain(ctypes.byref(sh), _dev_ptr(accepted_prev, "accepted_prev"),
+                                       _dev_ptr(q_prev, "q_prev"), _dev_ptr(k_prev, "k_prev"),
+                                       _dev_ptr(v_prev, "v_prev"), _dev_ptr(alpha_prev, "alpha_prev"),
+                                       _dev_ptr(beta_prev, "beta_prev"), _dev_ptr(q, "q"), _dev_ptr(k, "k"),
+                                       _dev_ptr(v, "v"), _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                       _dev_ptr(state, "state"), _dev_ptr(state_slot, "state_slot"),
+                                       _dev_ptr(out, "out"), _dev_ptr(persist, "persist"),
+                                       _dev_ptr(final_state, "final_state"), _dev_ptr(status, "status"),
+                                       _stream(stream))
+    _check(rc, "gdn_replay_verify_chain")
 
 
 def _prefill_shape(q, v, state, out, scale) -> GdnShape:

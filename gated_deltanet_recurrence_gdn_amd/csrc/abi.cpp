@@ -28,6 +28,8 @@ int check_verify(const gdn_shape* sh, const void* q, const void* k, const void* 
     if (sh->d_k != 32 && sh->d_k != 64 && sh->d_k != 128) return GDN_ERR_SHAPE;
     if (sh->d_v < 16 || sh->d_v > 256 || sh->d_v % 16 != 0) return GDN_ERR_SHAPE;
     if (state_slot != nullptr && sh->n_slots < 1) return GDN_ERR_SHAPE;
+    // per-node offsets of persisted states are 32-bit in the kernels
+    if ((long long)sh->h_v * sh->d_v * sh->d_k * GDN_MAX_NODES >= (1LL << 32)) return GDN_ERR_SHAPE;
     if (!valid_dtype(sh->qkv_dtype) || !valid_dtype(sh->out_dtype) || !valid_dtype(sh->persist_dtype))
         return GDN_ERR_DTYPE;
     if (sh->qkv_dtype == GDN_F16) return GDN_ERR_DTYPE;
@@ -42,7 +44,7 @@ int check_verify(const gdn_shape* sh, const void* q, const void* k, const void* 
 }
 
 struct VerifyPlan {
-    int m_groups, waves, rows_per_wg, slices;
+    int m_groups, epl, waves, rows_per_wg, slices;
     size_t lds;
 };
 
@@ -53,11 +55,14 @@ size_t stage_bytes(int n, int d_k, int rows) {
     return (size_t)floats * 4;
 }
 
-// Rows per wave R = m_groups * 512 / d_k.  Small problems take one row group
-// per wave (more waves in flight for a batch-1 step); large ones take two at
-// d_k = 128, halving the per-node LDS traffic of k and q per row.  Waves per
-// workgroup: the most (<= 4) that divide d_v and fit the LDS budget.
-int plan_verify(const gdn_shape* sh, int fork_slots, VerifyPlan* p) {
+// Lane layout: 8 state elements per lane and M row groups per wave, so a
+// wave holds R = M * 512 / d_k rows.  Large launches at d_k = 128 take two row
+// groups (bandwidth-bound; halves the per-node LDS traffic of k and q per
+// row); small ones take one (more waves in flight for a batch-1 step).  Waves
+// per workgroup: the most (<= 4) whose rows divide d_v and whose LDS fits.
+// (A 16-element layout -- one wave per SIMD at batch 1 -- measured slower:
+// verify 11.3 us against 10.0 us, the tree 19.8 us against 15.0 us.)
+int plan_verify(const gdn_shape* sh, int fork_slots, VerifyPlan* p, int blocks = 1) {
     const int rpg = 512 / sh->d_k;
     int m = 1;
     const long long waves_m1 = (long long)sh->batch * sh->h_v * (sh->d_v / rpg);
@@ -67,9 +72,11 @@ int plan_verify(const gdn_shape* sh, int fork_slots, VerifyPlan* p) {
     for (int w = 4; w >= 1; w /= 2) {
         if (sh->d_v % (w * R) != 0) continue;
         const int rows = w * R;
-        const size_t lds = stage_bytes(sh->n_nodes, sh->d_k, rows) + (size_t)fork_slots * rows * sh->d_k * 4;
+        const size_t lds = (size_t)blocks * stage_bytes(sh->n_nodes, sh->d_k, rows) +
+                           (size_t)fork_slots * rows * sh->d_k * 4;
         if (lds > (size_t)kMaxLdsBytes) continue;
         p->m_groups = m;
+        p->epl = 8;
         p->waves = w;
         p->rows_per_wg = rows;
         p->slices = sh->d_v / rows;
@@ -198,7 +205,7 @@ int gdn_verify_chain(const gdn_shape* shape, const void* q, const void* k, const
     VerifyArgs a = make_args(shape, p, q, k, v, alpha, beta, state, state_slot, out, persist, final_state, status);
     const long long grid = (long long)shape->batch * shape->h_v * p.slices;
     if (grid > 0x7fffffffLL) return GDN_ERR_SHAPE;
-    hipError_t e = launch_verify(a, nullptr, shape->d_k, p.m_groups, persist_mode(shape, persist), p.waves,
+    hipError_t e = launch_verify(a, nullptr, shape->d_k, p.m_groups, p.epl, persist_mode(shape, persist), p.waves,
                                  p.lds, (int)grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -223,7 +230,7 @@ int gdn_commit_verify_chain(const gdn_shape* shape, const int32_t* accepted_prev
     a.persist_prev_f16 = shape->persist_dtype == GDN_F16;
     const long long grid = (long long)shape->batch * shape->h_v * p.slices;
     if (grid > 0x7fffffffLL) return GDN_ERR_SHAPE;
-    hipError_t e = launch_verify(a, nullptr, shape->d_k, p.m_groups, persist_mode(shape, persist), p.waves,
+    hipError_t e = launch_verify(a, nullptr, shape->d_k, p.m_groups, p.epl, persist_mode(shape, persist), p.waves,
                                  p.lds, (int)grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -255,7 +262,7 @@ int gdn_verify_tree(const gdn_shape* shape, const int32_t* parent, int32_t n_tre
         a.per_seq_tree = 0;
         const long long grid = (long long)B * shape->h_v * p.slices;
         if (grid > 0x7fffffffLL) return GDN_ERR_SHAPE;
-        hipError_t e = launch_verify(a, &ts, shape->d_k, p.m_groups, pm, p.waves, p.lds, (int)grid,
+        hipError_t e = launch_verify(a, &ts, shape->d_k, p.m_groups, p.epl, pm, p.waves, p.lds, (int)grid,
                                      static_cast<hipStream_t>(stream));
         return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
     }
@@ -267,11 +274,90 @@ int gdn_verify_tree(const gdn_shape* shape, const int32_t* parent, int32_t n_tre
         a.seq0 = s0;
         a.n_seq = ns;
         const int grid = ns * shape->h_v * p.slices;
-        hipError_t e = launch_verify(a, &ts, shape->d_k, p.m_groups, pm, p.waves, p.lds, grid,
+        hipError_t e = launch_verify(a, &ts, shape->d_k, p.m_groups, p.epl, pm, p.waves, p.lds, grid,
                                      static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return GDN_ERR_HIP;
     }
     return GDN_OK;
+}
+
+int gdn_commit_replay(const gdn_shape* shape, const int32_t* parent, int32_t n_trees,
+                      const int32_t* accepted_node, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, float* state, const int32_t* state_slot,
+                      int32_t* status, void* stream) {
+    int rc = check_verify(shape, q, k, v, alpha, beta, state, state_slot, nullptr, nullptr, nullptr);
+    if (rc != GDN_OK) return rc;
+    const int B = shape->batch, N = shape->n_nodes;
+    if (parent != nullptr) {
+        if (!(n_trees == 1 || (n_trees == B && B > 0))) return GDN_ERR_SHAPE;
+        int slots = 0;
+        uint16_t walk[GDN_MAX_NODES];
+        for (int t = 0; t < n_trees; ++t)
+            if ((rc = plan_tree(parent + (size_t)t * N, N, walk, &slots)) != GDN_OK) return rc;
+    }
+    if (B == 0) return GDN_OK;
+    if (accepted_node == nullptr) return GDN_ERR_NULL;
+    if (!aligned(accepted_node, 4)) return GDN_ERR_ALIGN;
+    VerifyPlan p;
+    if ((rc = plan_verify(shape, 0, &p)) != GDN_OK) return rc;
+    VerifyArgs a = make_args(shape, p, q, k, v, alpha, beta, state, state_slot, nullptr, nullptr, nullptr, status);
+    a.accepted_prev = accepted_node;
+    a.state_w = state;
+    a.nt_stores = (double)B * shape->h_v * shape->d_v * shape->d_k * 4 < 256.0 * (1 << 20);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (parent == nullptr) {
+        const long long grid = (long long)B * shape->h_v * p.slices;
+        if (grid > 0x7fffffffLL) return GDN_ERR_SHAPE;
+        hipError_t e = launch_replay(a, nullptr, kReplayChain, shape->d_k, p.m_groups, p.epl, 0, p.waves, p.lds, (int)grid, st);
+        return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    }
+    TreeParents tp;
+    std::memset(&tp, 0, sizeof(tp));
+    const int per_seq = n_trees > 1;
+    a.per_seq_tree = per_seq;
+    const int span = per_seq ? kTreesPerLaunch : B;
+    for (int s0 = 0; s0 < B; s0 += span) {
+        const int ns = (B - s0 < span) ? (B - s0) : span;
+        for (int t = 0; t < (per_seq ? ns : 1); ++t)
+            for (int n = 0; n < N; ++n) tp.p[t][n] = (int8_t)parent[(size_t)(per_seq ? s0 + t : 0) * N + n];
+        a.seq0 = s0;
+        a.n_seq = ns;
+        const long long grid = (long long)ns * shape->h_v * p.slices;
+        if (grid > 0x7fffffffLL) return GDN_ERR_SHAPE;
+        hipError_t e = launch_replay(a, &tp, kReplayTree, shape->d_k, p.m_groups, p.epl, 0, p.waves, p.lds, (int)grid, st);
+        if (e != hipSuccess) return GDN_ERR_HIP;
+    }
+    return GDN_OK;
+}
+
+int gdn_replay_verify_chain(const gdn_shape* shape, const int32_t* accepted_prev, const void* q_prev,
+                            const void* k_prev, const void* v_prev, const float* alpha_prev,
+                            const float* beta_prev, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, float* state, const int32_t* state_slot,
+                            void* out, void* persist, float* final_state, int32_t* status, void* stream) {
+    int rc = check_verify(shape, q, k, v, alpha, beta, state, state_slot, out, persist, final_state);
+    if (rc != GDN_OK || shape->batch == 0) return rc;
+    if (!accepted_prev || !q_prev || !k_prev || !v_prev || !alpha_prev || !beta_prev) return GDN_ERR_NULL;
+    if (!aligned(accepted_prev, 4) || !aligned(alpha_prev, 4) || !aligned(beta_prev, 4)) return GDN_ERR_ALIGN;
+    if (!aligned(q_prev, 16) || !aligned(k_prev, 16) || !aligned(v_prev, 16)) return GDN_ERR_ALIGN;
+    if (final_state != nullptr && final_state == state) return GDN_ERR_SHAPE;
+    VerifyPlan p;
+    if ((rc = plan_verify(shape, 0, &p, 2)) != GDN_OK) return rc;
+    VerifyArgs a = make_args(shape, p, q, k, v, alpha, beta, state, state_slot, out, persist, final_state, status);
+    a.accepted_prev = accepted_prev;
+    a.state_w = state;
+    a.rq = q_prev; a.rk = k_prev; a.rv = v_prev; a.ralpha = alpha_prev; a.rbeta = beta_prev;
+    {
+        const double head = (double)shape->batch * shape->h_v * shape->d_v * shape->d_k;
+        const size_t pb = persist == nullptr ? 0 : (shape->persist_dtype == GDN_F16 ? 2 : 4);
+        const double written = head * (4 + (final_state ? 4 : 0) + (double)shape->n_nodes * pb);
+        a.nt_stores = written < 256.0 * (1 << 20);
+    }
+    const long long grid = (long long)shape->batch * shape->h_v * p.slices;
+    if (grid > 0x7fffffffLL) return GDN_ERR_SHAPE;
+    hipError_t e = launch_replay(a, nullptr, kReplayVerifyChain, shape->d_k, p.m_groups, p.epl, persist_mode(shape, persist),
+                                 p.waves, p.lds, (int)grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 int gdn_commit(const gdn_shape* shape, const int32_t* accepted_node, const void* persist,

@@ -61,6 +61,28 @@ struct VerifyArgs {
     float* state_w;      // the state cache written by the fused commit (same buffer as `state`)
     int32_t persist_prev_f16;
     int32_t nt_stores;   // 1: write-once outputs with non-temporal stores
+    // commit by replay (replay launches only): the replayed block's inputs; for the
+    // replay-only launch they are q, k, v, alpha, beta above and these stay null
+    const void* rq;
+    const void* rk;
+    const void* rv;
+    const float* ralpha;
+    const float* rbeta;
+};
+
+// Parent arrays of up to kTreesPerLaunch trees, for a replay along the root
+// path of a node chosen on the device (tree replay launches only).
+struct TreeParents {
+    int8_t p[kTreesPerLaunch][kMaxNodes];
+};
+
+// What a verify-family launch does.
+enum VerifyKind : int {
+    kVerifyChain = 0,        // chain verify (with the fused persisted-copy commit when accepted_prev is set)
+    kVerifyTree = 1,         // tree verify, host-planned depth-first walk
+    kReplayChain = 2,        // commit by replay of nodes 0 .. accepted
+    kReplayTree = 3,         // commit by replay of the accepted node's root path
+    kReplayVerifyChain = 4,  // replay commit of the previous chain block, then verify the next
 };
 
 // Depth-first walk of up to kTreesPerLaunch trees (tree launches only).
@@ -107,10 +129,17 @@ struct PrefillArgs {
 };
 
 // Verify kernel launch.  d_k selects the instantiation; m_groups is the number
-// of row groups each wave keeps (see verify.hip); persist_mode 0 = none,
+// of row groups each wave keeps and epl the state elements per lane (8; see
+// verify.hip); persist_mode 0 = none,
 // 1 = f16, 2 = fp32; tree == nullptr launches the chain kernel.
-hipError_t launch_verify(const VerifyArgs& a, const TreeSched* tree, int d_k, int m_groups,
+hipError_t launch_verify(const VerifyArgs& a, const TreeSched* tree, int d_k, int m_groups, int epl,
                          int persist_mode, int waves_per_wg, size_t lds_bytes, int grid,
+                         hipStream_t stream);
+
+// Replay launches (kind kReplayChain, kReplayTree or kReplayVerifyChain); parents is
+// used by kReplayTree only.
+hipError_t launch_replay(const VerifyArgs& a, const TreeParents* parents, int kind, int d_k, int m_groups,
+                         int epl, int persist_mode, int waves_per_wg, size_t lds_bytes, int grid,
                          hipStream_t stream);
 
 // Chunked prefill: a parallel prepare kernel per (sequence, chunk, value head)

@@ -13,15 +13,17 @@
 //
 // Mapping.  Every value row S[j][:] evolves independently given k and q, so
 // a head is split over workgroups by rows.  A row of d_k fp32 is spread over
-// LPR = d_k / 8 lanes, 8 consecutive elements each, so one wave holds
-// RPG = 64 / LPR rows per row group and M row groups (R = M * RPG rows).
-// The two row reductions (S k and S q) are DPP sums over the LPR lanes of a
-// row; the persisted f16 row is written with one 16-byte store per lane, a
-// full 256-byte row per 16 lanes.  The state never leaves VGPRs between
-// nodes; only the persisted copies, the outputs and the final state are
-// written.  All per-node inputs (k, q rows as fp32, this slice of v, the
-// gates and q.k) are staged once into LDS, so the node loop issues no global
-// loads and never waits on the vector-memory counter.
+// LPR = d_k / EPL lanes, EPL elements each (the launches use EPL = 8; the body
+// also takes 16, computing every node bit-identically), so one wave holds RPG = 64 / LPR rows per row group and M row groups
+// (R = M * RPG rows).  Lane c of a row holds the 8-element chunks c, c + LPR,
+// ... of it.  The two row reductions (S k and S q) are DPP sums over the LPR
+// lanes of a row; each persisted f16 chunk is one 16-byte store, and the
+// chunks of one store instruction cover LPR * 16 contiguous bytes of a row.
+// The state never leaves VGPRs between nodes; only the persisted copies, the
+// outputs and the final state are written.  All per-node inputs (k, q rows as
+// fp32, this slice of v, the gates and q.k) are staged once into LDS, so the
+// node loop issues no global loads and never waits on the vector-memory
+// counter.
 //
 // Trees are walked depth first (the host computes the walk): a node whose
 // parent is the previous node continues in registers; otherwise the parent's
@@ -42,42 +44,321 @@ __device__ __forceinline__ void put_out(void* out, size_t idx, float o) {
 }
 
 // Per-node operands a lane needs, read from LDS one node ahead of use.
-template <int M>
+template <int M, int EPL>
 struct NodeOps {
-    float k[8], q[8];
+    float k[EPL], q[EPL];
     f32x4 coef;  // alpha, beta, q.k, unused
     float vb[M]; // beta * v for this lane's rows
 };
 
-template <int DK, int M>
-__device__ __forceinline__ void read_node(NodeOps<M>& x, const float* kL, const float* qL, const f32x4* cL,
+template <int DK, int M, int EPL>
+__device__ __forceinline__ void read_node(NodeOps<M, EPL>& x, const float* kL, const float* qL, const f32x4* cL,
                                           const float* vbL, int node, int c, int vr0, int rows) {
-    constexpr int RPG = 64 / (DK / 8);
-    const f32x4 k0 = *reinterpret_cast<const f32x4*>(kL + node * DK + 8 * c);
-    const f32x4 k1 = *reinterpret_cast<const f32x4*>(kL + node * DK + 8 * c + 4);
-    const f32x4 q0 = *reinterpret_cast<const f32x4*>(qL + node * DK + 8 * c);
-    const f32x4 q1 = *reinterpret_cast<const f32x4*>(qL + node * DK + 8 * c + 4);
+    constexpr int LPR = DK / EPL, RPG = 64 / LPR;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        x.k[e] = k0[e];
-        x.k[4 + e] = k1[e];
-        x.q[e] = q0[e];
-        x.q[4 + e] = q1[e];
+    for (int j = 0; j < EPL / 8; ++j) {
+        const int off = node * DK + 8 * (c + LPR * j);
+        const f32x4 k0 = *reinterpret_cast<const f32x4*>(kL + off);
+        const f32x4 k1 = *reinterpret_cast<const f32x4*>(kL + off + 4);
+        const f32x4 q0 = *reinterpret_cast<const f32x4*>(qL + off);
+        const f32x4 q1 = *reinterpret_cast<const f32x4*>(qL + off + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x.k[8 * j + e] = k0[e];
+            x.k[8 * j + 4 + e] = k1[e];
+            x.q[8 * j + e] = q0[e];
+            x.q[8 * j + 4 + e] = q1[e];
+        }
     }
     x.coef = cL[node];
 #pragma unroll
     for (int m = 0; m < M; ++m) x.vb[m] = vbL[node * rows + vr0 + m * RPG];
 }
 
-template <int DK, int M, bool TREE, int PMODE, int OUT, bool NT>
-__device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t* walk) {
-    constexpr int LPR = DK / 8;   // lanes per state row
+// Inputs of one block of draft nodes.
+struct BlockIn {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+};
+
+// One block's staging area in LDS: k[N][DK] and q[N][DK] as fp32, the node
+// coefficients (alpha, beta, q.k) as f32x4 [N], beta * v [N][rows] for the
+// workgroup's rows, and walk[N] (tree walk codes or a replay path).
+template <int DK>
+struct StageArea {
+    float* kL;
+    float* qL;
+    f32x4* cL;
+    float* vbL;
+    int* walkL;
+    __device__ static int floats(int N, int rows) { return (2 * N * DK + 4 * N + N * rows + N + 3) & ~3; }
+    __device__ StageArea(float* base, int N, int rows) {
+        kL = base;
+        qL = kL + N * DK;
+        cL = reinterpret_cast<f32x4*>(qL + N * DK);
+        vbL = reinterpret_cast<float*>(cL + N);
+        walkL = reinterpret_cast<int*>(vbL + N * rows);
+    }
+};
+
+// Stage every node's inputs of NB blocks.  One pass issues all of a thread's
+// global loads (k and q chunks, beta * v, the gates; of every block) before
+// any LDS store, so the common case (N * d_k / 8 <= threads) costs one memory
+// round trip.  `walk` (tree verify only) goes to block 0's walk area.
+template <int DK, int NB>
+__device__ __forceinline__ void stage_blocks(const StageArea<DK> (&sa)[2], const BlockIn (&in)[2],
+                                             const VerifyArgs& a, int b, int h, int g, int row0,
+                                             const uint16_t* walk) {
+    constexpr int LPR = DK / 8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = blockDim.x;
+    const int N = a.n_nodes, rows = a.rows_per_wg, DV = a.d_v;
+    const bool bf16 = a.qkv_bf16 != 0;
+    const int chunks = N * LPR;  // 8-element chunks of k (and of q)
+    const int nvb = N * rows;
+    const int items = chunks > nvb ? chunks : nvb;
+    for (int base = wave * 64; base < items; base += nthr) {
+        const int e = base + lane;
+        const bool has_kq = e < chunks, has_v = e < nvb, has_g = e < N;
+        float kf[NB][8], qf[NB][8], vv[NB], vbeta[NB], ga[NB], gb[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            vv[i] = vbeta[i] = ga[i] = gb[i] = 0.f;
+            if (has_kq) {
+                const size_t src = (((size_t)b * N + e / LPR) * a.h_qk + g) * DK + 8 * (e % LPR);
+                load8_as_f32(in[i].k, src, bf16, kf[i]);
+                load8_as_f32(in[i].q, src, bf16, qf[i]);
+            }
+            if (has_v) {
+                const int n = e / rows, j = e % rows;
+                vv[i] = load1_as_f32(in[i].v, (((size_t)b * N + n) * a.h_v + h) * DV + row0 + j, bf16);
+                vbeta[i] = in[i].beta[((size_t)b * N + n) * a.h_v + h];
+            }
+            if (has_g) {
+                ga[i] = in[i].alpha[((size_t)b * N + e) * a.h_v + h];
+                gb[i] = in[i].beta[((size_t)b * N + e) * a.h_v + h];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            float part = 0.f;
+            if (has_kq) {
+                float* kd = sa[i].kL + (e / LPR) * DK + 8 * (e % LPR);
+                float* qd = sa[i].qL + (e / LPR) * DK + 8 * (e % LPR);
+                *reinterpret_cast<f32x4*>(kd) = f32x4{kf[i][0], kf[i][1], kf[i][2], kf[i][3]};
+                *reinterpret_cast<f32x4*>(kd + 4) = f32x4{kf[i][4], kf[i][5], kf[i][6], kf[i][7]};
+                *reinterpret_cast<f32x4*>(qd) = f32x4{qf[i][0], qf[i][1], qf[i][2], qf[i][3]};
+                *reinterpret_cast<f32x4*>(qd + 4) = f32x4{qf[i][4], qf[i][5], qf[i][6], qf[i][7]};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) part = fmaf(kf[i][j], qf[i][j], part);
+            }
+            part = group_sum<LPR>(part);
+            if (has_kq && (e % LPR) == 0) reinterpret_cast<float*>(sa[i].cL + e / LPR)[2] = part;
+            if (has_v) sa[i].vbL[e] = vbeta[i] * vv[i];
+            if (has_g) {
+                reinterpret_cast<float*>(sa[i].cL + e)[0] = ga[i];
+                reinterpret_cast<float*>(sa[i].cL + e)[1] = gb[i];
+                if (i == 0 && walk != nullptr) sa[0].walkL[e] = walk[e];
+            }
+        }
+    }
+}
+
+// Where a lane's rows sit: the lane holds chunks c, c + LPR, ... of rows
+// wrow + r + m RPG, m < M, of the workgroup's slice.
+struct LaneRows {
+    int b, h, row0, wrow, r, c;
+};
+
+// This lane's part of rows wrow + r + m RPG of a d_v x DK fp32 head.
+template <int DK, int M, int EPL>
+__device__ __forceinline__ void load_rows(float (&S)[M][EPL], const float* head_base, const LaneRows& L) {
+    constexpr int LPR = DK / EPL, RPG = 64 / LPR;
+    const float* src = head_base + (size_t)(L.row0 + L.wrow + L.r) * DK + 8 * L.c;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int j = 0; j < EPL / 8; ++j) {
+            const float* p = src + (size_t)m * RPG * DK + 8 * LPR * j;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(p);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                S[m][8 * j + e] = x0[e];
+                S[m][8 * j + 4 + e] = x1[e];
+            }
+        }
+}
+
+template <int DK, int M, int EPL, bool NT>
+__device__ __forceinline__ void store_state_rows(float* head_base, const LaneRows& L, const float (&S)[M][EPL]) {
+    constexpr int LPR = DK / EPL, RPG = 64 / LPR;
+    float* dst = head_base + (size_t)(L.row0 + L.wrow + L.r) * DK + 8 * L.c;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int j = 0; j < EPL / 8; ++j) {
+            float* d = dst + (size_t)m * RPG * DK + 8 * LPR * j;
+            store_stream<NT>(f32x4{S[m][8 * j], S[m][8 * j + 1], S[m][8 * j + 2], S[m][8 * j + 3]},
+                             reinterpret_cast<f32x4*>(d));
+            store_stream<NT>(f32x4{S[m][8 * j + 4], S[m][8 * j + 5], S[m][8 * j + 6], S[m][8 * j + 7]},
+                             reinterpret_cast<f32x4*>(d + 4));
+        }
+}
+
+// The node loop over n_steps steps of one staged block: per step the optional
+// fork restore, the two row reductions, the update, the persisted copy, the
+// output, the optional fork save.  CODES: step st runs node walk[st] with its
+// fork bits (a tree walk, or a replay path whose codes carry no fork bits);
+// otherwise step st runs node st.  The next step's operands are read from LDS
+// while the current step computes.
+// OUTS = false (a replay): no outputs, so neither S q nor o is formed.
+template <int DK, int M, int EPL, bool CODES, int PMODE, int OUT, bool NT, bool OUTS = true>
+__device__ __forceinline__ void node_loop(float (&S)[M][EPL], const StageArea<DK>& sa, int n_steps,
+                                          const VerifyArgs& a, void* out, const LaneRows& L, float* myfork,
+                                          int fork_stride) {
+    constexpr int LPR = DK / EPL, RPG = 64 / LPR, NJ = EPL / 8;
+    const int lane = threadIdx.x & 63, c = L.c, b = L.b, h = L.h;
+    const int N = a.n_nodes, DV = a.d_v, rows = a.rows_per_wg;
+    const size_t head_elems = (size_t)DV * DK;
+    // per-node strides fit 32 bits (the host bounds h_v d_v d_k * 32 below 2^32):
+    // a lane's persist and output addresses are a base plus node * stride
+    const uint32_t pstride = (uint32_t)(a.h_v * head_elems);  // persist elements per node
+    const uint32_t ostride = (uint32_t)(a.h_v * DV);          // output elements per node
+    const int vr0 = L.wrow + L.r;  // this lane's first row inside the slice
+    const size_t seq0 = (size_t)b * N;
+    const size_t pbase = seq0 * pstride + (size_t)h * head_elems + (size_t)(L.row0 + vr0) * DK + 8 * c;
+    const size_t obase = seq0 * ostride + (size_t)h * DV + L.row0 + vr0;
+    const float scale = a.scale;
+
+    auto step = [&](const NodeOps<M, EPL>& x, int code) {
+        const int node = sched_node((uint16_t)code);
+        if constexpr (CODES) {
+            if (code & kSchedRestore) {
+                const float* src = myfork + sched_restore_slot((uint16_t)code) * fork_stride;
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int j = 0; j < 2 * NJ; ++j) {
+                        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (m * 64 + lane) * EPL + 4 * j);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) S[m][4 * j + e] = x0[e];
+                    }
+            }
+        }
+        const float al = x.coef[0];
+        const float bal = x.coef[1] * al;     // beta * alpha
+        const float sal = scale * al;         // scale * alpha
+        const float sqk = scale * x.coef[2];  // scale * (q . k)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            // Row sums in one fixed order for every layout: each 8-element chunk
+            // is summed with two accumulators (even and odd elements), and the
+            // chunk sums of a row meet in the binary tree of the DPP steps over
+            // LPR lanes.  With two chunks per lane (LPR = 8 at d_k = 128), lane c
+            // holds chunks c and c + 8: each chunk's sum runs the 8-lane tree on
+            // its own, leaving the sums of chunks 0-7 and 8-15, which are then
+            // added -- the same tree the 16-lane layout forms, so a node's state
+            // is bit-identical whichever layout a launch takes.
+            float pk = 0.f, pq = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int e0 = 8 * j;
+                float pk0 = S[m][e0] * x.k[e0], pk1 = S[m][e0 + 1] * x.k[e0 + 1];
+                float pq0 = S[m][e0] * x.q[e0], pq1 = S[m][e0 + 1] * x.q[e0 + 1];
+#pragma unroll
+                for (int e = e0 + 2; e < e0 + 8; e += 2) {
+                    pk0 = fmaf(S[m][e], x.k[e], pk0);
+                    pk1 = fmaf(S[m][e + 1], x.k[e + 1], pk1);
+                    if constexpr (OUTS) {
+                        pq0 = fmaf(S[m][e], x.q[e], pq0);
+                        pq1 = fmaf(S[m][e + 1], x.q[e + 1], pq1);
+                    }
+                }
+                const float sk = group_sum<LPR>(pk0 + pk1);
+                const float sq = OUTS ? group_sum<LPR>(pq0 + pq1) : 0.f;
+                if (j == 0) {
+                    pk = sk;
+                    pq = sq;
+                } else {
+                    pk += sk;
+                    pq += sq;
+                }
+            }
+            const float u = fmaf(-bal, pk, x.vb[m]);  // beta (v - alpha S k)
+            const float o = fmaf(sal, pq, sqk * u);   // scale (alpha S q + (q.k) u)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) S[m][e] = fmaf(al, S[m][e], u * x.k[e]);
+            // persisted states are written once and read later by commit, never by this kernel
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const size_t at = pbase + (uint32_t)node * pstride + (uint32_t)(m * RPG * DK + 8 * LPR * j);
+                if constexpr (PMODE == 1) {
+                    f16x8 hv;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hv[e] = (_Float16)S[m][8 * j + e];
+                    store_stream<NT>(hv, reinterpret_cast<f16x8*>(static_cast<_Float16*>(a.persist) + at));
+                } else if constexpr (PMODE == 2) {
+                    float* dst = static_cast<float*>(a.persist) + at;
+                    store_stream<NT>(f32x4{S[m][8 * j], S[m][8 * j + 1], S[m][8 * j + 2], S[m][8 * j + 3]},
+                                     reinterpret_cast<f32x4*>(dst));
+                    store_stream<NT>(f32x4{S[m][8 * j + 4], S[m][8 * j + 5], S[m][8 * j + 6], S[m][8 * j + 7]},
+                                     reinterpret_cast<f32x4*>(dst + 4));
+                }
+            }
+            if (OUTS && out != nullptr && c == 0)
+                put_out<OUT>(out, obase + (uint32_t)node * ostride + (uint32_t)(m * RPG), o);
+        }
+        if constexpr (CODES) {
+            if (code & kSchedSave) {
+                float* dst = myfork + sched_save_slot((uint16_t)code) * fork_stride;
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int j = 0; j < 2 * NJ; ++j)
+                        *reinterpret_cast<f32x4*>(dst + (m * 64 + lane) * EPL + 4 * j) =
+                            f32x4{S[m][4 * j], S[m][4 * j + 1], S[m][4 * j + 2], S[m][4 * j + 3]};
+            }
+        }
+    };
+    auto code_at = [&](int st) {
+        const int x = st < n_steps ? st : n_steps - 1;
+        return CODES ? sa.walkL[x] : x;
+    };
+
+    // Two operand buffers in ping-pong: while one node computes, the next
+    // node's operands are already on their way from LDS.
+    NodeOps<M, EPL> opA, opB;
+    int codeA = code_at(0), codeB;
+    read_node<DK, M, EPL>(opA, sa.kL, sa.qL, sa.cL, sa.vbL, sched_node((uint16_t)codeA), c, vr0, rows);
+    for (int st = 0; st < n_steps; st += 2) {
+        codeB = code_at(st + 1);
+        read_node<DK, M, EPL>(opB, sa.kL, sa.qL, sa.cL, sa.vbL, sched_node((uint16_t)codeB), c, vr0, rows);
+        step(opA, codeA);
+        if (st + 1 >= n_steps) break;
+        codeA = code_at(st + 2);
+        read_node<DK, M, EPL>(opA, sa.kL, sa.qL, sa.cL, sa.vbL, sched_node((uint16_t)codeA), c, vr0, rows);
+        step(opB, codeB);
+    }
+}
+
+// One launch of the verify family (see VerifyKind).  The per-node arithmetic
+// is the same in every kind, so a node's state does not depend on whether it
+// was reached by a chain, a tree walk or a replay.
+template <int DK, int M, int EPL, int KIND, int PMODE, int OUT, bool NT>
+__device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t* walk, const int8_t* par) {
+    constexpr int LPR = DK / EPL; // lanes per state row
     constexpr int RPG = 64 / LPR; // rows per row group
     constexpr int R = M * RPG;    // rows per wave
+    constexpr bool TREE = KIND == kVerifyTree;
+    constexpr bool REPLAY = KIND == kReplayChain || KIND == kReplayTree || KIND == kReplayVerifyChain;
+    constexpr int NB = KIND == kReplayVerifyChain ? 2 : 1;  // staged blocks
     extern __shared__ __align__(16) float lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nthr = blockDim.x, nwaves = nthr >> 6;
+    const int nwaves = blockDim.x >> 6;
 
     int blk = xcd_logical_block(blockIdx.x, gridDim.x);
     const int slice = blk % a.slices;
@@ -99,7 +380,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
             return;
         }
     }
-    // fused commit of the previous step: its accepted node must be in range
+    // the accepted node of the committed block (fused commit or replay) must be in range
     int acc = 0;
     if (a.accepted_prev != nullptr) {
         acc = a.accepted_prev[b];
@@ -109,302 +390,216 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
         }
     }
 
-    // LDS: k[N][DK], q[N][DK] (fp32), coef[N] (alpha, beta, q.k), beta*v[N][rows],
-    // walk[N] (trees), then the fork slots.
-    float* kL = lds;
-    float* qL = kL + N * DK;
-    f32x4* cL = reinterpret_cast<f32x4*>(qL + N * DK);
-    float* vbL = reinterpret_cast<float*>(cL + N);
-    int* walkL = reinterpret_cast<int*>(vbL + N * rows);
-    const int stage_floats = (2 * N * DK + 4 * N + N * rows + N + 3) & ~3;
-    float* forkL = lds + stage_floats;
+    const int stage_floats = StageArea<DK>::floats(N, rows);
+    // (the second area is used by a replay + verify only)
+    const StageArea<DK> sa[2] = {StageArea<DK>(lds, N, rows), StageArea<DK>(lds + stage_floats, N, rows)};
+    float* forkL = lds + NB * stage_floats;
 
     // 1. this wave's state rows -> VGPRs (issued first; the loads overlap staging)
-    const int c = lane % LPR, r = lane / LPR;
-    const int wrow = wave * R;  // first row of this wave inside the slice
+    LaneRows L;
+    L.b = b;
+    L.h = h;
+    L.row0 = row0;
+    L.c = lane % LPR;
+    L.r = lane / LPR;
+    L.wrow = wave * R;  // first row of this wave inside the slice
     const size_t head_elems = (size_t)DV * DK;
-    float S[M][8];
-    const size_t my_rows = (size_t)(row0 + wrow + r) * DK + 8 * c;  // this lane's first element in a head
-    if (a.accepted_prev == nullptr) {
-        const float* src = a.state + ((size_t)s * a.h_v + h) * head_elems + my_rows;
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (size_t)m * RPG * DK);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + (size_t)m * RPG * DK + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                S[m][e] = x0[e];
-                S[m][4 + e] = x1[e];
-            }
-        }
+    float S[M][EPL];
+    float* cache_head = (a.state_w != nullptr ? a.state_w : const_cast<float*>(a.state)) +
+                        ((size_t)s * a.h_v + h) * head_elems;
+    if (KIND != kVerifyChain || a.accepted_prev == nullptr) {
+        load_rows<DK, M, EPL>(S, a.state + ((size_t)s * a.h_v + h) * head_elems, L);
     } else {
         // Commit while loading: the initial state is the previous step's accepted node
         // (its exact fp32 final state when the whole block was accepted, else its persisted
         // copy widened to fp32); it is also written back to the state cache.
         if (a.final_prev != nullptr && acc == N - 1) {
-            const float* src = a.final_prev + ((size_t)b * a.h_v + h) * head_elems + my_rows;
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (size_t)m * RPG * DK);
-                const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + (size_t)m * RPG * DK + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    S[m][e] = x0[e];
-                    S[m][4 + e] = x1[e];
-                }
-            }
+            load_rows<DK, M, EPL>(S, a.final_prev + ((size_t)b * a.h_v + h) * head_elems, L);
         } else if (a.persist_prev_f16) {
             const _Float16* src = static_cast<const _Float16*>(a.persist_prev) +
-                                  (((size_t)b * N + acc) * a.h_v + h) * head_elems + my_rows;
+                                  (((size_t)b * N + acc) * a.h_v + h) * head_elems +
+                                  (size_t)(row0 + L.wrow + L.r) * DK + 8 * L.c;
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const f16x8 hv = *reinterpret_cast<const f16x8*>(src + (size_t)m * RPG * DK);
+            for (int m = 0; m < M; ++m)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) S[m][e] = (float)hv[e];
-            }
-        } else {
-            const float* src = static_cast<const float*>(a.persist_prev) +
-                               (((size_t)b * N + acc) * a.h_v + h) * head_elems + my_rows;
+                for (int j = 0; j < EPL / 8; ++j) {
+                    const f16x8 hv = *reinterpret_cast<const f16x8*>(src + (size_t)m * RPG * DK + 8 * LPR * j);
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (size_t)m * RPG * DK);
-                const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + (size_t)m * RPG * DK + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    S[m][e] = x0[e];
-                    S[m][4 + e] = x1[e];
+                    for (int e = 0; e < 8; ++e) S[m][8 * j + e] = (float)hv[e];
                 }
-            }
+        } else {
+            load_rows<DK, M, EPL>(S, static_cast<const float*>(a.persist_prev) +
+                                         (((size_t)b * N + acc) * a.h_v + h) * head_elems, L);
         }
-        float* dst = a.state_w + ((size_t)s * a.h_v + h) * head_elems + my_rows;
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            store_stream<NT>(f32x4{S[m][0], S[m][1], S[m][2], S[m][3]}, reinterpret_cast<f32x4*>(dst + (size_t)m * RPG * DK));
-            store_stream<NT>(f32x4{S[m][4], S[m][5], S[m][6], S[m][7]},
-                         reinterpret_cast<f32x4*>(dst + (size_t)m * RPG * DK + 4));
-        }
+        store_state_rows<DK, M, EPL, NT>(cache_head, L, S);
     }
 
-    // 2. stage every node's inputs.  One pass issues all of a thread's global
-    //    loads (k and q chunks, beta * v, the gates) before any LDS store, so
-    //    the common case (N * d_k / 8 <= threads) costs one memory round trip.
-    const bool bf16 = a.qkv_bf16 != 0;
-    const int chunks = N * LPR;  // 8-element chunks of k (and of q)
-    const int nvb = N * rows;
-    const int items = chunks > nvb ? chunks : nvb;
-    for (int base = wave * 64; base < items; base += nthr) {
-        const int e = base + lane;
-        float kf[8], qf[8], vv = 0.f, vbeta = 0.f, ga = 0.f, gb = 0.f;
-        const bool has_kq = e < chunks, has_v = e < nvb, has_g = e < N;
-        if (has_kq) {
-            const size_t src = (((size_t)b * N + e / LPR) * a.h_qk + g) * DK + 8 * (e % LPR);
-            load8_as_f32(a.k, src, bf16, kf);
-            load8_as_f32(a.q, src, bf16, qf);
-        }
-        if (has_v) {
-            const int n = e / rows, j = e % rows;
-            vv = load1_as_f32(a.v, (((size_t)b * N + n) * a.h_v + h) * DV + row0 + j, bf16);
-            vbeta = a.beta[((size_t)b * N + n) * a.h_v + h];
-        }
-        if (has_g) {
-            ga = a.alpha[((size_t)b * N + e) * a.h_v + h];
-            gb = a.beta[((size_t)b * N + e) * a.h_v + h];
-        }
-        float part = 0.f;
-        if (has_kq) {
-            float* kd = kL + (e / LPR) * DK + 8 * (e % LPR);
-            float* qd = qL + (e / LPR) * DK + 8 * (e % LPR);
-            *reinterpret_cast<f32x4*>(kd) = f32x4{kf[0], kf[1], kf[2], kf[3]};
-            *reinterpret_cast<f32x4*>(kd + 4) = f32x4{kf[4], kf[5], kf[6], kf[7]};
-            *reinterpret_cast<f32x4*>(qd) = f32x4{qf[0], qf[1], qf[2], qf[3]};
-            *reinterpret_cast<f32x4*>(qd + 4) = f32x4{qf[4], qf[5], qf[6], qf[7]};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) part = fmaf(kf[i], qf[i], part);
-        }
-        part = group_sum<LPR>(part);
-        if (has_kq && (e % LPR) == 0) reinterpret_cast<float*>(cL + e / LPR)[2] = part;
-        if (has_v) vbL[e] = vbeta * vv;
-        if (has_g) {
-            reinterpret_cast<float*>(cL + e)[0] = ga;
-            reinterpret_cast<float*>(cL + e)[1] = gb;
-            if constexpr (TREE) walkL[e] = walk[e];
+    // 2. stage every node's inputs (both blocks of a replay + verify)
+    if constexpr (KIND == kReplayVerifyChain) {
+        const BlockIn in[2] = {{a.rq, a.rk, a.rv, a.ralpha, a.rbeta}, {a.q, a.k, a.v, a.alpha, a.beta}};
+        stage_blocks<DK, 2>(sa, in, a, b, h, g, row0, nullptr);
+    } else {
+        const BlockIn in[2] = {{a.q, a.k, a.v, a.alpha, a.beta}, {a.q, a.k, a.v, a.alpha, a.beta}};
+        stage_blocks<DK, 1>(sa, in, a, b, h, g, row0, TREE ? walk : nullptr);
+    }
+    // a tree replay runs the accepted node's root path, root first
+    int n_steps = N;
+    if constexpr (KIND == kReplayChain || KIND == kReplayVerifyChain) n_steps = acc + 1;
+    if constexpr (KIND == kReplayTree) {
+        int d = 0;
+        for (int x = acc; x >= 0 && d < kMaxNodes; x = par[x]) ++d;
+        n_steps = d;
+        if (tid == 0) {
+            int x = acc;
+            for (int i = d - 1; i >= 0; --i) {
+                sa[0].walkL[i] = x;
+                x = par[x];
+            }
         }
     }
     __syncthreads();
 
-    // 3. node loop: reductions, update, persist, output; next node's operands
-    //    are read from LDS while the current node computes.
-    const size_t node_elems = (size_t)a.h_v * head_elems;  // persist elements per node
-    const size_t prow = (size_t)h * head_elems + (size_t)(row0 + wrow + r) * DK + 8 * c;
+    // 3. the node loops
     const int fork_stride = nwaves * R * DK;
-    float* myfork = forkL + wrow * DK;
-    const float scale = a.scale;
-    const int vr0 = wrow + r;  // this lane's first row inside the slice
-
-    // One node: optional fork restore, the two row reductions, the update,
-    // the persisted copy, the output, optional fork save.
-    auto step = [&](const NodeOps<M>& x, int code) {
-        const int node = sched_node((uint16_t)code);
-        if constexpr (TREE) {
-            if (code & kSchedRestore) {
-                const float* src = myfork + sched_restore_slot((uint16_t)code) * fork_stride;
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (m * 64 + lane) * 8);
-                    const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + (m * 64 + lane) * 8 + 4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        S[m][e] = x0[e];
-                        S[m][4 + e] = x1[e];
-                    }
-                }
-            }
-        }
-        const float al = x.coef[0];
-        const float bal = x.coef[1] * al;     // beta * alpha
-        const float sal = scale * al;         // scale * alpha
-        const float sqk = scale * x.coef[2];  // scale * (q . k)
-        const size_t nbase = ((size_t)b * N + node);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            // two accumulators per product halve the dependent FMA chain
-            float pk0 = S[m][0] * x.k[0], pk1 = S[m][1] * x.k[1];
-            float pq0 = S[m][0] * x.q[0], pq1 = S[m][1] * x.q[1];
-#pragma unroll
-            for (int e = 2; e < 8; e += 2) {
-                pk0 = fmaf(S[m][e], x.k[e], pk0);
-                pk1 = fmaf(S[m][e + 1], x.k[e + 1], pk1);
-                pq0 = fmaf(S[m][e], x.q[e], pq0);
-                pq1 = fmaf(S[m][e + 1], x.q[e + 1], pq1);
-            }
-            const float pk = group_sum<LPR>(pk0 + pk1);
-            const float pq = group_sum<LPR>(pq0 + pq1);
-            const float u = fmaf(-bal, pk, x.vb[m]);  // beta (v - alpha S k)
-            const float o = fmaf(sal, pq, sqk * u);   // scale (alpha S q + (q.k) u)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) S[m][e] = fmaf(al, S[m][e], u * x.k[e]);
-            // persisted states are written once and read later by commit, never by this kernel
-            if constexpr (PMODE == 1) {
-                f16x8 hv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) hv[e] = (_Float16)S[m][e];
-                store_stream<NT>(hv, reinterpret_cast<f16x8*>(static_cast<_Float16*>(a.persist) + nbase * node_elems +
-                                                          prow + (size_t)m * RPG * DK));
-            } else if constexpr (PMODE == 2) {
-                float* dst = static_cast<float*>(a.persist) + nbase * node_elems + prow + (size_t)m * RPG * DK;
-                store_stream<NT>(f32x4{S[m][0], S[m][1], S[m][2], S[m][3]}, reinterpret_cast<f32x4*>(dst));
-                store_stream<NT>(f32x4{S[m][4], S[m][5], S[m][6], S[m][7]}, reinterpret_cast<f32x4*>(dst + 4));
-            }
-            if (a.out != nullptr && c == 0)
-                put_out<OUT>(a.out, (nbase * a.h_v + h) * DV + row0 + vr0 + m * RPG, o);
-        }
-        if constexpr (TREE) {
-            if (code & kSchedSave) {
-                float* dst = myfork + sched_save_slot((uint16_t)code) * fork_stride;
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    *reinterpret_cast<f32x4*>(dst + (m * 64 + lane) * 8) = f32x4{S[m][0], S[m][1], S[m][2], S[m][3]};
-                    *reinterpret_cast<f32x4*>(dst + (m * 64 + lane) * 8 + 4) = f32x4{S[m][4], S[m][5], S[m][6], S[m][7]};
-                }
-            }
-        }
-    };
-    auto code_at = [&](int st) { return TREE ? walkL[st < N ? st : N - 1] : (st < N ? st : N - 1); };
-
-    // Two operand buffers in ping-pong: while one node computes, the next
-    // node's operands are already on their way from LDS.
-    NodeOps<M> opA, opB;
-    int codeA = code_at(0), codeB;
-    read_node<DK, M>(opA, kL, qL, cL, vbL, sched_node((uint16_t)codeA), c, vr0, rows);
-    for (int st = 0; st < N; st += 2) {
-        codeB = code_at(st + 1);
-        read_node<DK, M>(opB, kL, qL, cL, vbL, sched_node((uint16_t)codeB), c, vr0, rows);
-        step(opA, codeA);
-        if (st + 1 >= N) break;
-        codeA = code_at(st + 2);
-        read_node<DK, M>(opA, kL, qL, cL, vbL, sched_node((uint16_t)codeA), c, vr0, rows);
-        step(opB, codeB);
+    float* myfork = forkL + L.wrow * DK;
+    if constexpr (REPLAY) {
+        // replay of the committed block: no outputs, no persisted copies; the result
+        // is the committed state
+        node_loop<DK, M, EPL, KIND == kReplayTree, 0, OUT, NT, false>(S, sa[0], n_steps, a, nullptr, L, myfork,
+                                                                      fork_stride);
+        store_state_rows<DK, M, EPL, NT>(cache_head, L, S);
     }
-
-    // 4. final state (chains): the exact fp32 state after node N-1
-    if constexpr (!TREE) {
-        if (a.final_state != nullptr) {
-            float* dst = a.final_state + ((size_t)b * a.h_v + h) * head_elems + (size_t)(row0 + wrow + r) * DK + 8 * c;
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float* d = dst + (size_t)m * RPG * DK;
-                store_stream<NT>(f32x4{S[m][0], S[m][1], S[m][2], S[m][3]}, reinterpret_cast<f32x4*>(d));
-                store_stream<NT>(f32x4{S[m][4], S[m][5], S[m][6], S[m][7]}, reinterpret_cast<f32x4*>(d + 4));
-            }
+    if constexpr (KIND == kReplayVerifyChain || !REPLAY) {
+        node_loop<DK, M, EPL, TREE, PMODE, OUT, NT>(S, sa[NB - 1], N, a, a.out, L, myfork, fork_stride);
+        // 4. final state (chains): the exact fp32 state after node N-1
+        if constexpr (!TREE) {
+            if (a.final_state != nullptr)
+                store_state_rows<DK, M, EPL, NT>(a.final_state + ((size_t)b * a.h_v + h) * head_elems, L, S);
         }
     }
 }
 
-template <int DK, int M, int PMODE, int OUT, bool NT>
+// Kernel template arguments: <d_k, row groups per wave M, elements per lane
+// EPL, persist mode (0 none, 1 f16, 2 fp32), output dtype (0 fp32, 1 bf16,
+// 2 f16), non-temporal stores>.
+template <int DK, int M, int EPL, int PMODE, int OUT, bool NT>
 __global__ __launch_bounds__(256) void verify_chain_kernel(const VerifyArgs a) {
-    verify_body<DK, M, false, PMODE, OUT, NT>(a, nullptr);
+    verify_body<DK, M, EPL, kVerifyChain, PMODE, OUT, NT>(a, nullptr, nullptr);
 }
 
 // The fused commit + verify launch: the same body, under its own symbol so kernel
 // traces and counters tell it apart from a plain verify.
-template <int DK, int M, int PMODE, int OUT, bool NT>
+template <int DK, int M, int EPL, int PMODE, int OUT, bool NT>
 __global__ __launch_bounds__(256) void commit_verify_chain_kernel(const VerifyArgs a) {
-    verify_body<DK, M, false, PMODE, OUT, NT>(a, nullptr);
+    verify_body<DK, M, EPL, kVerifyChain, PMODE, OUT, NT>(a, nullptr, nullptr);
 }
 
-template <int DK, int M, int PMODE, int OUT>
+template <int DK, int M, int EPL, int PMODE, int OUT>
 __global__ __launch_bounds__(256) void verify_tree_kernel(const VerifyArgs a, const TreeSched t) {
     const int bl = xcd_logical_block(blockIdx.x, gridDim.x) / (a.slices * a.h_v);
-    verify_body<DK, M, true, PMODE, OUT, true>(a, t.step[a.per_seq_tree ? bl : 0]);
+    verify_body<DK, M, EPL, kVerifyTree, PMODE, OUT, true>(a, t.step[a.per_seq_tree ? bl : 0], nullptr);
 }
 
-template <int DK, int M, int PMODE, int OUT>
+template <int DK, int M, int EPL, bool NT>
+__global__ __launch_bounds__(256) void replay_chain_kernel(const VerifyArgs a) {
+    verify_body<DK, M, EPL, kReplayChain, 0, 0, NT>(a, nullptr, nullptr);
+}
+
+template <int DK, int M, int EPL, bool NT>
+__global__ __launch_bounds__(256) void replay_tree_kernel(const VerifyArgs a, const TreeParents t) {
+    const int bl = xcd_logical_block(blockIdx.x, gridDim.x) / (a.slices * a.h_v);
+    verify_body<DK, M, EPL, kReplayTree, 0, 0, NT>(a, nullptr, t.p[a.per_seq_tree ? bl : 0]);
+}
+
+template <int DK, int M, int EPL, int PMODE, int OUT, bool NT>
+__global__ __launch_bounds__(256) void replay_verify_chain_kernel(const VerifyArgs a) {
+    verify_body<DK, M, EPL, kReplayVerifyChain, PMODE, OUT, NT>(a, nullptr, nullptr);
+}
+
+template <int DK, int M, int EPL, int PMODE, int OUT>
 hipError_t launch_one(const VerifyArgs& a, const TreeSched* t, int waves, size_t lds, int grid, hipStream_t st) {
+    const dim3 g(grid), blk(64 * waves);
     if (t != nullptr)
-        hipLaunchKernelGGL((verify_tree_kernel<DK, M, PMODE, OUT>), dim3(grid), dim3(64 * waves), lds, st, a, *t);
+        hipLaunchKernelGGL((verify_tree_kernel<DK, M, EPL, PMODE, OUT>), g, blk, lds, st, a, *t);
     else if (a.accepted_prev != nullptr && a.nt_stores)
-        hipLaunchKernelGGL((commit_verify_chain_kernel<DK, M, PMODE, OUT, true>), dim3(grid), dim3(64 * waves), lds,
-                           st, a);
+        hipLaunchKernelGGL((commit_verify_chain_kernel<DK, M, EPL, PMODE, OUT, true>), g, blk, lds, st, a);
     else if (a.accepted_prev != nullptr)
-        hipLaunchKernelGGL((commit_verify_chain_kernel<DK, M, PMODE, OUT, false>), dim3(grid), dim3(64 * waves), lds,
-                           st, a);
+        hipLaunchKernelGGL((commit_verify_chain_kernel<DK, M, EPL, PMODE, OUT, false>), g, blk, lds, st, a);
     else if (a.nt_stores)
-        hipLaunchKernelGGL((verify_chain_kernel<DK, M, PMODE, OUT, true>), dim3(grid), dim3(64 * waves), lds, st, a);
+        hipLaunchKernelGGL((verify_chain_kernel<DK, M, EPL, PMODE, OUT, true>), g, blk, lds, st, a);
     else
-        hipLaunchKernelGGL((verify_chain_kernel<DK, M, PMODE, OUT, false>), dim3(grid), dim3(64 * waves), lds, st, a);
+        hipLaunchKernelGGL((verify_chain_kernel<DK, M, EPL, PMODE, OUT, false>), g, blk, lds, st, a);
     return hipGetLastError();
 }
 
-template <int DK, int M, int PMODE>
+template <int DK, int M, int EPL, int PMODE>
 hipError_t launch_dkmp(const VerifyArgs& a, const TreeSched* t, int waves, size_t lds, int grid, hipStream_t st) {
     switch (a.out_dtype) {
-        case GDN_F32: return launch_one<DK, M, PMODE, 0>(a, t, waves, lds, grid, st);
-        case GDN_BF16: return launch_one<DK, M, PMODE, 1>(a, t, waves, lds, grid, st);
-        case GDN_F16: return launch_one<DK, M, PMODE, 2>(a, t, waves, lds, grid, st);
+        case GDN_F32: return launch_one<DK, M, EPL, PMODE, 0>(a, t, waves, lds, grid, st);
+        case GDN_BF16: return launch_one<DK, M, EPL, PMODE, 1>(a, t, waves, lds, grid, st);
+        case GDN_F16: return launch_one<DK, M, EPL, PMODE, 2>(a, t, waves, lds, grid, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int DK, int M>
-hipError_t launch_dkm(const VerifyArgs& a, const TreeSched* t, int pmode, int waves, size_t lds,
-                      int grid, hipStream_t st) {
+template <int DK, int M, int EPL>
+hipError_t launch_dkm(const VerifyArgs& a, const TreeSched* t, int pmode, int waves, size_t lds, int grid,
+                      hipStream_t st) {
     switch (pmode) {
-        case 0: return launch_dkmp<DK, M, 0>(a, t, waves, lds, grid, st);
-        case 1: return launch_dkmp<DK, M, 1>(a, t, waves, lds, grid, st);
-        case 2: return launch_dkmp<DK, M, 2>(a, t, waves, lds, grid, st);
+        case 0: return launch_dkmp<DK, M, EPL, 0>(a, t, waves, lds, grid, st);
+        case 1: return launch_dkmp<DK, M, EPL, 1>(a, t, waves, lds, grid, st);
+        case 2: return launch_dkmp<DK, M, EPL, 2>(a, t, waves, lds, grid, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <int DK, int M, int EPL>
+hipError_t launch_replay_dkm(const VerifyArgs& a, const TreeParents* tp, int kind, int pmode, int waves, size_t lds,
+                             int grid, hipStream_t st) {
+    const dim3 g(grid), blk(64 * waves);
+    if (kind == kReplayChain) {
+        if (a.nt_stores) hipLaunchKernelGGL((replay_chain_kernel<DK, M, EPL, true>), g, blk, lds, st, a);
+        else hipLaunchKernelGGL((replay_chain_kernel<DK, M, EPL, false>), g, blk, lds, st, a);
+    } else if (kind == kReplayTree) {
+        if (a.nt_stores) hipLaunchKernelGGL((replay_tree_kernel<DK, M, EPL, true>), g, blk, lds, st, a, *tp);
+        else hipLaunchKernelGGL((replay_tree_kernel<DK, M, EPL, false>), g, blk, lds, st, a, *tp);
+    } else if (kind == kReplayVerifyChain) {
+        // outputs in fp32, f16 or bf16; node states persisted or not (the replay design persists none)
+#define GDN_RV(PM, OT)                                                                                              \
+    do {                                                                                                            \
+        if (a.nt_stores) hipLaunchKernelGGL((replay_verify_chain_kernel<DK, M, EPL, PM, OT, true>), g, blk, lds, st, a); \
+        else hipLaunchKernelGGL((replay_verify_chain_kernel<DK, M, EPL, PM, OT, false>), g, blk, lds, st, a);       \
+    } while (0)
+        const int ot = a.out_dtype == GDN_F32 ? 0 : a.out_dtype == GDN_BF16 ? 1 : 2;
+        if (pmode == 0) { if (ot == 0) GDN_RV(0, 0); else if (ot == 1) GDN_RV(0, 1); else GDN_RV(0, 2); }
+        else if (pmode == 1) { if (ot == 0) GDN_RV(1, 0); else if (ot == 1) GDN_RV(1, 1); else GDN_RV(1, 2); }
+        else { if (ot == 0) GDN_RV(2, 0); else if (ot == 1) GDN_RV(2, 1); else GDN_RV(2, 2); }
+#undef GDN_RV
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_verify(const VerifyArgs& a, const TreeSched* tree, int d_k, int m_groups,
-                         int persist_mode, int waves_per_wg, size_t lds_bytes, int grid,
-                         hipStream_t stream) {
-    if (d_k == 128 && m_groups == 1) return launch_dkm<128, 1>(a, tree, persist_mode, waves_per_wg, lds_bytes, grid, stream);
-    if (d_k == 128 && m_groups == 2) return launch_dkm<128, 2>(a, tree, persist_mode, waves_per_wg, lds_bytes, grid, stream);
-    if (d_k == 64 && m_groups == 1) return launch_dkm<64, 1>(a, tree, persist_mode, waves_per_wg, lds_bytes, grid, stream);
-    if (d_k == 32 && m_groups == 1) return launch_dkm<32, 1>(a, tree, persist_mode, waves_per_wg, lds_bytes, grid, stream);
+// The lane layouts built: 8 elements per lane; d_k 128 with one or two row
+// groups, d_k 64 and 32 with one.
+hipError_t launch_replay(const VerifyArgs& a, const TreeParents* parents, int kind, int d_k, int m_groups, int epl,
+                         int persist_mode, int waves, size_t lds, int grid, hipStream_t st) {
+    if (d_k == 128 && m_groups == 1 && epl == 8) return launch_replay_dkm<128, 1, 8>(a, parents, kind, persist_mode, waves, lds, grid, st);
+    if (d_k == 128 && m_groups == 2 && epl == 8) return launch_replay_dkm<128, 2, 8>(a, parents, kind, persist_mode, waves, lds, grid, st);
+    if (d_k == 64 && m_groups == 1 && epl == 8) return launch_replay_dkm<64, 1, 8>(a, parents, kind, persist_mode, waves, lds, grid, st);
+    if (d_k == 32 && m_groups == 1 && epl == 8) return launch_replay_dkm<32, 1, 8>(a, parents, kind, persist_mode, waves, lds, grid, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_verify(const VerifyArgs& a, const TreeSched* tree, int d_k, int m_groups, int epl, int persist_mode,
+                         int waves, size_t lds, int grid, hipStream_t st) {
+    if (d_k == 128 && m_groups == 1 && epl == 8) return launch_dkm<128, 1, 8>(a, tree, persist_mode, waves, lds, grid, st);
+    if (d_k == 128 && m_groups == 2 && epl == 8) return launch_dkm<128, 2, 8>(a, tree, persist_mode, waves, lds, grid, st);
+    if (d_k == 64 && m_groups == 1 && epl == 8) return launch_dkm<64, 1, 8>(a, tree, persist_mode, waves, lds, grid, st);
+    if (d_k == 32 && m_groups == 1 && epl == 8) return launch_dkm<32, 1, 8>(a, tree, persist_mode, waves, lds, grid, st);
     return hipErrorInvalidValue;
 }
 

@@ -202,3 +202,25 @@ def algorithmic_bytes_verify(w: Workload, out_bytes: int = 4) -> dict:
     items["fused_total"] = (items["verify_total"] - items["state_read"] + B * w.h_v * hs * p_b
                             + B * w.h_v * hs * 4 + B * 4)
     return items
+
+
+def algorithmic_bytes_replay(w: Workload, out_bytes: int = 4) -> dict:
+    """Bytes of one decode step with commit by replay, in one launch: the cached
+    state read and the committed state written (fp32), the replayed block's
+    inputs (counted whole: the accepted prefix is drawn per step) and the
+    accepted index, the next block's inputs and its outputs.  No node states
+    are persisted and no final state is written."""
+    B, N = w.batch, w.n_nodes
+    qk_b = 2 if w.qkv_bf16 else 4
+    hs = w.d_v * w.d_k
+    block_in = 2 * B * N * w.h_qk * w.d_k * qk_b + B * N * w.h_v * w.d_v * qk_b + 2 * B * N * w.h_v * 4
+    items = {
+        "state_read": B * w.h_v * hs * 4,
+        "replayed_inputs": block_in,
+        "accepted": B * 4,
+        "inputs": block_in,
+        "out": B * N * w.h_v * w.d_v * out_bytes,
+        "state_write": B * w.h_v * hs * 4,
+    }
+    items["total"] = sum(items.values())
+    return items

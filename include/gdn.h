@@ -75,7 +75,8 @@ typedef struct gdn_shape {
     int32_t batch;         /* independent sequences (or sequence x layer units), >= 0 */
     int32_t n_nodes;       /* draft nodes per sequence; tokens per sequence for prefill */
     int32_t h_qk;          /* q/k heads, >= 1 */
-    int32_t h_v;           /* value heads, a multiple of h_qk */
+    int32_t h_v;           /* value heads, a multiple of h_qk; verify and commit by replay need
+                              h_v * d_v * d_k * GDN_MAX_NODES < 2^32 */
     int32_t d_k;           /* key channels: 32, 64 or 128 */
     int32_t d_v;           /* value channels: a multiple of 16, at most 256 */
     int32_t n_slots;       /* rows of `state` when state_slot is given (ignored otherwise) */
@@ -164,6 +165,52 @@ int gdn_verify_tree(const gdn_shape* shape, const int32_t* parent, int32_t n_tre
 int gdn_commit(const gdn_shape* shape, const int32_t* accepted_node, const void* persist,
                const float* final_state, float* state, const int32_t* state_slot,
                int32_t* status, void* stream);
+
+/*
+ * Commit by replay: set the cached state to the accepted node's state by
+ * running the recurrence again over the accepted nodes, from the state the
+ * block was verified from, with the block's retained inputs.  Page "400 tok/s
+ * with Qwen3.5", section "Handling recurrent state" (checkpoint-and-replay: the
+ * state from before the draft block is kept with the projected inputs, and a
+ * replay kernel advances it through the accepted positions only).  With this
+ * commit a verify needs to persist no node states (persist = NULL).
+ *
+ * On entry state[slot(b)] is the state the block was verified from (the
+ * checkpoint); on return it is the fp32 state after node accepted_node[b]
+ * (device array [B]).  The nodes replayed are the node's root path: nodes
+ * 0 .. a of a chain (parent == NULL), or the ancestors of a, root first, of a
+ * tree (parent: HOST array as in gdn_verify_tree, n_trees x N with n_trees = 1
+ * or batch).  The arithmetic per node is the verify's, so the result equals
+ * bit for bit the fp32 node state that gdn_verify_chain / gdn_verify_tree
+ * persist with persist_dtype F32 for the same inputs.  q, k, v, alpha, beta are
+ * the block's inputs, laid out as for verify.  No outputs are written;
+ * shape.out_dtype, persist_dtype and scale are not used.  A node outside
+ * [0, N) or a slot outside [0, n_slots) skips the sequence (its state is left
+ * as it was) and sets *status.
+ */
+int gdn_commit_replay(const gdn_shape* shape, const int32_t* parent, int32_t n_trees,
+                      const int32_t* accepted_node, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, float* state, const int32_t* state_slot,
+                      int32_t* status, void* stream);
+
+/*
+ * One launch for a decode step with commit by replay: replay the previous chain
+ * block's accepted nodes (as gdn_commit_replay with parent = NULL, inputs
+ * q_prev .. beta_prev and accepted_prev), write the result to state[slot(b)],
+ * then verify the next chain (q .. beta) from it, as gdn_verify_chain would
+ * from the updated cache.  Page "400 tok/s with Qwen3.5", section "Handling
+ * recurrent state".  The replayed state never leaves registers between the
+ * two.  persist is usually NULL in this scheme (nothing to persist: the next
+ * step replays); out and final_state are as in gdn_verify_chain, and
+ * final_state may not be `state`.  The previous block has this call's shape.
+ * An accepted node outside [0, N) skips the sequence entirely (state and
+ * outputs untouched) and sets *status to GDN_ERR_NODE.
+ */
+int gdn_replay_verify_chain(const gdn_shape* shape, const int32_t* accepted_prev, const void* q_prev,
+                            const void* k_prev, const void* v_prev, const float* alpha_prev,
+                            const float* beta_prev, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, float* state, const int32_t* state_slot,
+                            void* out, void* persist, float* final_state, int32_t* status, void* stream);
 
 /*
  * Chunked prefill of a prompt: the same recurrence over shape.n_nodes = T

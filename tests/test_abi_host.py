@@ -75,6 +75,7 @@ E = gb.CODES
     (dict(qkv_dtype=7), "GDN_ERR_DTYPE"),
     (dict(persist_dtype=gb.GDN_BF16), "GDN_ERR_DTYPE"),
     (dict(scale=float("nan")), "GDN_ERR_SHAPE"),
+    (dict(h_v=8192, h_qk=16), "GDN_ERR_SHAPE"),  # per-node persist offsets would pass 2^32
 ])
 def test_verify_chain_rejects_bad_shapes(kw, code):
     assert chain(shape(**kw)) == E[code]
@@ -217,3 +218,40 @@ def test_fused_commit_verify_rejects_bad_requests():
     assert f(shape(), acc=FAKE + 2) == E["GDN_ERR_ALIGN"]
     assert f(shape(), fin=FAKE) == E["GDN_ERR_SHAPE"]  # final_state == state
     assert f(shape(d_k=96)) == E["GDN_ERR_SHAPE"]
+
+
+def test_commit_replay_rejects_bad_requests():
+    L = gb.lib()
+
+    def f(sh, parent=None, n_trees=0, acc=FAKE, q=FAKE, st=FAKE):
+        par = np.ascontiguousarray(parent, dtype=np.int32) if parent is not None else None
+        return L.gdn_commit_replay(ctypes.byref(sh), par.ctypes.data if par is not None else None, n_trees, acc,
+                                   q, FAKE, FAKE, FAKE, FAKE, st, None, None, None)
+    assert f(shape(), acc=None) == E["GDN_ERR_NULL"]
+    assert f(shape(), acc=FAKE + 2) == E["GDN_ERR_ALIGN"]
+    assert f(shape(), q=None) == E["GDN_ERR_NULL"]
+    assert f(shape(), st=FAKE + 4) == E["GDN_ERR_ALIGN"]
+    assert f(shape(d_k=96)) == E["GDN_ERR_SHAPE"]
+    assert f(shape(n_nodes=33)) == E["GDN_ERR_SHAPE"]
+    # tree paths: the parent rules of gdn_verify_tree, checked before anything else
+    assert f(shape(n_nodes=3), parent=[0, 0, 1], n_trees=1) == E["GDN_ERR_PARENT"]
+    assert f(shape(n_nodes=3), parent=[-1, 0, 2], n_trees=1) == E["GDN_ERR_PARENT"]
+    assert f(shape(n_nodes=3, batch=2), parent=[-1, 0, 1] * 3, n_trees=3) == E["GDN_ERR_SHAPE"]
+    deep = [-1] + list(range(16))  # 17 nodes on one path
+    assert f(shape(n_nodes=17), parent=deep, n_trees=1) == E["GDN_ERR_PARENT"]
+    assert f(shape(batch=0), acc=None, q=None) == 0
+
+
+def test_replay_verify_rejects_bad_requests():
+    L = gb.lib()
+
+    def f(sh, acc=FAKE, qp=FAKE, ap=FAKE, st=FAKE, fin=None, out=FAKE):
+        return L.gdn_replay_verify_chain(ctypes.byref(sh), acc, qp, FAKE, FAKE, ap, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, st, None, out, None, fin, None, None)
+    assert f(shape(), acc=None) == E["GDN_ERR_NULL"]
+    assert f(shape(), qp=None) == E["GDN_ERR_NULL"]
+    assert f(shape(), qp=FAKE + 8) == E["GDN_ERR_ALIGN"]
+    assert f(shape(), ap=FAKE + 2) == E["GDN_ERR_ALIGN"]
+    assert f(shape(), fin=FAKE) == E["GDN_ERR_SHAPE"]  # final_state == state
+    assert f(shape(h_v=47)) == E["GDN_ERR_SHAPE"]
+    assert f(shape(batch=0), acc=None, qp=None) == 0
