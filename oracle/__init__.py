@@ -22,6 +22,9 @@ Parity status per function (the tests that pin each one are in
            inputs do not reach a node
   chunked  pinned: equals the stepwise chain for every chunk length
   commit   pinned: by its definition (index semantics), exercised in tests
+  conv_commit  pinned: a causal convolution over the committed history and
+           the next inputs equals the convolution over the whole accepted
+           stream (chains and tree paths); index and slot handling
 """
 from __future__ import annotations
 
@@ -190,3 +193,64 @@ def commit(state, nodes, accepted, final=None, state_slot=None):
         src = final[b] if (final is not None and a == N - 1) else nodes[b, a]
         new[s] = src
     return new, bad
+
+
+def conv_commit(history, x, accepted, parent=None, state_slot=None):
+    """Commit of the causal-convolution input history, by definition.
+
+    Page "400 tok/s with Qwen3.5", section "Handling recurrent state": the
+    convolution history is committed to the same boundary as the recurrent
+    state.  A causal convolution of width W reads the current input row and the
+    W - 1 rows before it, so the history a sequence keeps is its last W - 1
+    input rows, oldest first.
+
+    history [slots][W-1][C]; x [B][N][C] (the draft block's inputs);
+    accepted [B]; parent None (a chain: node n follows node n - 1) or [N] /
+    [B][N] (node 0 follows the history).  For sequence b with a = accepted[b],
+    the accepted input stream is the history rows followed by the inputs of
+    the nodes on a's root path, root first; the new history is the last W - 1
+    rows of that stream.  Out-of-range nodes or slots leave the entry as it
+    was.  Returns (new_history, n_rejected).
+    """
+    hist = np.asarray(history)
+    new = np.array(hist, copy=True)
+    B, N = x.shape[0], x.shape[1]
+    keep = hist.shape[1]
+    bad = 0
+    for b in range(B):
+        a = int(accepted[b])
+        s = int(state_slot[b]) if state_slot is not None else b
+        if not (0 <= a < N) or not (0 <= s < hist.shape[0]):
+            bad += 1
+            continue
+        if parent is None:
+            path = list(range(a + 1))
+        else:
+            par = np.asarray(parent)
+            par = par[b] if par.ndim == 2 else par
+            path, n = [], a
+            while n >= 0:
+                path.append(n)
+                n = int(par[n])
+            path.reverse()
+        stream = [hist[s, i] for i in range(keep)] + [x[b, n] for n in path]
+        for i in range(keep):
+            new[s, i] = stream[len(stream) - keep + i]
+    return new, bad
+
+
+def causal_conv(history, x_rows, weight):
+    """The causal depthwise convolution the history serves (for pins only):
+    y_t[c] = sum_j weight[c][j] * u_{t - (W-1) + j}[c] over the stream u =
+    history rows followed by x_rows; one output per x row.  history [W-1][C],
+    x_rows [T][C], weight [C][W]."""
+    hist = np.asarray(history, dtype=np.float64)
+    xs = np.asarray(x_rows, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    W = w.shape[1]
+    u = np.concatenate([hist, xs], axis=0)
+    y = np.zeros_like(xs)
+    for t in range(xs.shape[0]):
+        for j in range(W):
+            y[t] += w[:, j] * u[t + j]
+    return y

@@ -361,3 +361,73 @@ def test_regression_fixture(oracle_mod):
     tr = oracle_mod.tree(i["q"], i["k"], i["v"], i["alpha"], i["beta"], i["state0"], g["parent"])
     assert np.array_equal(tr["out"], np.array(g["tree"]["out"]))
     assert np.array_equal(tr["nodes"], np.array(g["tree"]["nodes"]))
+
+
+# --------------------------------------------------------------------------
+# convolution history commit
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("W", [2, 4, 6])
+def test_conv_commit_continues_the_convolution_of_a_chain(oracle_mod, W):
+    """Convolving the next inputs from the committed history gives the same
+    outputs as convolving the whole accepted stream: the history holds the
+    last W - 1 accepted rows, oldest first."""
+    rng = np.random.default_rng(60 + W)
+    B, N, C = 3, 9, 5
+    hist = rng.standard_normal((B, W - 1, C))
+    x = rng.standard_normal((B, N, C))
+    z = rng.standard_normal((B, 4, C))  # the next inputs
+    w = rng.standard_normal((C, W))
+    acc = np.array([0, W - 3 if W > 2 else 1, N - 1], np.int32)
+    new, bad = oracle_mod.conv_commit(hist, x, acc)
+    assert bad == 0
+    for b in range(B):
+        a = int(acc[b])
+        whole = oracle_mod.causal_conv(hist[b], np.concatenate([x[b, :a + 1], z[b]]), w)
+        cont = oracle_mod.causal_conv(new[b], z[b], w)
+        assert np.allclose(cont, whole[a + 1:], rtol=0, atol=1e-12)
+    # closed forms: a long accepted prefix keeps only draft rows; a short one shifts the history
+    assert np.array_equal(new[2], x[2, N - W + 1:])
+    a0 = int(acc[0])
+    assert np.array_equal(new[0], np.concatenate([hist[0, a0 + 1:], x[0, :a0 + 1]]))
+
+
+def test_conv_commit_follows_the_tree_path(oracle_mod):
+    rng = np.random.default_rng(70)
+    B, N, C, W = 2, 12, 4, 4
+    par = np.array([-1, 0, 0, 1, 1, 2, 3, 3, 5, 8, 9, 6], np.int32)
+    hist = rng.standard_normal((B, W - 1, C))
+    x = rng.standard_normal((B, N, C))
+    z = rng.standard_normal((B, 3, C))
+    w = rng.standard_normal((C, W))
+    for a in range(N):
+        path, n = [], a
+        while n >= 0:
+            path.append(n)
+            n = int(par[n])
+        path = path[::-1]
+        new, bad = oracle_mod.conv_commit(hist, x, np.array([a, a], np.int32), parent=par)
+        assert bad == 0
+        # equals the chain commit of the path's inputs
+        chain_new, _ = oracle_mod.conv_commit(hist, x[:, path], np.array([len(path) - 1] * B, np.int32))
+        assert np.array_equal(new, chain_new)
+        whole = oracle_mod.causal_conv(hist[0], np.concatenate([x[0, path], z[0]]), w)
+        assert np.allclose(oracle_mod.causal_conv(new[0], z[0], w), whole[len(path):], rtol=0, atol=1e-12)
+    # per-sequence parents
+    pars = np.stack([par, np.arange(-1, N - 1, dtype=np.int32)])
+    new, _ = oracle_mod.conv_commit(hist, x, np.array([10, 10], np.int32), parent=pars)
+    assert np.array_equal(new[1], x[1, 8:11])
+    assert np.array_equal(new[0], x[0, [8, 9, 10]])  # root path 0, 2, 5, 8, 9, 10
+
+
+def test_conv_commit_slots_and_rejections(oracle_mod):
+    rng = np.random.default_rng(71)
+    B, N, C, W = 3, 5, 2, 3
+    hist = rng.standard_normal((5, W - 1, C))
+    x = rng.standard_normal((B, N, C))
+    slots = np.array([4, 0, 2], np.int32)
+    new, bad = oracle_mod.conv_commit(hist, x, np.array([3, 5, 0], np.int32), state_slot=slots)
+    assert bad == 1
+    assert np.array_equal(new[4], x[0, 2:4])
+    assert np.array_equal(new[0], hist[0])  # node 5 out of range: untouched
+    assert np.array_equal(new[2], np.concatenate([hist[2, 1:], x[2, :1]]))
+    assert np.array_equal(new[1], hist[1]) and np.array_equal(new[3], hist[3])
