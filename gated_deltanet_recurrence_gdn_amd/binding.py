@@ -20,6 +20,7 @@ GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
 GDN_MAX_NODES = 32
 GDN_MAX_TREE_DEPTH = 16
 GDN_PREFILL_CHUNK = 64
+GDN_MAX_CONV_WIDTH = 8
 
 STATUS = {
     0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE", -4: "GDN_ERR_ALIGN",
@@ -33,6 +34,11 @@ class GdnError(RuntimeError):
     def __init__(self, code: int, what: str):
         self.code = code
         super().__init__(f"{what}: {STATUS.get(code, code)} ({gdn_status_string(code)})")
+
+
+class GdnConvShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_nodes", ctypes.c_int32), ("channels", ctypes.c_int32),
+                ("width", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class GdnShape(ctypes.Structure):
@@ -51,6 +57,7 @@ _SIGS = {
     "gdn_commit": [ctypes.POINTER(GdnShape)] + [_vp] * 7,
     "gdn_commit_replay": [ctypes.POINTER(GdnShape), _vp, ctypes.c_int32] + [_vp] * 10,
     "gdn_replay_verify_chain": [ctypes.POINTER(GdnShape)] + [_vp] * 18,
+    "gdn_conv_commit": [ctypes.POINTER(GdnConvShape), _vp, ctypes.c_int32] + [_vp] * 6,
     "gdn_status_string": [ctypes.c_int],
     "gdn_tree_walk": [_vp, ctypes.c_int32, _vp, _vp],
     "gdn_prefill_workspace_bytes": [ctypes.POINTER(GdnShape)],
@@ -226,6 +233,26 @@ def gdn_replay_verify_chain(accepted_prev, q_prev, k_prev, v_prev, alpha_prev, b
                                        _dev_ptr(final_state, "final_state"), _dev_ptr(status, "status"),
                                        _stream(stream))
     _check(rc, "gdn_replay_verify_chain")
+
+
+def gdn_conv_commit(accepted_node, x, conv_state, *, parent=None, state_slot=None, status=None,
+                    stream=None) -> None:
+    """Commit the convolution history: conv_state [slots][W-1][C] <- the last
+    W-1 rows of (history, inputs x [B][N][C] along the accepted node's root
+    path); chain when ``parent`` is None, else a host array [N] or [B][N]."""
+    B, N, C = x.shape
+    if conv_state.dtype != x.dtype:
+        raise TypeError("conv_state and x must have one dtype")
+    sh = GdnConvShape(B, N, C, conv_state.shape[1] + 1, conv_state.shape[0], _dtype_code(x))
+    par, n_trees = None, 0
+    if parent is not None:
+        par = _host_parent(parent)
+        n_trees = 1 if par.ndim == 1 else par.shape[0]
+    rc = lib().gdn_conv_commit(ctypes.byref(sh), par.ctypes.data if par is not None else None, n_trees,
+                               _dev_ptr(accepted_node, "accepted_node"), _dev_ptr(x, "x"),
+                               _dev_ptr(conv_state, "conv_state"), _dev_ptr(state_slot, "state_slot"),
+                               _dev_ptr(status, "status"), _stream(stream))
+    _check(rc, "gdn_conv_commit")
 
 
 def _prefill_shape(q, v, state, out, scale) -> GdnShape:

@@ -387,6 +387,57 @@ int gdn_commit(const gdn_shape* shape, const int32_t* accepted_node, const void*
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+int gdn_conv_commit(const gdn_conv_shape* shape, const int32_t* parent, int32_t n_trees,
+                    const int32_t* accepted_node, const void* x, void* conv_state,
+                    const int32_t* state_slot, int32_t* status, void* stream) {
+    if (shape == nullptr) return GDN_ERR_NULL;
+    const gdn_conv_shape* sh = shape;
+    if (sh->batch < 0 || sh->n_nodes < 1 || sh->n_nodes > GDN_MAX_NODES) return GDN_ERR_SHAPE;
+    if (sh->width < 2 || sh->width > GDN_MAX_CONV_WIDTH || sh->channels < 1) return GDN_ERR_SHAPE;
+    if (state_slot != nullptr && sh->n_slots < 1) return GDN_ERR_SHAPE;
+    if (!valid_dtype(sh->dtype)) return GDN_ERR_DTYPE;
+    const long long row = (long long)sh->channels * (sh->dtype == GDN_F32 ? 4 : 2);
+    if (row % 16 != 0 || row / 16 > 0x7fffffffLL) return GDN_ERR_SHAPE;
+    const int B = sh->batch, N = sh->n_nodes;
+    int rc;
+    if (parent != nullptr) {
+        if (!(n_trees == 1 || (n_trees == B && B > 0))) return GDN_ERR_SHAPE;
+        int slots = 0;
+        uint16_t walk[GDN_MAX_NODES];
+        for (int t = 0; t < n_trees; ++t)
+            if ((rc = plan_tree(parent + (size_t)t * N, N, walk, &slots)) != GDN_OK) return rc;
+    }
+    if (B == 0) return GDN_OK;
+    if (!accepted_node || !x || !conv_state) return GDN_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(conv_state, 16)) return GDN_ERR_ALIGN;
+    if (!aligned(accepted_node, 4) || !aligned(state_slot, 4)) return GDN_ERR_ALIGN;
+    ConvArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = static_cast<const unsigned char*>(x);
+    a.hist = static_cast<unsigned char*>(conv_state);
+    a.accepted = accepted_node; a.state_slot = state_slot; a.status = status;
+    a.n_nodes = N; a.keep = sh->width - 1; a.pieces = (int32_t)(row / 16); a.n_slots = sh->n_slots;
+    a.wg_per_seq = (a.pieces + 255) / 256;
+    a.chain = parent == nullptr;
+    a.per_seq_tree = n_trees > 1;
+    TreeParents tp;
+    std::memset(&tp, 0, sizeof(tp));
+    const int span = a.per_seq_tree ? kTreesPerLaunch : B;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int s0 = 0; s0 < B; s0 += span) {
+        const int ns = (B - s0 < span) ? (B - s0) : span;
+        if (parent != nullptr)
+            for (int t = 0; t < (a.per_seq_tree ? ns : 1); ++t)
+                for (int n = 0; n < N; ++n)
+                    tp.p[t][n] = (int8_t)parent[(size_t)(a.per_seq_tree ? s0 + t : 0) * N + n];
+        a.seq0 = s0;
+        const long long grid = (long long)ns * a.wg_per_seq;
+        if (grid > 0x7fffffffLL) return GDN_ERR_SHAPE;
+        if (launch_conv_commit(a, &tp, (int)grid, st) != hipSuccess) return GDN_ERR_HIP;
+    }
+    return GDN_OK;
+}
+
 namespace {
 int check_prefill(const gdn_shape* sh) {
     if (sh == nullptr) return GDN_ERR_NULL;

@@ -105,6 +105,24 @@ struct CommitArgs {
     int32_t n_slots;
 };
 
+// Commit of the causal-convolution history (conv_commit.hip).
+constexpr int kMaxConvKeep = GDN_MAX_CONV_WIDTH - 1;
+struct ConvArgs {
+    const unsigned char* x;      // [B][N][C] block inputs
+    unsigned char* hist;         // [slots][keep][C] history, updated in place
+    const int32_t* accepted;
+    const int32_t* state_slot;
+    int32_t* status;
+    int32_t n_nodes;
+    int32_t keep;         // W - 1 history rows
+    int32_t pieces;       // 16-byte pieces per row (C * element size / 16)
+    int32_t wg_per_seq;   // workgroups per sequence
+    int32_t n_slots;
+    int32_t seq0;         // first sequence of this launch
+    int32_t chain;        // 1: parents are n - 1
+    int32_t per_seq_tree; // 0: tree 0 for every sequence; 1: tree b - seq0
+};
+
 struct PrefillArgs {
     void* workspace; // see prefill_workspace_bytes
     const void* q;
@@ -150,5 +168,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int d_k, int out_dtype, hipStrea
 
 hipError_t launch_commit(const CommitArgs& a, bool persist_f16, int grid, int block,
                          hipStream_t stream);
+
+hipError_t launch_conv_commit(const ConvArgs& a, const TreeParents* parents, int grid, hipStream_t stream);
 
 }  // namespace gdn

@@ -54,6 +54,7 @@ extern "C" {
 #define GDN_MAX_NODES 32      /* draft nodes per verify call (a 22-node tree plus margin) */
 #define GDN_MAX_TREE_DEPTH 16 /* nodes on a root-to-leaf path, root included */
 #define GDN_PREFILL_CHUNK 64  /* tokens per chunk of gdn_prefill_chunked */
+#define GDN_MAX_CONV_WIDTH 8  /* taps of the causal convolution whose history gdn_conv_commit keeps */
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -211,6 +212,36 @@ int gdn_replay_verify_chain(const gdn_shape* shape, const int32_t* accepted_prev
                             const float* beta_prev, const void* q, const void* k, const void* v,
                             const float* alpha, const float* beta, float* state, const int32_t* state_slot,
                             void* out, void* persist, float* final_state, int32_t* status, void* stream);
+
+/* Shape of a causal-convolution history commit. */
+typedef struct gdn_conv_shape {
+    int32_t batch;    /* sequences, >= 0 */
+    int32_t n_nodes;  /* draft nodes per sequence, 1 .. GDN_MAX_NODES */
+    int32_t channels; /* C, input channels of the convolution; C * element size a multiple of 16 bytes */
+    int32_t width;    /* W, taps of the convolution, 2 .. GDN_MAX_CONV_WIDTH; the history keeps W - 1 rows */
+    int32_t n_slots;  /* rows of conv_state when state_slot is given (ignored otherwise) */
+    int32_t dtype;    /* element type of x and conv_state: GDN_F32, GDN_BF16 or GDN_F16 (bytes are copied) */
+} gdn_conv_shape;
+
+/*
+ * Commit the causal-convolution input history to the accepted boundary.
+ * Page "400 tok/s with Qwen3.5", section "Handling recurrent state": the
+ * convolution history is committed to the same boundary as the recurrent
+ * state.  A causal convolution of width W reads the current input row and the
+ * W - 1 before it, so each sequence keeps its last W - 1 input rows:
+ *     conv_state [n_slots][W-1][C]   oldest row first (16-byte aligned)
+ *     x          [B][N][C]           the draft block's convolution inputs
+ * On return conv_state[slot(b)] holds the last W - 1 rows of the accepted
+ * stream: the previous history rows followed by the inputs of the nodes on
+ * accepted_node[b]'s root path, root first (nodes 0 .. a of a chain when
+ * parent == NULL; parent as in gdn_verify_tree otherwise, n_trees = 1 or
+ * batch).  Rows are copied bit for bit.  accepted_node is a DEVICE array [B];
+ * a node outside [0, N) or a slot outside [0, n_slots) skips the sequence and
+ * sets *status.
+ */
+int gdn_conv_commit(const gdn_conv_shape* shape, const int32_t* parent, int32_t n_trees,
+                    const int32_t* accepted_node, const void* x, void* conv_state,
+                    const int32_t* state_slot, int32_t* status, void* stream);
 
 /*
  * Chunked prefill of a prompt: the same recurrence over shape.n_nodes = T

@@ -255,3 +255,30 @@ def test_replay_verify_rejects_bad_requests():
     assert f(shape(), fin=FAKE) == E["GDN_ERR_SHAPE"]  # final_state == state
     assert f(shape(h_v=47)) == E["GDN_ERR_SHAPE"]
     assert f(shape(batch=0), acc=None, qp=None) == 0
+
+
+def test_conv_commit_rejects_bad_requests():
+    L = gb.lib()
+
+    def f(batch=2, n_nodes=16, channels=64, width=4, n_slots=2, dtype=gb.GDN_BF16, parent=None, n_trees=0,
+          acc=FAKE, x=FAKE, hist=FAKE, slot=None):
+        sh = gb.GdnConvShape(batch, n_nodes, channels, width, n_slots, dtype)
+        par = np.ascontiguousarray(parent, dtype=np.int32) if parent is not None else None
+        return L.gdn_conv_commit(ctypes.byref(sh), par.ctypes.data if par is not None else None, n_trees, acc, x,
+                                 hist, slot, None, None)
+    assert L.gdn_conv_commit(None, None, 0, FAKE, FAKE, FAKE, None, None, None) == E["GDN_ERR_NULL"]
+    assert f(width=1) == E["GDN_ERR_SHAPE"]
+    assert f(width=9) == E["GDN_ERR_SHAPE"]
+    assert f(channels=0) == E["GDN_ERR_SHAPE"]
+    assert f(channels=12) == E["GDN_ERR_SHAPE"]          # 24 bytes a row: not whole 16-byte pieces
+    assert f(n_nodes=0) == E["GDN_ERR_SHAPE"]
+    assert f(n_nodes=33) == E["GDN_ERR_SHAPE"]
+    assert f(dtype=5) == E["GDN_ERR_DTYPE"]
+    assert f(acc=None) == E["GDN_ERR_NULL"]
+    assert f(x=FAKE + 8) == E["GDN_ERR_ALIGN"]
+    assert f(hist=FAKE + 4) == E["GDN_ERR_ALIGN"]
+    assert f(acc=FAKE + 2) == E["GDN_ERR_ALIGN"]
+    assert f(slot=FAKE, n_slots=0) == E["GDN_ERR_SHAPE"]
+    assert f(n_nodes=3, parent=[-1, 0, 0], n_trees=3) == E["GDN_ERR_SHAPE"]
+    assert f(n_nodes=3, parent=[-1, 1, 0], n_trees=1) == E["GDN_ERR_PARENT"]
+    assert f(batch=0, acc=None, x=None, hist=None) == 0
