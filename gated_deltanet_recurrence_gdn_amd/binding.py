@@ -58,6 +58,7 @@ _SIGS = {
     "gdn_commit_replay": [ctypes.POINTER(GdnShape), _vp, ctypes.c_int32] + [_vp] * 10,
     "gdn_replay_verify_chain": [ctypes.POINTER(GdnShape)] + [_vp] * 18,
     "gdn_conv_commit": [ctypes.POINTER(GdnConvShape), _vp, ctypes.c_int32] + [_vp] * 6,
+    "gdn_commit_index": [_vp, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp],
     "gdn_status_string": [ctypes.c_int],
     "gdn_tree_walk": [_vp, ctypes.c_int32, _vp, _vp],
     "gdn_prefill_workspace_bytes": [ctypes.POINTER(GdnShape)],
@@ -233,6 +234,16 @@ def gdn_replay_verify_chain(accepted_prev, q_prev, k_prev, v_prev, alpha_prev, b
                                        _dev_ptr(final_state, "final_state"), _dev_ptr(status, "status"),
                                        _stream(stream))
     _check(rc, "gdn_replay_verify_chain")
+
+
+def gdn_commit_index(accepted_node, state_slot, n_nodes: int, draft_row0: int, n_slots: int, *, status=None,
+                     stream=None) -> None:
+    """Index-table commit: state_slot[b] <- draft_row0 + b * n_nodes + accepted_node[b] (device arrays)."""
+    B = state_slot.shape[0]
+    rc = lib().gdn_commit_index(_dev_ptr(accepted_node, "accepted_node"), _dev_ptr(state_slot, "state_slot"), B,
+                                int(n_nodes), int(draft_row0), int(n_slots), _dev_ptr(status, "status"),
+                                _stream(stream))
+    _check(rc, "gdn_commit_index")
 
 
 def gdn_conv_commit(accepted_node, x, conv_state, *, parent=None, state_slot=None, status=None,

@@ -387,6 +387,19 @@ int gdn_commit(const gdn_shape* shape, const int32_t* accepted_node, const void*
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+int gdn_commit_index(const int32_t* accepted_node, int32_t* state_slot, int32_t batch, int32_t n_nodes,
+                     int32_t draft_row0, int32_t n_slots, int32_t* status, void* stream) {
+    if (batch < 0 || n_nodes < 1 || n_nodes > GDN_MAX_NODES || draft_row0 < 0 || n_slots < 1) return GDN_ERR_SHAPE;
+    if ((long long)draft_row0 + (long long)batch * n_nodes > n_slots) return GDN_ERR_SHAPE;
+    if (batch == 0) return GDN_OK;
+    if (accepted_node == nullptr || state_slot == nullptr) return GDN_ERR_NULL;
+    if (!aligned(accepted_node, 4) || !aligned(state_slot, 4) || !aligned(status, 4)) return GDN_ERR_ALIGN;
+    IndexCommitArgs a;
+    a.accepted = accepted_node; a.state_slot = state_slot; a.status = status; a.batch = batch;
+    a.n_nodes = n_nodes; a.draft_row0 = draft_row0; a.n_slots = n_slots;
+    return launch_commit_index(a, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 int gdn_conv_commit(const gdn_conv_shape* shape, const int32_t* parent, int32_t n_trees,
                     const int32_t* accepted_node, const void* x, void* conv_state,
                     const int32_t* state_slot, int32_t* status, void* stream) {

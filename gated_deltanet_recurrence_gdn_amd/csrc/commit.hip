@@ -61,7 +61,32 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a) {
     store_stream<NT>(x1, reinterpret_cast<f32x4*>(dst + 4));
 }
 
+// Index-table commit: one thread per sequence writes the row of its accepted
+// node into the index table (page "LightSeek's TokenSpeed Hits 580 Tokens per
+// Second on Qwen3.5's 400B Model", section "How they actually got there":
+// move pointers, not data).
+__global__ __launch_bounds__(256) void commit_index_kernel(const IndexCommitArgs a) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= a.batch) return;
+    const int acc = a.accepted[b];
+    const long long row = (long long)a.draft_row0 + (long long)b * a.n_nodes + acc;
+    if (acc < 0 || acc >= a.n_nodes) {
+        if (a.status != nullptr) a.status[0] = GDN_ERR_NODE;
+        return;
+    }
+    if (row >= a.n_slots) {
+        if (a.status != nullptr) a.status[0] = GDN_ERR_SLOT;
+        return;
+    }
+    a.state_slot[b] = (int32_t)row;
+}
+
 }  // namespace
+
+hipError_t launch_commit_index(const IndexCommitArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(commit_index_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_commit(const CommitArgs& a, bool persist_f16, int grid, int block, hipStream_t stream) {
     // non-temporal stores for small commits (shorter drain), plain ones for large (faster streaming)

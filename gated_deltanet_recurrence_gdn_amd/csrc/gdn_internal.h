@@ -105,6 +105,17 @@ struct CommitArgs {
     int32_t n_slots;
 };
 
+struct IndexCommitArgs {
+    const int32_t* accepted;
+    int32_t* state_slot;
+    int32_t* status;
+    int32_t batch;
+    int32_t n_nodes;
+    int32_t draft_row0;
+    int32_t n_slots;
+};
+hipError_t launch_commit_index(const IndexCommitArgs& a, hipStream_t stream);
+
 // Commit of the causal-convolution history (conv_commit.hip).
 constexpr int kMaxConvKeep = GDN_MAX_CONV_WIDTH - 1;
 struct ConvArgs {

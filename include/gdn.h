@@ -213,6 +213,30 @@ int gdn_replay_verify_chain(const gdn_shape* shape, const int32_t* accepted_prev
                             const float* alpha, const float* beta, float* state, const int32_t* state_slot,
                             void* out, void* persist, float* final_state, int32_t* status, void* stream);
 
+/*
+ * Index-table commit: commit the accepted node by pointing the sequence's
+ * index-table entry at the row that already holds its state, instead of
+ * copying the state.  Page "LightSeek's TokenSpeed Hits 580 Tokens per Second
+ * on Qwen3.5's 400B Model", section "How they actually got there" (move
+ * pointers, not data: the state buffer gains a draft region, and an index
+ * table records which row holds each sequence's state).
+ *
+ * Protocol.  `state` is a pool [n_slots][h_v][d_v][d_k] fp32 whose rows
+ * draft_row0 .. draft_row0 + B N - 1 form the draft region; state_slot [B] is
+ * the index table.  gdn_verify_chain / gdn_verify_tree are called with this
+ * state_slot and with persist = the pool's row draft_row0 (persist_dtype F32),
+ * so node n of sequence b is persisted, exactly, in row draft_row0 + b N + n.
+ * A verify may persist over the row it reads its state from: every element is
+ * read before it is written.  gdn_commit_index then sets, on the device,
+ *     state_slot[b] <- draft_row0 + b N + accepted_node[b]
+ * and the next verify reads the accepted node's exact fp32 state from there.
+ * accepted_node and state_slot are DEVICE arrays [B]; draft_row0 + B N must
+ * not exceed n_slots.  An accepted node outside [0, n_nodes) leaves the entry
+ * as it was and sets *status to GDN_ERR_NODE.
+ */
+int gdn_commit_index(const int32_t* accepted_node, int32_t* state_slot, int32_t batch, int32_t n_nodes,
+                     int32_t draft_row0, int32_t n_slots, int32_t* status, void* stream);
+
 /* Shape of a causal-convolution history commit. */
 typedef struct gdn_conv_shape {
     int32_t batch;    /* sequences, >= 0 */

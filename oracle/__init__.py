@@ -25,6 +25,9 @@ Parity status per function (the tests that pin each one are in
   conv_commit  pinned: a causal convolution over the committed history and
            the next inputs equals the convolution over the whole accepted
            stream (chains and tree paths); index and slot handling
+  commit_index  pinned by its definition (index semantics) and by the
+           property that the pool row it selects holds the accepted node's
+           state, checked against the chain in tests
 """
 from __future__ import annotations
 
@@ -254,3 +257,28 @@ def causal_conv(history, x_rows, weight):
         for j in range(W):
             y[t] += w[:, j] * u[t + j]
     return y
+
+
+def commit_index(state_slot, accepted, draft_row0, n_nodes, n_slots):
+    """Index-table commit, by definition.
+
+    Page "LightSeek's TokenSpeed Hits 580 Tokens per Second on Qwen3.5's 400B
+    Model", section "How they actually got there" (move pointers, not data):
+    the state buffer is extended with a draft region that holds every node's
+    state, and an index table records which row holds a sequence's state;
+    the commit writes one index instead of copying a state.  With node n of
+    sequence b persisted in row draft_row0 + b * n_nodes + n, the commit sets
+    state_slot[b] to the accepted node's row.  An accepted node outside
+    [0, n_nodes), or a row outside [0, n_slots), leaves the entry as it was.
+    Returns (new_state_slot, n_rejected).
+    """
+    new = np.array(state_slot, dtype=np.int64, copy=True)
+    bad = 0
+    for b in range(len(new)):
+        a = int(accepted[b])
+        row = draft_row0 + b * n_nodes + a
+        if not (0 <= a < n_nodes) or not (0 <= row < n_slots):
+            bad += 1
+            continue
+        new[b] = row
+    return new.astype(np.int32), bad

@@ -282,3 +282,18 @@ def test_conv_commit_rejects_bad_requests():
     assert f(n_nodes=3, parent=[-1, 0, 0], n_trees=3) == E["GDN_ERR_SHAPE"]
     assert f(n_nodes=3, parent=[-1, 1, 0], n_trees=1) == E["GDN_ERR_PARENT"]
     assert f(batch=0, acc=None, x=None, hist=None) == 0
+
+
+def test_commit_index_rejects_bad_requests():
+    L = gb.lib()
+    f = lambda acc=FAKE, slot=FAKE, B=2, N=16, row0=4, n_slots=36, status=None: L.gdn_commit_index(  # noqa: E731
+        acc, slot, B, N, row0, n_slots, status, None)
+    assert f(acc=None) == E["GDN_ERR_NULL"]
+    assert f(slot=None) == E["GDN_ERR_NULL"]
+    assert f(acc=FAKE + 2) == E["GDN_ERR_ALIGN"]
+    assert f(status=FAKE + 1) == E["GDN_ERR_ALIGN"]
+    assert f(N=0) == E["GDN_ERR_SHAPE"]
+    assert f(N=33) == E["GDN_ERR_SHAPE"]
+    assert f(row0=-1) == E["GDN_ERR_SHAPE"]
+    assert f(n_slots=35) == E["GDN_ERR_SHAPE"]  # the draft region passes the pool
+    assert f(B=0, acc=None, slot=None) == 0

@@ -431,3 +431,27 @@ def test_conv_commit_slots_and_rejections(oracle_mod):
     assert np.array_equal(new[0], hist[0])  # node 5 out of range: untouched
     assert np.array_equal(new[2], np.concatenate([hist[2, 1:], x[2, :1]]))
     assert np.array_equal(new[1], hist[1]) and np.array_equal(new[3], hist[3])
+
+
+def test_commit_index_selects_the_accepted_nodes_row(oracle_mod):
+    """With node states persisted in a pool's draft rows (row draft_row0 + b N + n),
+    the committed index points at the row holding the accepted node's state."""
+    rng = np.random.default_rng(80)
+    B, N, Hqk, Hv, dk, dv = 3, 5, 1, 2, 3, 4
+    q, k, v, alpha, beta, S0 = _rand_inputs(80, B=B, N=N, Hqk=Hqk, Hv=Hv, dk=dk, dv=dv)
+    ref = oracle_mod.chain(q, k, v, alpha, beta, S0)
+    draft_row0 = 4
+    n_slots = draft_row0 + B * N
+    pool = rng.standard_normal((n_slots, Hv, dv, dk))
+    pool[draft_row0:] = ref["nodes"].reshape(B * N, Hv, dv, dk)
+    slot = np.array([0, 1, 2], np.int32)
+    acc = np.array([2, N - 1, N], np.int32)  # the last one out of range
+    new, bad = oracle_mod.commit_index(slot, acc, draft_row0, N, n_slots)
+    assert bad == 1 and new[2] == 2
+    for b in range(2):
+        assert np.array_equal(pool[new[b]], ref["nodes"][b, acc[b]])
+    # a row past the pool is rejected too
+    new2, bad2 = oracle_mod.commit_index(slot, np.array([0, 0, 0], np.int32), draft_row0, N, n_slots - 1)
+    assert bad2 == 0
+    new3, bad3 = oracle_mod.commit_index(slot, np.array([0, 0, N - 1], np.int32), draft_row0, N, n_slots - 1)
+    assert bad3 == 1 and new3[2] == 2
