@@ -294,6 +294,8 @@ def secondary(torch, gb, wl, dev, args):
     torch.cuda.empty_cache()
     out["replay_chain"] = bench_replay(torch, gb, wl, dev, args)
     log("replay_chain", out["replay_chain"])
+    out["index_chain"] = bench_index(torch, gb, wl, dev, args)
+    log("index_chain", out["index_chain"])
     out["prefill"] = bench_prefill(torch, gb, wl, dev, max(5, args.steps // 25))
     log("prefill", out["prefill"])
     return out
@@ -326,6 +328,42 @@ def bench_replay(torch, gb, wl, dev, args):
            "achieved_gbs": led["total"] / (km * 1e-3) / 1e9,
            "hbm_frac": led["total"] / (km * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "kernel": "replay_verify_chain_kernel<128,1,no persist,f32 out,nt>"}
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_index(torch, gb, wl, dev, args):
+    """Decode step with the index-table commit at the chain workload: verify
+    through the index table with fp32 node states persisted into the pool's
+    draft rows, then gdn_commit_index (two launches, no state copy).  Each
+    buffer set is one pool: the canonical row and 16 draft rows."""
+    w = wl.WORKLOADS["chain"]
+    led = wl.algorithmic_bytes_index(w)
+    N = w.n_nodes
+    sets = []
+    for i in range(args.sets):
+        s = dev_set(torch, wl.make_inputs(w, seed=wl.WORKLOAD_SEEDS[w.name] + 7919 * i), dev)
+        pool = torch.empty(1 + N, w.h_v, w.d_v, w.d_k, device=dev)
+        pool[0] = s["state0"][0]
+        s["pool"], s["persist"] = pool, pool[1:].view(1, N, w.h_v, w.d_v, w.d_k)
+        s["slot"] = torch.zeros(1, dtype=torch.int32, device=dev)
+        s["out"] = torch.empty(1, N, w.h_v, w.d_v, device=dev)
+        sets.append(s)
+
+    def verify(s):
+        gb.gdn_verify_chain(s["q"], s["k"], s["v"], s["alpha"], s["beta"], s["pool"], out=s["out"],
+                            persist=s["persist"], state_slot=s["slot"])
+
+    def step(s):
+        verify(s)
+        gb.gdn_commit_index(s["accepted"], s["slot"], N, 1, 1 + N)
+
+    sm, km = time_steps(torch, sets, step, verify, args.steps, args.warmup)
+    res = {"tokens_per_s_per_layer": w.batch * N / (sm * 1e-3), "ms_per_step": sm, "verify_us": km * 1e3,
+           "step_bytes": led["total"], "step_gbs": led["total"] / (sm * 1e-3) / 1e9,
+           "verify_gbs": (led["total"] - led["commit"]) / (km * 1e-3) / 1e9,
+           "kernel": "verify_chain_kernel<128,1,8,fp32 persist,f32 out,nt> + commit_index_kernel"}
     del sets
     torch.cuda.empty_cache()
     return res

@@ -63,6 +63,9 @@ _SIGS = {
     "gdn_tree_walk": [_vp, ctypes.c_int32, _vp, _vp],
     "gdn_prefill_workspace_bytes": [ctypes.POINTER(GdnShape)],
     "gdn_prefill_chunked": [ctypes.POINTER(GdnShape)] + [_vp] * 9 + [ctypes.c_size_t, _vp, _vp],
+    "gdn_prefill_varlen_workspace_bytes": [ctypes.POINTER(GdnShape), _vp],
+    "gdn_prefill_boundary_states": [_vp, ctypes.c_int32, ctypes.c_int32],
+    "gdn_prefill_varlen": [ctypes.POINTER(GdnShape)] + [_vp] * 10 + [ctypes.c_int32, _vp, ctypes.c_size_t, _vp, _vp],
 }
 
 
@@ -78,7 +81,9 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = {"gdn_status_string": ctypes.c_char_p,
-                          "gdn_prefill_workspace_bytes": ctypes.c_size_t}.get(name, ctypes.c_int)
+                          "gdn_prefill_workspace_bytes": ctypes.c_size_t,
+                          "gdn_prefill_varlen_workspace_bytes": ctypes.c_size_t,
+                          "gdn_prefill_boundary_states": ctypes.c_int64}.get(name, ctypes.c_int)
         _lib = L
     return _lib
 
@@ -296,3 +301,36 @@ def gdn_prefill_chunked(q, k, v, alpha, beta, state, out, *, state_slot=None, st
                                    _dev_ptr(workspace, "workspace"), ws_bytes, _dev_ptr(status, "status"),
                                    _stream(stream))
     _check(rc, "gdn_prefill_chunked")
+
+
+def _host_cu(cu_seqlens) -> np.ndarray:
+    if isinstance(cu_seqlens, torch.Tensor):
+        cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    return np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+
+
+def gdn_prefill_boundary_states(cu_seqlens, state_interval: int) -> int:
+    cu = _host_cu(cu_seqlens)
+    return int(lib().gdn_prefill_boundary_states(cu.ctypes.data, cu.size - 1, int(state_interval)))
+
+
+def gdn_prefill_varlen(cu_seqlens, q, k, v, alpha, beta, state, out, *, chunk_states=None, state_interval: int = 1,
+                       state_slot=None, status=None, workspace=None, scale: float = 1.0, stream=None) -> None:
+    """Varlen prefill of sequences packed along the token dimension (q [total][h_qk][d_k], ...);
+    ``cu_seqlens`` is a host array [B + 1]; see include/gdn.h."""
+    cu = _host_cu(cu_seqlens)
+    total, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    sh = GdnShape(cu.size - 1, total, Hqk, Hv, dk, dv, state.shape[0], _dtype_code(q), _dtype_code(out), GDN_F16,
+                  float(scale))
+    if workspace is None:
+        need = int(lib().gdn_prefill_varlen_workspace_bytes(ctypes.byref(sh), cu.ctypes.data))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib().gdn_prefill_varlen(ctypes.byref(sh), cu.ctypes.data, _dev_ptr(q, "q"), _dev_ptr(k, "k"),
+                                  _dev_ptr(v, "v"), _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                  _dev_ptr(state, "state"), _dev_ptr(state_slot, "state_slot"), _dev_ptr(out, "out"),
+                                  _dev_ptr(chunk_states, "chunk_states"), int(state_interval),
+                                  _dev_ptr(workspace, "workspace"), ws_bytes, _dev_ptr(status, "status"),
+                                  _stream(stream))
+    _check(rc, "gdn_prefill_varlen")

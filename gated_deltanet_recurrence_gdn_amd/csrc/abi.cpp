@@ -467,7 +467,8 @@ int check_prefill(const gdn_shape* sh) {
 
 size_t gdn_prefill_workspace_bytes(const gdn_shape* shape) {
     if (check_prefill(shape) != GDN_OK || shape->batch == 0 || shape->n_nodes == 0) return 0;
-    return prefill_workspace_bytes(shape->batch, shape->n_nodes, shape->h_qk, shape->h_v, shape->d_k);
+    const long long units = (long long)shape->batch * ((shape->n_nodes + GDN_PREFILL_CHUNK - 1) / GDN_PREFILL_CHUNK);
+    return prefill_workspace_bytes(units, shape->h_qk, shape->h_v, shape->d_k);
 }
 
 int gdn_prefill_chunked(const gdn_shape* shape, const void* q, const void* k, const void* v,
@@ -478,11 +479,12 @@ int gdn_prefill_chunked(const gdn_shape* shape, const void* q, const void* k, co
     const gdn_shape* sh = shape;
     if (state_slot != nullptr && sh->n_slots < 1) return GDN_ERR_SHAPE;
     if (sh->batch == 0 || sh->n_nodes == 0) return GDN_OK;
+    if ((long long)sh->batch * sh->n_nodes > 0x7fffffffLL) return GDN_ERR_SHAPE;
     if (!q || !k || !v || !alpha || !beta || !state || !out) return GDN_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return GDN_ERR_ALIGN;
     if (!aligned(alpha, 4) || !aligned(beta, 4) || !aligned(state, 4) || !aligned(state_slot, 4))
         return GDN_ERR_ALIGN;
-    const size_t need = prefill_workspace_bytes(sh->batch, sh->n_nodes, sh->h_qk, sh->h_v, sh->d_k);
+    const size_t need = gdn_prefill_workspace_bytes(sh);
     if (workspace == nullptr || workspace_bytes < need) return GDN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return GDN_ERR_ALIGN;
     PrefillArgs a;
@@ -492,8 +494,105 @@ int gdn_prefill_chunked(const gdn_shape* shape, const void* q, const void* k, co
     a.out = out; a.status = status; a.batch = sh->batch; a.T = sh->n_nodes; a.h_qk = sh->h_qk; a.h_v = sh->h_v;
     a.d_v = sh->d_v; a.group = sh->h_v / sh->h_qk; a.slices = sh->d_v / 32; a.n_slots = sh->n_slots;
     a.qkv_bf16 = sh->qkv_dtype == GDN_BF16; a.scale = sh->scale;
-    hipError_t e = launch_prefill(a, sh->d_k, sh->out_dtype, static_cast<hipStream_t>(stream));
+    a.varlen = 0;
+    a.units = sh->batch * ((sh->n_nodes + GDN_PREFILL_CHUNK - 1) / GDN_PREFILL_CHUNK);
+    PrefillSeqs seqs;
+    std::memset(&seqs, 0, sizeof(seqs));
+    hipError_t e = launch_prefill(a, seqs, sh->d_k, sh->out_dtype, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+namespace {
+// cu_seqlens: batch + 1 nondecreasing offsets from 0 to the total token count.
+int check_cu_seqlens(const int32_t* cu, int batch, int total) {
+    if (cu == nullptr) return GDN_ERR_NULL;
+    if (cu[0] != 0 || cu[batch] != total) return GDN_ERR_SHAPE;
+    for (int b = 0; b < batch; ++b)
+        if (cu[b + 1] < cu[b]) return GDN_ERR_SHAPE;
+    return GDN_OK;
+}
+long long chunks_of(int T) { return (T + GDN_PREFILL_CHUNK - 1) / GDN_PREFILL_CHUNK; }
+}  // namespace
+
+int64_t gdn_prefill_boundary_states(const int32_t* cu_seqlens, int32_t batch, int32_t state_interval) {
+    if (cu_seqlens == nullptr || batch < 0 || state_interval < 1) return -1;
+    if (check_cu_seqlens(cu_seqlens, batch, cu_seqlens[batch]) != GDN_OK) return -1;
+    int64_t n = 0;
+    for (int b = 0; b < batch; ++b)
+        n += (cu_seqlens[b + 1] - cu_seqlens[b]) / ((int64_t)GDN_PREFILL_CHUNK * state_interval);
+    return n;
+}
+
+size_t gdn_prefill_varlen_workspace_bytes(const gdn_shape* shape, const int32_t* cu_seqlens) {
+    if (check_prefill(shape) != GDN_OK || shape->batch == 0) return 0;
+    if (check_cu_seqlens(cu_seqlens, shape->batch, shape->n_nodes) != GDN_OK) return 0;
+    // launches take up to kMaxPrefillSeqs sequences each and reuse the workspace in turn
+    long long most = 0;
+    for (int s0 = 0; s0 < shape->batch; s0 += kMaxPrefillSeqs) {
+        long long units = 0;
+        for (int b = s0; b < shape->batch && b < s0 + kMaxPrefillSeqs; ++b)
+            units += chunks_of(cu_seqlens[b + 1] - cu_seqlens[b]);
+        if (units > most) most = units;
+    }
+    return most == 0 ? 0 : prefill_workspace_bytes(most, shape->h_qk, shape->h_v, shape->d_k);
+}
+
+int gdn_prefill_varlen(const gdn_shape* shape, const int32_t* cu_seqlens, const void* q, const void* k,
+                       const void* v, const float* alpha, const float* beta, float* state,
+                       const int32_t* state_slot, void* out, float* chunk_states, int32_t state_interval,
+                       void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
+    int rc = check_prefill(shape);
+    if (rc != GDN_OK) return rc;
+    const gdn_shape* sh = shape;
+    if (state_slot != nullptr && sh->n_slots < 1) return GDN_ERR_SHAPE;
+    if (sh->batch == 0) return GDN_OK;
+    if ((rc = check_cu_seqlens(cu_seqlens, sh->batch, sh->n_nodes)) != GDN_OK) return rc;
+    if (chunk_states != nullptr && state_interval < 1) return GDN_ERR_SHAPE;
+    if (sh->n_nodes == 0) return GDN_OK;
+    if (!q || !k || !v || !alpha || !beta || !state || !out) return GDN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return GDN_ERR_ALIGN;
+    if (!aligned(alpha, 4) || !aligned(beta, 4) || !aligned(state, 4) || !aligned(state_slot, 4) ||
+        !aligned(chunk_states, 4))
+        return GDN_ERR_ALIGN;
+    const size_t need = gdn_prefill_varlen_workspace_bytes(sh, cu_seqlens);
+    if (workspace == nullptr || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return GDN_ERR_ALIGN;
+    PrefillArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.workspace = workspace;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state = state; a.state_slot = state_slot;
+    a.out = out; a.status = status; a.T = 0; a.h_qk = sh->h_qk; a.h_v = sh->h_v;
+    a.d_v = sh->d_v; a.group = sh->h_v / sh->h_qk; a.slices = sh->d_v / 32; a.n_slots = sh->n_slots;
+    a.qkv_bf16 = sh->qkv_dtype == GDN_BF16; a.scale = sh->scale;
+    a.varlen = 1;
+    a.chunk_states = chunk_states;
+    a.state_interval = chunk_states != nullptr ? state_interval : 1;
+    const long long span = (long long)GDN_PREFILL_CHUNK * a.state_interval;
+    long long cst = 0;
+    for (int s0 = 0; s0 < sh->batch; s0 += kMaxPrefillSeqs) {
+        const int ns = sh->batch - s0 < kMaxPrefillSeqs ? sh->batch - s0 : kMaxPrefillSeqs;
+        PrefillSeqs seqs;
+        std::memset(&seqs, 0, sizeof(seqs));
+        long long units = 0;
+        for (int i = 0; i <= ns; ++i) {
+            seqs.tok0[i] = cu_seqlens[s0 + i];
+            seqs.unit0[i] = (int32_t)units;
+            seqs.cst0[i] = (int32_t)cst;
+            if (i < ns) {
+                const int T = cu_seqlens[s0 + i + 1] - cu_seqlens[s0 + i];
+                units += chunks_of(T);
+                cst += T / span;
+            }
+        }
+        if (units == 0) continue;
+        if (cst > 0x7fffffffLL) return GDN_ERR_SHAPE;
+        a.batch = ns;
+        a.seq0 = s0;
+        a.units = (int32_t)units;
+        hipError_t e = launch_prefill(a, seqs, sh->d_k, sh->out_dtype, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return GDN_ERR_HIP;
+    }
+    return GDN_OK;
 }
 
 }  // extern "C"

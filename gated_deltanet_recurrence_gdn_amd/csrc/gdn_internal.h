@@ -134,6 +134,16 @@ struct ConvArgs {
     int32_t per_seq_tree; // 0: tree 0 for every sequence; 1: tree b - seq0
 };
 
+// Per-sequence tables of a varlen prefill launch (up to kMaxPrefillSeqs
+// sequences): first token, first chunk unit (workspace block) and first
+// emitted boundary state of each sequence, each with one past-the-end entry.
+constexpr int kMaxPrefillSeqs = 64;
+struct PrefillSeqs {
+    int32_t tok0[kMaxPrefillSeqs + 1];
+    int32_t unit0[kMaxPrefillSeqs + 1];
+    int32_t cst0[kMaxPrefillSeqs + 1];
+};
+
 struct PrefillArgs {
     void* workspace; // see prefill_workspace_bytes
     const void* q;
@@ -155,6 +165,12 @@ struct PrefillArgs {
     int32_t n_slots;
     int32_t qkv_bf16;
     float scale;
+    int32_t varlen;         // 0: batch sequences of T tokens; 1: per-sequence tables (PrefillSeqs)
+    int32_t units;          // chunk units (workspace blocks) of this launch
+    float* chunk_states;    // nullable: states at chunk-interval boundaries
+    int32_t state_interval; // chunks between emitted states (>= 1 when chunk_states is set)
+    int32_t seq_states;     // boundary states emitted per sequence (equal-length launches)
+    int32_t seq0;           // first sequence of this launch (index of state_slot and of state rows)
 };
 
 // Verify kernel launch.  d_k selects the instantiation; m_groups is the number
@@ -171,11 +187,12 @@ hipError_t launch_replay(const VerifyArgs& a, const TreeParents* parents, int ki
                          int epl, int persist_mode, int waves_per_wg, size_t lds_bytes, int grid,
                          hipStream_t stream);
 
-// Chunked prefill: a parallel prepare kernel per (sequence, chunk, value head)
-// writes the state-independent chunk operands to the workspace; a scan kernel
-// per (sequence, value head, 32 value columns) then walks the chunks.
-size_t prefill_workspace_bytes(int batch, int T, int h_qk, int h_v, int d_k);
-hipError_t launch_prefill(const PrefillArgs& a, int d_k, int out_dtype, hipStream_t stream);
+// Chunked prefill: a parallel prepare kernel per (chunk unit, q/k head) writes
+// the state-independent chunk operands to the workspace; a scan kernel per
+// (sequence, value head, 32 value columns) then walks the chunks.  `units` is
+// the number of 64-token chunk units of the launch (one workspace block each).
+size_t prefill_workspace_bytes(long long units, int h_qk, int h_v, int d_k);
+hipError_t launch_prefill(const PrefillArgs& a, const PrefillSeqs& seqs, int d_k, int out_dtype, hipStream_t stream);
 
 hipError_t launch_commit(const CommitArgs& a, bool persist_f16, int grid, int block,
                          hipStream_t stream);

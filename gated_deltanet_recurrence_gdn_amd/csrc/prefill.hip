@@ -112,10 +112,11 @@ __device__ __forceinline__ int pair_row(int tile, int c) {
     return 32 * (tile >> 1) + 8 * (c >> 2) + 4 * (tile & 1) + (c & 3);
 }
 
-// Workspace layout (bytes), per sequence b and chunk c:
-//   T', P  [B][nch][h_v][C x C]     f16, T' = T diag(beta)
-//   gates  [B][nch][h_v][3][C]      fp32: gamma_t, beta_t, Gamma_{C,t}
-//   K, Q   [B][nch][h_qk][C x d_k]  f16
+// Workspace layout (bytes), per chunk unit u (a sequence's chunk ck is unit
+// unit0 + ck; units of one launch are numbered sequence after sequence):
+//   T', P  [units][h_v][C x C]     f16, T' = T diag(beta)
+//   gates  [units][h_v][3][C]      fp32: gamma_t, beta_t, Gamma_{C,t}
+//   K, Q   [units][h_qk][C x d_k]  f16
 // The matrices are stored in the scan's operand-fragment order: fragment f
 // (1 KB) holds, for lane l = 16 g + c, the 8 contraction-consecutive values of
 // row pair_row(tile, c) starting at column 32 (block) + 8 g, at f * 1 KB + 16 l.
@@ -125,9 +126,8 @@ __device__ __forceinline__ int pair_row(int tile, int c) {
 struct WsLayout {
     size_t T, P, G, K, Q, total;
 };
-__host__ __device__ inline WsLayout ws_layout(int B, int nch, int h_qk, int h_v, int d_k) {
+__host__ __device__ inline WsLayout ws_layout(size_t units, int h_qk, int h_v, int d_k) {
     WsLayout w;
-    const size_t units = (size_t)B * nch;
     w.T = 0;
     w.P = w.T + units * h_v * kC * kC * 2;
     w.G = w.P + units * h_v * kC * kC * 2;
@@ -135,6 +135,31 @@ __host__ __device__ inline WsLayout ws_layout(int B, int nch, int h_qk, int h_v,
     w.Q = w.K + units * h_qk * (size_t)d_k * kC * 2;
     w.total = w.Q + units * h_qk * (size_t)d_k * kC * 2;
     return w;
+}
+
+// Where sequence b of a launch lives: its first token in the packed token
+// dimension, its tokens, its first chunk unit and chunk count, and the index
+// of its first emitted boundary state.  Equal-length launches compute these;
+// varlen launches read them from the host-built tables.
+struct SeqInfo {
+    int tok0, T, unit0, nch, cst0;
+};
+__device__ __forceinline__ SeqInfo seq_info(const PrefillArgs& a, const PrefillSeqs& t, int b) {
+    SeqInfo q;
+    if (a.varlen) {
+        q.tok0 = t.tok0[b];
+        q.T = t.tok0[b + 1] - q.tok0;
+        q.unit0 = t.unit0[b];
+        q.nch = t.unit0[b + 1] - q.unit0;
+        q.cst0 = t.cst0[b];
+    } else {
+        q.T = a.T;
+        q.nch = (a.T + kC - 1) / kC;
+        q.tok0 = b * a.T;
+        q.unit0 = b * q.nch;
+        q.cst0 = b * a.seq_states;
+    }
+    return q;
 }
 
 // ---------------------------------------------------------------------------
@@ -184,15 +209,15 @@ __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory")
 // One value head's UT transform and output fragments, on one wave.
 template <int DK>
 __device__ __forceinline__ void prepare_head(PrepLds<DK>& L, PrepWave& W, const PrefillArgs& a, unsigned char* wsb,
-                                             const WsLayout& ws, int b, int ck, int nch, int hv) {
+                                             const WsLayout& ws, const SeqInfo& sq, int ck, int hv) {
     const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
     const int t0 = ck * kC;
-    const size_t unit_v = ((size_t)b * nch + ck) * a.h_v + hv;
+    const size_t unit_v = ((size_t)sq.unit0 + ck) * a.h_v + hv;
 
     // gates: lane = token; l2_t by a wave prefix sum of the clamped log2 alpha
     {
-        const bool in = t0 + lane < a.T;
-        const size_t gi = ((size_t)b * a.T + (in ? t0 + lane : a.T - 1)) * a.h_v + hv;
+        const bool in = t0 + lane < sq.T;
+        const size_t gi = ((size_t)sq.tok0 + (in ? t0 + lane : sq.T - 1)) * a.h_v + hv;
         const float al = in ? a.alpha[gi] : 1.f;
         const float bt = in ? a.beta[gi] : 0.f;
         float x = fmaxf(log2_fast(al), kLogFloor * kLog2e);
@@ -315,23 +340,29 @@ __device__ __forceinline__ void prepare_head(PrepLds<DK>& L, PrepWave& W, const 
 }
 
 template <int DK, bool BF16>
-__global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs a, const PrefillSeqs seqs) {
     constexpr int kLdK = DK + 8;
     constexpr int KSD = DK / 32;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     PrepLds<DK>& L = *reinterpret_cast<PrepLds<DK>*>(lds_raw);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nch = (a.T + kC - 1) / kC;
     int blk = xcd_logical_block(blockIdx.x, gridDim.x);
     const int g = blk % a.h_qk;
-    blk /= a.h_qk;
-    const int ck = blk % nch;
-    const int b = blk / nch;
+    const int u = blk / a.h_qk;  // chunk unit
+    int b;
+    if (a.varlen) {
+        b = 0;
+        while (seqs.unit0[b + 1] <= u) ++b;  // the sequence holding unit u (empty ones are skipped)
+    } else {
+        b = u / ((a.T + kC - 1) / kC);
+    }
+    const SeqInfo sq = seq_info(a, seqs, b);
+    const int ck = u - sq.unit0;
     const int t0 = ck * kC;
-    const WsLayout ws = ws_layout(a.batch, nch, a.h_qk, a.h_v, DK);
+    const WsLayout ws = ws_layout(a.units, a.h_qk, a.h_v, DK);
     unsigned char* wsb = static_cast<unsigned char*>(a.workspace);
-    const size_t unit_q = ((size_t)b * nch + ck) * a.h_qk + g;
+    const size_t unit_q = (size_t)u * a.h_qk + g;
 
     // 1. K, Q chunk -> LDS (f16).  All loads are issued first (token index
     //    clamped into the sequence), then converted and stored; rows past T are zero.
@@ -342,8 +373,8 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         for (int n = 0; n < NK; ++n) {
             const int e = tid + 256 * n;
             const int t = e / (DK / 8), d = 8 * (e % (DK / 8));
-            const int tc = t0 + t < a.T ? t0 + t : a.T - 1;
-            const size_t src = (((size_t)b * a.T + tc) * a.h_qk + g) * DK + d;
+            const int tc = t0 + t < sq.T ? t0 + t : sq.T - 1;
+            const size_t src = (((size_t)sq.tok0 + tc) * a.h_qk + g) * DK + d;
             raw_load<BF16>(rk[n], a.k, src);
             raw_load<BF16>(rq[n], a.q, src);
         }
@@ -351,7 +382,7 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         for (int n = 0; n < NK; ++n) {
             const int e = tid + 256 * n;
             const int t = e / (DK / 8), d = 8 * (e % (DK / 8));
-            const bool valid = t0 + t < a.T;
+            const bool valid = t0 + t < sq.T;
             *reinterpret_cast<h8*>(&L.Kf()[t * kLdK + d]) = raw_to_h8<BF16>(rk[n], valid);
             *reinterpret_cast<h8*>(&L.Qf()[t * kLdK + d]) = raw_to_h8<BF16>(rq[n], valid);
         }
@@ -391,7 +422,7 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
 
     // 3. one value head per wave (waves past the head count only help with steps 1-2)
     for (int j = wave; j < a.group; j += 4)
-        prepare_head<DK>(L, L.w(wave), a, wsb, ws, b, ck, nch, g * a.group + j);
+        prepare_head<DK>(L, L.w(wave), a, wsb, ws, sq, ck, g * a.group + j);
 }
 
 // ---------------------------------------------------------------------------
@@ -472,15 +503,16 @@ struct ScanCtx {
     const unsigned char* wsb;
     WsLayout ws;
     int b, h, g, nch, col0, cols;  // the workgroup's first value column and column count
+    int tok0, T, unit0;            // the sequence's first token, tokens and first chunk unit
     __device__ int clamp_ck(int ck) const { return ck < nch ? ck : nch - 1; }
     // the chunk's block of a per-value-head array (per_unit bytes per head and chunk)
     __device__ rsrc_t ws_v(size_t arr, uint32_t per_unit, int ck) const {
-        return make_rsrc(wsb + arr + ((size_t)b * nch * a->h_v + h) * per_unit +
+        return make_rsrc(wsb + arr + ((size_t)unit0 * a->h_v + h) * per_unit +
                              (size_t)(uint32_t)clamp_ck(ck) * (uint32_t)(a->h_v * per_unit),
                          per_unit);
     }
     __device__ rsrc_t ws_q(size_t arr, uint32_t per_unit, int ck) const {
-        return make_rsrc(wsb + arr + ((size_t)b * nch * a->h_qk + g) * per_unit +
+        return make_rsrc(wsb + arr + ((size_t)unit0 * a->h_qk + g) * per_unit +
                              (size_t)(uint32_t)clamp_ck(ck) * (uint32_t)(a->h_qk * per_unit),
                          per_unit);
     }
@@ -488,10 +520,10 @@ struct ScanCtx {
     // tensor, bounded at the sequence's last token
     __device__ rsrc_t rows(const void* base, int esz, int ck) const {
         const int t0 = clamp_ck(ck) * kC;
-        const int n = a->T - t0 < kC ? a->T - t0 : kC;
+        const int n = T - t0 < kC ? T - t0 : kC;
         const size_t row = (size_t)a->h_v * a->d_v;
         return make_rsrc(static_cast<const unsigned char*>(base) +
-                             (((size_t)b * a->T + t0) * row + (size_t)h * a->d_v + col0) * esz,
+                             (((size_t)tok0 + t0) * row + (size_t)h * a->d_v + col0) * esz,
                          (uint32_t)(((size_t)(n - 1) * row + cols) * esz));
     }
 };
@@ -878,7 +910,7 @@ struct ScanLayout {
 // columns): waves 0 .. NSL-1 are the chain waves of the NSL 16-column slices,
 // waves NSL .. 2 NSL - 1 their output waves.
 template <int DK, int OUT, bool BF16, int NSL>
-__global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillArgs a, const PrefillSeqs seqs) {
     using L = ScanLayout<DK, OUT, BF16, NSL>;
     constexpr int NT = DK / 16;
     extern __shared__ __align__(16) unsigned char lds_raw[];
@@ -896,14 +928,19 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
     X.h = blk % a.h_v;
     X.b = blk / a.h_v;
     X.g = X.h / a.group;
-    X.nch = (a.T + kC - 1) / kC;
-    X.ws = ws_layout(a.batch, X.nch, a.h_qk, a.h_v, DK);
+    const SeqInfo sq = seq_info(a, seqs, X.b);
+    if (sq.nch == 0) return;  // an empty sequence: its state stays as it is (uniform over the workgroup)
+    X.nch = sq.nch;
+    X.tok0 = sq.tok0;
+    X.T = sq.T;
+    X.unit0 = sq.unit0;
+    X.ws = ws_layout(a.units, a.h_qk, a.h_v, DK);
     X.cols = 16 * NSL;
     X.col0 = X.cols * grp;
 
-    int s = X.b;
+    int s = a.seq0 + X.b;
     if (a.state_slot != nullptr) {
-        s = a.state_slot[X.b];
+        s = a.state_slot[a.seq0 + X.b];
         if (s < 0 || s >= a.n_slots) {
             if (threadIdx.x == 0 && a.status != nullptr) a.status[0] = GDN_ERR_SLOT;
             return;  // uniform over the workgroup: every wave leaves before any barrier
@@ -935,6 +972,15 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
         const unsigned char* cur = lds_raw + (ck & 1) * L::BLK;
         if (chain) {
             chain_chunk<DK, BF16, NSL>(st, cur, xc, sl);
+            // the state after every state_interval-th full chunk, for prefix caching
+            if (a.chunk_states != nullptr && (ck + 1) % a.state_interval == 0 && (ck + 1) * kC <= X.T) {
+                const size_t m = (size_t)sq.cst0 + (ck + 1) / a.state_interval - 1;
+                float* csp = a.chunk_states + ((m * a.h_v + X.h) * a.d_v + X.col0 + 16 * sl + c) * DK;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) csp[pair_row(t, 4 * lg) + r] = st[t][r];
+            }
         } else {
             if (ck > 0) write_out<DK, OUT>(X, ost, ck - 1, sl);
             unsigned char* nxt = lds_raw + ((ck + 1) & 1) * L::BLK;
@@ -960,7 +1006,7 @@ hipError_t set_lds(K kernel, size_t lds) {
 }
 
 template <int DK, int OUT, bool BF16, int NSL>
-hipError_t launch_scan_nsl(const PrefillArgs& a, hipStream_t st) {
+hipError_t launch_scan_nsl(const PrefillArgs& a, const PrefillSeqs& seqs, hipStream_t st) {
     PrefillArgs s = a;
     s.slices = a.d_v / (16 * NSL);
     const long long grid = (long long)a.batch * a.h_v * s.slices;
@@ -968,7 +1014,7 @@ hipError_t launch_scan_nsl(const PrefillArgs& a, hipStream_t st) {
     const size_t lds = ScanLayout<DK, OUT, BF16, NSL>::BYTES;
     hipError_t e = set_lds(&prefill_scan_kernel<DK, OUT, BF16, NSL>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT, BF16, NSL>), dim3((int)grid), dim3(128 * NSL), lds, st, s);
+    hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT, BF16, NSL>), dim3((int)grid), dim3(128 * NSL), lds, st, s, seqs);
     return hipGetLastError();
 }
 
@@ -976,45 +1022,45 @@ hipError_t launch_scan_nsl(const PrefillArgs& a, hipStream_t st) {
 // operands for 64 columns, two waves per SIMD) the chain waves shared their
 // SIMDs and the scan measured 25% slower.
 template <int DK, int OUT, bool BF16>
-hipError_t launch_scan(const PrefillArgs& a, hipStream_t st) {
-    return launch_scan_nsl<DK, OUT, BF16, 2>(a, st);
+hipError_t launch_scan(const PrefillArgs& a, const PrefillSeqs& seqs, hipStream_t st) {
+    return launch_scan_nsl<DK, OUT, BF16, 2>(a, seqs, st);
 }
 
 template <int DK, bool BF16>
-hipError_t launch_dk(const PrefillArgs& a, int out_dtype, int prep_grid, hipStream_t st) {
+hipError_t launch_dk(const PrefillArgs& a, const PrefillSeqs& seqs, int out_dtype, int prep_grid, hipStream_t st) {
     const size_t lds = PrepLds<DK>::bytes(a.group < 4 ? a.group : 4);
     hipError_t e = set_lds(&prefill_prepare_kernel<DK, BF16>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_prepare_kernel<DK, BF16>), dim3(prep_grid), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((prefill_prepare_kernel<DK, BF16>), dim3(prep_grid), dim3(256), lds, st, a, seqs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     switch (out_dtype) {
-        case GDN_F32: return launch_scan<DK, 0, BF16>(a, st);
-        case GDN_BF16: return launch_scan<DK, 1, BF16>(a, st);
-        case GDN_F16: return launch_scan<DK, 2, BF16>(a, st);
+        case GDN_F32: return launch_scan<DK, 0, BF16>(a, seqs, st);
+        case GDN_BF16: return launch_scan<DK, 1, BF16>(a, seqs, st);
+        case GDN_F16: return launch_scan<DK, 2, BF16>(a, seqs, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int DK>
-hipError_t launch_dk_any(const PrefillArgs& a, int out_dtype, int prep_grid, hipStream_t st) {
-    return a.qkv_bf16 ? launch_dk<DK, true>(a, out_dtype, prep_grid, st) : launch_dk<DK, false>(a, out_dtype, prep_grid, st);
+hipError_t launch_dk_any(const PrefillArgs& a, const PrefillSeqs& seqs, int out_dtype, int prep_grid, hipStream_t st) {
+    return a.qkv_bf16 ? launch_dk<DK, true>(a, seqs, out_dtype, prep_grid, st)
+                      : launch_dk<DK, false>(a, seqs, out_dtype, prep_grid, st);
 }
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int batch, int T, int h_qk, int h_v, int d_k) {
-    const int nch = (T + kC - 1) / kC;
-    return ws_layout(batch, nch, h_qk, h_v, d_k).total;
+size_t prefill_workspace_bytes(long long units, int h_qk, int h_v, int d_k) {
+    return ws_layout((size_t)units, h_qk, h_v, d_k).total;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int d_k, int out_dtype, hipStream_t stream) {
-    const int nch = (a.T + kC - 1) / kC;
-    const long long prep = (long long)a.batch * nch * a.h_qk;
+hipError_t launch_prefill(const PrefillArgs& a, const PrefillSeqs& seqs, int d_k, int out_dtype, hipStream_t stream) {
+    const long long prep = (long long)a.units * a.h_qk;
     if (prep > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (prep == 0) return hipSuccess;
     switch (d_k) {
-        case 32: return launch_dk_any<32>(a, out_dtype, (int)prep, stream);
-        case 64: return launch_dk_any<64>(a, out_dtype, (int)prep, stream);
-        case 128: return launch_dk_any<128>(a, out_dtype, (int)prep, stream);
+        case 32: return launch_dk_any<32>(a, seqs, out_dtype, (int)prep, stream);
+        case 64: return launch_dk_any<64>(a, seqs, out_dtype, (int)prep, stream);
+        case 128: return launch_dk_any<128>(a, seqs, out_dtype, (int)prep, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -224,3 +224,24 @@ def algorithmic_bytes_replay(w: Workload, out_bytes: int = 4) -> dict:
     }
     items["total"] = sum(items.values())
     return items
+
+
+def algorithmic_bytes_index(w: Workload, out_bytes: int = 4) -> dict:
+    """Bytes of one decode step with the index-table commit: the verify reads
+    the state through the index table and persists every node's state in fp32
+    into the pool's draft rows; the commit writes one index per sequence."""
+    B, N = w.batch, w.n_nodes
+    qk_b = 2 if w.qkv_bf16 else 4
+    hs = w.d_v * w.d_k
+    items = {
+        "index_read": B * 4,
+        "state_read": B * w.h_v * hs * 4,
+        "qk": 2 * B * N * w.h_qk * w.d_k * qk_b,
+        "v": B * N * w.h_v * w.d_v * qk_b,
+        "gates": 2 * B * N * w.h_v * 4,
+        "out": B * N * w.h_v * w.d_v * out_bytes,
+        "persist_f32": B * N * w.h_v * hs * 4,
+        "commit": B * 4 + B * 4,
+    }
+    items["total"] = sum(items.values())
+    return items

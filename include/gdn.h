@@ -300,6 +300,38 @@ int gdn_prefill_chunked(const gdn_shape* shape, const void* q, const void* k, co
                         size_t workspace_bytes, int32_t* status, void* stream);
 
 /*
+ * Varlen batched prefill with chunk-boundary states.  The same recurrence
+ * and chunked evaluation as gdn_prefill_chunked, for `batch` sequences of
+ * different lengths packed one after another along the token dimension, in
+ * one call.  Page "LightSeek's TokenSpeed Hits 580 Tokens per Second on
+ * Qwen3.5's 400B Model", section "How they actually got there" (hybrid prefix
+ * caching needs the recurrent state at the exact prefix boundary): the call
+ * can also emit the state at every state_interval-th chunk boundary.
+ *
+ * cu_seqlens is a HOST array [batch + 1]: 0 = cu[0] <= cu[1] <= ... <=
+ * cu[batch] = shape.n_nodes (the total token count); sequence b holds tokens
+ * cu[b] .. cu[b+1]-1 of
+ *     q, k [total][h_qk][d_k],  v [total][h_v][d_v],  alpha, beta [total][h_v],
+ *     out [total][h_v][d_v] (out_dtype, 16-byte aligned),
+ * and state[slot(b)] (initial state in, final state out, in place; an empty
+ * sequence keeps its state).  chunk_states (nullable, fp32, [n][h_v][d_v][d_k])
+ * receives, sequence after sequence, the state after token
+ * 64 state_interval m - 1 of the sequence for m = 1, 2, ... while that token
+ * exists: n = gdn_prefill_boundary_states(cu_seqlens, batch, state_interval)
+ * states in all.  state_interval >= 1 when chunk_states is set.  Sequences
+ * are processed in launches of up to 64; the workspace (at least
+ * gdn_prefill_varlen_workspace_bytes(shape, cu_seqlens) bytes) is reused by
+ * each.  Other arguments, limits and errors as gdn_prefill_chunked; an
+ * invalid cu_seqlens returns GDN_ERR_SHAPE (GDN_ERR_NULL if missing).
+ */
+size_t gdn_prefill_varlen_workspace_bytes(const gdn_shape* shape, const int32_t* cu_seqlens);
+int64_t gdn_prefill_boundary_states(const int32_t* cu_seqlens, int32_t batch, int32_t state_interval);
+int gdn_prefill_varlen(const gdn_shape* shape, const int32_t* cu_seqlens, const void* q, const void* k,
+                       const void* v, const float* alpha, const float* beta, float* state,
+                       const int32_t* state_slot, void* out, float* chunk_states, int32_t state_interval,
+                       void* workspace, size_t workspace_bytes, int32_t* status, void* stream);
+
+/*
  * Plan (and validate) the walk gdn_verify_tree takes through one tree.
  * Host-only; enqueues nothing.  Writes n_nodes steps to `walk` (host,
  * uint16 each): bits 0-4 the node, bit 5 "restore the parent's state from

@@ -297,3 +297,38 @@ def test_commit_index_rejects_bad_requests():
     assert f(row0=-1) == E["GDN_ERR_SHAPE"]
     assert f(n_slots=35) == E["GDN_ERR_SHAPE"]  # the draft region passes the pool
     assert f(B=0, acc=None, slot=None) == 0
+
+
+def test_prefill_varlen_rejects_bad_requests():
+    L = gb.lib()
+    P = dict(batch=3, n_nodes=300, h_qk=16, h_v=48, d_k=128, d_v=128, out_dtype=gb.GDN_F16)
+
+    def f(cu, sh=None, cs=None, interval=1, ws=FAKE, ws_bytes=1 << 30, q=FAKE):
+        c = np.ascontiguousarray(cu, dtype=np.int32) if cu is not None else None
+        return L.gdn_prefill_varlen(ctypes.byref(sh or shape(**P)), c.ctypes.data if c is not None else None, q,
+                                    FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, cs, interval, ws, ws_bytes, None, None)
+    assert f([0, 100, 200, 300], q=None) == E["GDN_ERR_NULL"]
+    assert f(None) == E["GDN_ERR_NULL"]
+    assert f([1, 100, 200, 300]) == E["GDN_ERR_SHAPE"]     # does not start at 0
+    assert f([0, 100, 90, 300]) == E["GDN_ERR_SHAPE"]      # decreasing
+    assert f([0, 100, 200, 299]) == E["GDN_ERR_SHAPE"]     # does not end at the token count
+    assert f([0, 100, 200, 300], cs=FAKE, interval=0) == E["GDN_ERR_SHAPE"]
+    assert f([0, 100, 200, 300], ws=None) == E["GDN_ERR_WORKSPACE"]
+    sh = shape(**P)
+    cu = np.array([0, 100, 200, 300], np.int32)
+    need = L.gdn_prefill_varlen_workspace_bytes(ctypes.byref(sh), cu.ctypes.data)
+    per_unit = 48 * 2 * 64 * 64 * 2 + 48 * 3 * 64 * 4 + 16 * 2 * 128 * 64 * 2
+    assert need == 6 * per_unit                            # 2 + 2 + 2 chunk units
+    assert f(cu, ws_bytes=need - 1) == E["GDN_ERR_WORKSPACE"]
+    assert f([0, 0, 0, 0], sh=shape(**{**P, "n_nodes": 0}), q=None, ws=None) == 0  # no tokens: no-op
+    assert f(None, sh=shape(**{**P, "batch": 0}), q=None, ws=None) == 0
+
+
+def test_prefill_boundary_state_count():
+    L = gb.lib()
+    cu = np.array([0, 64, 64, 200, 1864, 1865], np.int32)
+    assert L.gdn_prefill_boundary_states(cu.ctypes.data, 5, 1) == 1 + 0 + 2 + 26 + 0
+    assert L.gdn_prefill_boundary_states(cu.ctypes.data, 5, 2) == 0 + 0 + 1 + 13 + 0
+    assert L.gdn_prefill_boundary_states(cu.ctypes.data, 5, 0) == -1
+    bad = np.array([0, 10, 5], np.int32)
+    assert L.gdn_prefill_boundary_states(bad.ctypes.data, 2, 1) == -1
