@@ -207,20 +207,35 @@ struct PrepLds {
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 
 // One value head's UT transform and output fragments, on one wave.
+// The gates of token t0 + lane of value head hv (alpha = 1, beta = 0 past the
+// sequence's end: no-op tokens).
+struct Gate {
+    float al, bt;
+};
+__device__ __forceinline__ Gate load_gate(const PrefillArgs& a, const SeqInfo& sq, int t0, int hv) {
+    const int lane = threadIdx.x & 63;
+    const bool in = t0 + lane < sq.T;
+    const size_t gi = ((size_t)sq.tok0 + (in ? t0 + lane : sq.T - 1)) * a.h_v + hv;
+    Gate gt;
+    gt.al = a.alpha[gi];
+    gt.bt = a.beta[gi];
+    if (!in) {
+        gt.al = 1.f;
+        gt.bt = 0.f;
+    }
+    return gt;
+}
+
 template <int DK>
 __device__ __forceinline__ void prepare_head(PrepLds<DK>& L, PrepWave& W, const PrefillArgs& a, unsigned char* wsb,
-                                             const WsLayout& ws, const SeqInfo& sq, int ck, int hv) {
+                                             const WsLayout& ws, const SeqInfo& sq, int ck, int hv, const Gate gt) {
     const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
-    const int t0 = ck * kC;
     const size_t unit_v = ((size_t)sq.unit0 + ck) * a.h_v + hv;
 
     // gates: lane = token; l2_t by a wave prefix sum of the clamped log2 alpha
     {
-        const bool in = t0 + lane < sq.T;
-        const size_t gi = ((size_t)sq.tok0 + (in ? t0 + lane : sq.T - 1)) * a.h_v + hv;
-        const float al = in ? a.alpha[gi] : 1.f;
-        const float bt = in ? a.beta[gi] : 0.f;
-        float x = fmaxf(log2_fast(al), kLogFloor * kLog2e);
+        const float bt = gt.bt;
+        float x = fmaxf(log2_fast(gt.al), kLogFloor * kLog2e);
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(x, off, 64);
@@ -236,18 +251,27 @@ __device__ __forceinline__ void prepare_head(PrepLds<DK>& L, PrepWave& W, const 
     }
     wave_lds_order();
 
-    // A = strict_lower(beta_t Gamma_{t,i} K K^T) on the lower tiles
+    // A = strict_lower(beta_t Gamma_{t,i} K K^T) on the lower tiles; this lane's
+    // row gates (tokens 16 it + 4 lg + r) and column gates (tokens 16 jt + c)
+    // are read once, the row ones four at a time
+    f32x4 lt4[4], bt4[4];
+    float lc[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        lt4[it] = *reinterpret_cast<const f32x4*>(W.ell + 16 * it + 4 * lg);
+        bt4[it] = *reinterpret_cast<const f32x4*>(W.be + 16 * it + 4 * lg);
+        lc[it] = W.ell[16 * it + c];
+    }
 #pragma unroll
     for (int it = 0; it < 4; ++it)
 #pragma unroll
         for (int jt = 0; jt <= it; ++jt) {
             const int i = 16 * jt + c;
-            const float li = W.ell[i];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * it + 4 * lg + r;
                 const float kk = L.KK[tix(it, jt)][(4 * lg + r) * 16 + c];
-                W.A[tix(it, jt)][(4 * lg + r) * 16 + c] = t > i ? W.be[t] * exp2_fast(W.ell[t] - li) * kk : 0.f;
+                W.A[tix(it, jt)][(4 * lg + r) * 16 + c] = t > i ? bt4[it][r] * exp2_fast(lt4[it][r] - lc[jt]) * kk : 0.f;
             }
         }
     wave_lds_order();
@@ -322,13 +346,17 @@ __device__ __forceinline__ void prepare_head(PrepLds<DK>& L, PrepWave& W, const 
             const f32x4 ta = *reinterpret_cast<const f32x4*>(trow), tb = *reinterpret_cast<const f32x4*>(trow + 4);
             const f32x4 qa = *reinterpret_cast<const f32x4*>(qrow), qb = *reinterpret_cast<const f32x4*>(qrow + 4);
             const float lt = W.ell[t];
+            const f32x4 ba = *reinterpret_cast<const f32x4*>(W.be + i0), bb = *reinterpret_cast<const f32x4*>(W.be + i0 + 4);
+            const f32x4 la = *reinterpret_cast<const f32x4*>(W.ell + i0), lb = *reinterpret_cast<const f32x4*>(W.ell + i0 + 4);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = i0 + e;
                 const float tval = e < 4 ? ta[e] : tb[e - 4];
                 const float qval = e < 4 ? qa[e] : qb[e - 4];
-                tv[e] = (_Float16)(i <= t ? tval * W.be[i] : 0.f);
-                pv[e] = (_Float16)(i <= t ? exp2_fast(lt - W.ell[i]) * qval : 0.f);
+                const float bi = e < 4 ? ba[e] : bb[e - 4];
+                const float li = e < 4 ? la[e] : lb[e - 4];
+                tv[e] = (_Float16)(i <= t ? tval * bi : 0.f);
+                pv[e] = (_Float16)(i <= t ? exp2_fast(lt - li) * qval : 0.f);
             }
         } else {
 #pragma unroll
@@ -363,6 +391,9 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
     const WsLayout ws = ws_layout(a.units, a.h_qk, a.h_v, DK);
     unsigned char* wsb = static_cast<unsigned char*>(a.workspace);
     const size_t unit_q = (size_t)u * a.h_qk + g;
+
+    // the gates of this wave's first value head, loaded with K and Q
+    const Gate gate0 = wave < a.group ? load_gate(a, sq, t0, g * a.group + wave) : Gate{1.f, 0.f};
 
     // 1. K, Q chunk -> LDS (f16).  All loads are issued first (token index
     //    clamped into the sequence), then converted and stored; rows past T are zero.
@@ -422,7 +453,8 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
 
     // 3. one value head per wave (waves past the head count only help with steps 1-2)
     for (int j = wave; j < a.group; j += 4)
-        prepare_head<DK>(L, L.w(wave), a, wsb, ws, sq, ck, g * a.group + j);
+        prepare_head<DK>(L, L.w(wave), a, wsb, ws, sq, ck, g * a.group + j,
+                         j == wave ? gate0 : load_gate(a, sq, t0, g * a.group + j));
 }
 
 // ---------------------------------------------------------------------------
