@@ -42,6 +42,48 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Two sums over the same lane groups, step by step: each DPP step of one sum
+// fills the other's data-hazard slot, so neither needs wait states.
+template <int LPR>
+__device__ __forceinline__ void group_sum2(float& x, float& y) {
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16, "group of 4, 8 or 16 lanes");
+    x += dpp_f32<0xB1>(x);
+    y += dpp_f32<0xB1>(y);
+    x += dpp_f32<0x4E>(x);
+    y += dpp_f32<0x4E>(y);
+    if constexpr (LPR >= 8) {
+        x += dpp_f32<0x141>(x);
+        y += dpp_f32<0x141>(y);
+    }
+    if constexpr (LPR >= 16) {
+        x += dpp_f32<0x140>(x);
+        y += dpp_f32<0x140>(y);
+    }
+}
+
+// Makes each of EPL fp32 values an opaque register value (an empty asm that
+// "modifies" them in place, so nothing is copied).  A conversion of such a
+// value to f16 then rounds the given fp32 number, two per v_cvt_pk_f16_f32,
+// instead of the compiler refolding the producing multiply-add into a
+// mixed-precision one (one instruction per element).
+template <int EPL>
+__device__ __forceinline__ void opaque_f32x8(float (&x)[EPL]) {
+#pragma unroll
+    for (int j = 0; j < EPL; j += 8)
+        asm volatile("" : "+v"(x[j]), "+v"(x[j + 1]), "+v"(x[j + 2]), "+v"(x[j + 3]), "+v"(x[j + 4]), "+v"(x[j + 5]),
+                     "+v"(x[j + 6]), "+v"(x[j + 7]));
+}
+
+// Eight fp32 values -> f16, round to nearest even, two per instruction.
+__device__ __forceinline__ f16x8 to_f16x8(float x0, float x1, float x2, float x3, float x4, float x5, float x6,
+                                          float x7) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 a = __builtin_convertvector(f2{x0, x1}, h2), b = __builtin_convertvector(f2{x2, x3}, h2);
+    const h2 c = __builtin_convertvector(f2{x4, x5}, h2), d = __builtin_convertvector(f2{x6, x7}, h2);
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // bf16 <-> fp32.  bf16 widening is exact; narrowing rounds to nearest even.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }

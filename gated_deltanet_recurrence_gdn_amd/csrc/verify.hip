@@ -277,8 +277,13 @@ __device__ __forceinline__ void node_loop(float (&S)[M][EPL], const StageArea<DK
                         pq1 = fmaf(S[m][e + 1], x.q[e + 1], pq1);
                     }
                 }
-                const float sk = group_sum<LPR>(pk0 + pk1);
-                const float sq = OUTS ? group_sum<LPR>(pq0 + pq1) : 0.f;
+                float sk = pk0 + pk1, sq = 0.f;
+                if constexpr (OUTS) {
+                    sq = pq0 + pq1;
+                    group_sum2<LPR>(sk, sq);
+                } else {
+                    sk = group_sum<LPR>(sk);
+                }
                 if (j == 0) {
                     pk = sk;
                     pq = sq;
@@ -291,14 +296,14 @@ __device__ __forceinline__ void node_loop(float (&S)[M][EPL], const StageArea<DK
             const float o = fmaf(sal, pq, sqk * u);   // scale (alpha S q + (q.k) u)
 #pragma unroll
             for (int e = 0; e < EPL; ++e) S[m][e] = fmaf(al, S[m][e], u * x.k[e]);
+            if constexpr (PMODE == 1) opaque_f32x8(S[m]);  // the persisted f16 is this fp32 state rounded
             // persisted states are written once and read later by commit, never by this kernel
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const size_t at = pbase + (uint32_t)node * pstride + (uint32_t)(m * RPG * DK + 8 * LPR * j);
                 if constexpr (PMODE == 1) {
-                    f16x8 hv;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) hv[e] = (_Float16)S[m][8 * j + e];
+                    const float* x = &S[m][8 * j];
+                    const f16x8 hv = to_f16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
                     store_stream<NT>(hv, reinterpret_cast<f16x8*>(static_cast<_Float16*>(a.persist) + at));
                 } else if constexpr (PMODE == 2) {
                     float* dst = static_cast<float*>(a.persist) + at;

@@ -426,3 +426,16 @@ def test_fused_bad_accepted_node_skips_sequence():
     assert int(status.item()) == gb.CODES["GDN_ERR_NODE"]
     assert torch.equal(st[1], t["state0"][1]) and torch.count_nonzero(per[1]) == 0
     assert torch.equal(st[0], per1[0, 2].float()) and torch.equal(st[2], per1[2, 5].float())
+
+
+def test_f16_persist_is_the_fp32_node_state_rounded():
+    """Each persisted f16 node state is the kernel's fp32 node state rounded once
+    to nearest even (bit for bit), for chains and trees."""
+    w, d = small_inputs(151, 2, 16, 2, 6, 128, 128, tree=True)
+    t = dev_inputs(d)
+    _, p16, f16fin = run_chain(t, 16, persist_dtype=torch.float16)
+    _, p32, _ = run_chain(t, 16, persist_dtype=torch.float32)
+    assert torch.equal(p16, p32.to(torch.float16))
+    _, q16 = run_tree(t, d["parent"], 16, persist_dtype=torch.float16)
+    _, q32 = run_tree(t, d["parent"], 16, persist_dtype=torch.float32)
+    assert torch.equal(q16, q32.to(torch.float16))
