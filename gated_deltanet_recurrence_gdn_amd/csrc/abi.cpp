@@ -458,6 +458,7 @@ int check_prefill(const gdn_shape* sh) {
     if (sh->h_qk < 1 || sh->h_v < 1 || sh->h_v % sh->h_qk != 0) return GDN_ERR_SHAPE;
     if (sh->d_k != 32 && sh->d_k != 64 && sh->d_k != 128) return GDN_ERR_SHAPE;
     if (sh->d_v < 32 || sh->d_v > 256 || sh->d_v % 32 != 0) return GDN_ERR_SHAPE;
+    if (sh->h_v / sh->h_qk > 128) return GDN_ERR_UNSUPPORTED;  // the prepare kernel keeps every group's gates in LDS
     if (sh->qkv_dtype != GDN_F32 && sh->qkv_dtype != GDN_BF16) return GDN_ERR_DTYPE;
     if (!valid_dtype(sh->out_dtype)) return GDN_ERR_DTYPE;
     if (!std::isfinite(sh->scale)) return GDN_ERR_SHAPE;

@@ -165,48 +165,48 @@ __device__ __forceinline__ SeqInfo seq_info(const PrefillArgs& a, const PrefillS
 // ---------------------------------------------------------------------------
 // prepare: one (sequence, chunk, q/k head) per workgroup
 // ---------------------------------------------------------------------------
-// K and Q are loaded and K K^T, Q K^T formed once per q/k head (on the matrix
-// cores, four waves); then each of the head's value heads is handled by one
-// wave on its own, with no further barrier: gates, the masked A, the UT
-// transform T = (I + A)^-1 and the T' and P fragments.  Lower 16 x 16 tiles
-// are kept tile-major: tile (it, jt), jt <= it, is tile number
-// it (it + 1) / 2 + jt, element (r, c) at r * 16 + c.
+// K and Q are loaded and K K^T, Q K^T formed once per q/k head on the matrix
+// cores: 20 lower 16 x 16 tiles, five per wave, kept in the registers of the
+// wave that formed them.  Every value head's gates are formed up front, one
+// head per wave.  Then the four waves take the head's value heads one after
+// another, together: each turns its K K^T tiles into tiles of
+// A = strict_lower(beta_t Gamma_{t,i} k_t.k_i) and its Q K^T tiles into tiles of
+// P = Gamma o tril(Q K^T); one wave forms the diagonal 16 x 16 blocks of
+// T = (I + A)^-1 by forward substitution while the others write P's fragments;
+// the off-diagonal blocks follow by distance (three, two, then one block, one
+// per wave, v_mfma_f32_16x16x4_f32); then all four write T' = T diag(beta).
+// Lower tiles are kept tile-major: tile (it, jt), jt <= it, is tile number
+// it (it + 1) / 2 + jt, element (r, c) at r * 16 + c.  The working set of one
+// value head reuses the LDS of the K, Q chunk, so four workgroups fit a CU.
 __device__ __forceinline__ constexpr int tix(int it, int jt) { return it * (it + 1) / 2 + jt; }
+__device__ __forceinline__ constexpr int tile_row(int tx) { return tx < 1 ? 0 : tx < 3 ? 1 : tx < 6 ? 2 : 3; }
 
-// One wave's working set for one value head.  The diagonal tiles of T
-// replace those of A (each is read in full before it is overwritten); the
-// off-diagonal tiles of T have their own slots.
-struct PrepWave {
-    float ell[kC];       // l2_t (base-2 log gates, prefix-summed)
-    float be[kC];        // beta_t
-    float A[10][256];    // strict lower beta Gamma K K^T, lower tiles; diagonal tiles then hold T
-    float To[6][256];    // off-diagonal tiles of T = (I + A)^-1
-    float Y[256];        // scratch tile
+// The working set of one value head.  The diagonal tiles of T replace those
+// of A (each is read in full before it is overwritten); the off-diagonal
+// tiles of T have their own slots.
+struct PrepHead {
+    float A[10][256];  // strict lower beta Gamma K K^T; diagonal tiles then hold T
+    float To[6][256];  // off-diagonal tiles of T = (I + A)^-1
+    float P[10][256];  // Gamma o tril(Q K^T)
+    float Y[4][256];   // per-wave scratch tile of the off-diagonal products
     __device__ float* T(int it, int jt) { return it == jt ? A[tix(it, it)] : To[tix(it, jt) - it]; }
 };
 
+// LDS: the gates of the q/k head's `group` value heads ([group][2][64] fp32:
+// l2_t, beta_t), then the K, Q chunk [token][d_k + 8] (f16), whose bytes the
+// value-head working set takes over once the Gram tiles are formed.
 template <int DK>
 struct PrepLds {
     static constexpr int kLdK = DK + 8;
-    float KK[10][256];  // K K^T, lower tiles
-    float QK[10][256];  // Q K^T, lower tiles
-    // then the K, Q chunk [token][d_k] (f16) for the Gram products, and afterwards
-    // in the same bytes one PrepWave per wave that works on a value head
     static constexpr size_t kIn = 2 * (size_t)kC * kLdK * 2;
-    static size_t bytes(int waves) {
-        const size_t w = (size_t)waves * sizeof(PrepWave);
-        return 2 * 10 * 256 * 4 + (w > kIn ? w : kIn);
-    }
-    __device__ _Float16* Kf() { return reinterpret_cast<_Float16*>(this + 1); }
-    __device__ _Float16* Qf() { return Kf() + kC * kLdK; }
-    __device__ PrepWave& w(int i) { return reinterpret_cast<PrepWave*>(this + 1)[i]; }
+    static constexpr size_t kUnion = kIn > sizeof(PrepHead) ? kIn : sizeof(PrepHead);
+    static size_t bytes(int group) { return (size_t)group * 2 * kC * 4 + kUnion; }
 };
 
 // Orders this wave's LDS accesses for the compiler where lanes exchange data
 // through LDS (the hardware keeps one wave's LDS operations in order).
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 
-// One value head's UT transform and output fragments, on one wave.
 // The gates of token t0 + lane of value head hv (alpha = 1, beta = 0 past the
 // sequence's end: no-op tokens).
 struct Gate {
@@ -226,145 +226,77 @@ __device__ __forceinline__ Gate load_gate(const PrefillArgs& a, const SeqInfo& s
     return gt;
 }
 
-template <int DK>
-__device__ __forceinline__ void prepare_head(PrepLds<DK>& L, PrepWave& W, const PrefillArgs& a, unsigned char* wsb,
-                                             const WsLayout& ws, const SeqInfo& sq, int ck, int hv, const Gate gt) {
+// One value head's gates on one wave (lane = token): l2_t by a prefix sum of
+// the clamped log2 alpha; l2_t and beta_t to LDS, gamma_t, beta_t and
+// Gamma_{C,t} to the workspace.
+__device__ __forceinline__ void head_gates(const Gate gt, float* gl, float* gw) {
+    const int lane = threadIdx.x & 63;
+    float x = fmaxf(log2_fast(gt.al), kLogFloor * kLog2e);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    const float lC = __shfl(x, 63, 64);
+    gl[lane] = x;
+    gl[kC + lane] = gt.bt;
+    gw[lane] = exp2_fast(x);
+    gw[kC + lane] = gt.bt;
+    gw[2 * kC + lane] = exp2_fast(lC - x);
+}
+
+// Fragment f (0 .. 5, the lower-triangular (tile, block) pairs in the scan's
+// order) of T' = T diag(beta) or of P, f16, to the workspace.  Lane (c, lg)
+// writes row pair_row(tile, c), columns 32 blk + 8 lg .. + 8.
+template <bool TPRIME>
+__device__ __forceinline__ void write_frag(PrepHead& W, const float* gl, _Float16* dst, int f) {
     const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
-    const size_t unit_v = ((size_t)sq.unit0 + ck) * a.h_v + hv;
-
-    // gates: lane = token; l2_t by a wave prefix sum of the clamped log2 alpha
-    {
-        const float bt = gt.bt;
-        float x = fmaxf(log2_fast(gt.al), kLogFloor * kLog2e);
+    const int tile = f < 2 ? f : 2 + (f - 2) / 2, blk = f < 2 ? 0 : (f - 2) % 2;
+    const int t = pair_row(tile, c), i0 = 32 * blk + 8 * lg;
+    const int it = t >> 4, jt = i0 >> 4;
+    h8 v;
+    if (jt <= it) {
+        const float* row = (TPRIME ? W.T(it, jt) : W.P[tix(it, jt)]) + (t & 15) * 16 + (i0 & 15);
+        const f32x4 xa = *reinterpret_cast<const f32x4*>(row), xb = *reinterpret_cast<const f32x4*>(row + 4);
+        if constexpr (TPRIME) {
+            const f32x4 ba = *reinterpret_cast<const f32x4*>(gl + kC + i0);
+            const f32x4 bb = *reinterpret_cast<const f32x4*>(gl + kC + i0 + 4);
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
-        }
-        const float lC = __shfl(x, 63, 64);
-        W.ell[lane] = x;
-        W.be[lane] = bt;
-        float* gw = reinterpret_cast<float*>(wsb + ws.G) + unit_v * 3 * kC;
-        gw[lane] = exp2_fast(x);
-        gw[kC + lane] = bt;
-        gw[2 * kC + lane] = exp2_fast(lC - x);
-    }
-    wave_lds_order();
-
-    // A = strict_lower(beta_t Gamma_{t,i} K K^T) on the lower tiles; this lane's
-    // row gates (tokens 16 it + 4 lg + r) and column gates (tokens 16 jt + c)
-    // are read once, the row ones four at a time
-    f32x4 lt4[4], bt4[4];
-    float lc[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        lt4[it] = *reinterpret_cast<const f32x4*>(W.ell + 16 * it + 4 * lg);
-        bt4[it] = *reinterpret_cast<const f32x4*>(W.be + 16 * it + 4 * lg);
-        lc[it] = W.ell[16 * it + c];
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int jt = 0; jt <= it; ++jt) {
-            const int i = 16 * jt + c;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * it + 4 * lg + r;
-                const float kk = L.KK[tix(it, jt)][(4 * lg + r) * 16 + c];
-                W.A[tix(it, jt)][(4 * lg + r) * 16 + c] = t > i ? bt4[it][r] * exp2_fast(lt4[it][r] - lc[jt]) * kk : 0.f;
-            }
-        }
-    wave_lds_order();
-
-    // diagonal 16 x 16 blocks of T by forward substitution: lane = (block, column)
-    {
-        const int bb = lane >> 4, j = lane & 15;
-        const float* Ab = W.A[tix(bb, bb)];
-        float x[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            float arow[16];
-#pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(Ab + t * 16 + 4 * m4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) arow[4 * m4 + e] = v[e];
-            }
-            float sum = (t == j) ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < t; ++m) sum = fmaf(-arow[m], x[m], sum);
-            x[t] = sum;
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) W.T(bb, bb)[t * 16 + j] = x[t];  // after all reads of A_bb
-    }
-    wave_lds_order();
-
-    // off-diagonal blocks by distance: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
-    // (v_mfma_f32_16x16x4_f32: A[i][4 s + lg], B[4 s + lg][c], D rows 4 lg + r)
-#pragma unroll
-    for (int dist = 1; dist < 4; ++dist)
-#pragma unroll
-        for (int jb = 0; jb + dist < 4; ++jb) {
-            const int ib = jb + dist;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = jb; kb < ib; ++kb) {
-                const float* Ab = W.A[tix(ib, kb)];
-                const float* Tb = W.T(kb, jb);
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ab[c * 16 + 4 * s + lg], Tb[(4 * s + lg) * 16 + c], acc,
-                                                               0, 0, 0);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) W.Y[(4 * lg + r) * 16 + c] = acc[r];
-            wave_lds_order();
-            const float* Ti = W.T(ib, ib);
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                x = __builtin_amdgcn_mfma_f32_16x16x4f32(Ti[c * 16 + 4 * s + lg], W.Y[(4 * s + lg) * 16 + c], x, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) W.T(ib, jb)[(4 * lg + r) * 16 + c] = -x[r];
-            wave_lds_order();
-        }
-
-    // T' = T diag(beta) and P = Gamma o tril(Q K^T) -> workspace in fragment
-    // order (the six lower-triangular fragments); zero above the diagonal
-    _Float16* Tw = reinterpret_cast<_Float16*>(wsb + ws.T) + unit_v * kC * kC;
-    _Float16* Pw = reinterpret_cast<_Float16*>(wsb + ws.P) + unit_v * kC * kC;
-#pragma unroll
-    for (int f = 0; f < 6; ++f) {
-        const int tile = f < 2 ? f : 2 + (f - 2) / 2, blk = f < 2 ? 0 : (f - 2) % 2;
-        const int t = pair_row(tile, c), i0 = 32 * blk + 8 * lg;
-        const int it = t >> 4, jt = i0 >> 4;
-        h8 tv, pv;
-        if (jt <= it) {
-            const float* trow = W.T(it, jt) + (t & 15) * 16 + (i0 & 15);
-            const float* qrow = L.QK[tix(it, jt)] + (t & 15) * 16 + (i0 & 15);
-            const f32x4 ta = *reinterpret_cast<const f32x4*>(trow), tb = *reinterpret_cast<const f32x4*>(trow + 4);
-            const f32x4 qa = *reinterpret_cast<const f32x4*>(qrow), qb = *reinterpret_cast<const f32x4*>(qrow + 4);
-            const float lt = W.ell[t];
-            const f32x4 ba = *reinterpret_cast<const f32x4*>(W.be + i0), bb = *reinterpret_cast<const f32x4*>(W.be + i0 + 4);
-            const f32x4 la = *reinterpret_cast<const f32x4*>(W.ell + i0), lb = *reinterpret_cast<const f32x4*>(W.ell + i0 + 4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int i = i0 + e;
-                const float tval = e < 4 ? ta[e] : tb[e - 4];
-                const float qval = e < 4 ? qa[e] : qb[e - 4];
-                const float bi = e < 4 ? ba[e] : bb[e - 4];
-                const float li = e < 4 ? la[e] : lb[e - 4];
-                tv[e] = (_Float16)(i <= t ? tval * bi : 0.f);
-                pv[e] = (_Float16)(i <= t ? exp2_fast(lt - li) * qval : 0.f);
-            }
+            for (int e = 0; e < 8; ++e)
+                v[e] = (_Float16)(i0 + e <= t ? (e < 4 ? xa[e] * ba[e] : xb[e - 4] * bb[e - 4]) : 0.f);
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) tv[e] = pv[e] = (_Float16)0.f;
+            for (int e = 0; e < 8; ++e) v[e] = (_Float16)(e < 4 ? xa[e] : xb[e - 4]);  // zero above the diagonal
         }
-        *reinterpret_cast<h8*>(Tw + (f * 64 + lane) * 8) = tv;
-        *reinterpret_cast<h8*>(Pw + (f * 64 + lane) * 8) = pv;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (_Float16)0.f;
     }
+    *reinterpret_cast<h8*>(dst + (f * 64 + lane) * 8) = v;
+}
+
+// Off-diagonal block (ib, jb) of T on one wave: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+// (v_mfma_f32_16x16x4_f32: A[i][4 s + lg], B[4 s + lg][c], D rows 4 lg + r).
+__device__ __forceinline__ void offdiag_block(PrepHead& W, int ib, int jb, float* Y) {
+    const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = jb; kb < ib; ++kb) {
+        const float* Ab = W.A[tix(ib, kb)];
+        const float* Tb = W.T(kb, jb);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ab[c * 16 + 4 * s + lg], Tb[(4 * s + lg) * 16 + c], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Y[(4 * lg + r) * 16 + c] = acc[r];
+    wave_lds_order();
+    const float* Ti = W.T(ib, ib);
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(Ti[c * 16 + 4 * s + lg], Y[(4 * s + lg) * 16 + c], x, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) W.T(ib, jb)[(4 * lg + r) * 16 + c] = -x[r];
 }
 
 template <int DK, bool BF16>
@@ -372,8 +304,7 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
     constexpr int kLdK = DK + 8;
     constexpr int KSD = DK / 32;
     extern __shared__ __align__(16) unsigned char lds_raw[];
-    PrepLds<DK>& L = *reinterpret_cast<PrepLds<DK>*>(lds_raw);
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int blk = xcd_logical_block(blockIdx.x, gridDim.x);
     const int g = blk % a.h_qk;
@@ -391,6 +322,12 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
     const WsLayout ws = ws_layout(a.units, a.h_qk, a.h_v, DK);
     unsigned char* wsb = static_cast<unsigned char*>(a.workspace);
     const size_t unit_q = (size_t)u * a.h_qk + g;
+    const size_t unit_v0 = (size_t)u * a.h_v + (size_t)g * a.group;  // the first value head's unit block
+    float* gates = reinterpret_cast<float*>(lds_raw);  // [group][2][64]
+    unsigned char* un = lds_raw + (size_t)a.group * 2 * kC * 4;
+    _Float16* Kf = reinterpret_cast<_Float16*>(un);
+    _Float16* Qf = Kf + kC * kLdK;
+    PrepHead& W = *reinterpret_cast<PrepHead*>(un);
 
     // the gates of this wave's first value head, loaded with K and Q
     const Gate gate0 = wave < a.group ? load_gate(a, sq, t0, g * a.group + wave) : Gate{1.f, 0.f};
@@ -414,28 +351,31 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
             const int e = tid + 256 * n;
             const int t = e / (DK / 8), d = 8 * (e % (DK / 8));
             const bool valid = t0 + t < sq.T;
-            *reinterpret_cast<h8*>(&L.Kf()[t * kLdK + d]) = raw_to_h8<BF16>(rk[n], valid);
-            *reinterpret_cast<h8*>(&L.Qf()[t * kLdK + d]) = raw_to_h8<BF16>(rq[n], valid);
+            *reinterpret_cast<h8*>(&Kf[t * kLdK + d]) = raw_to_h8<BF16>(rk[n], valid);
+            *reinterpret_cast<h8*>(&Qf[t * kLdK + d]) = raw_to_h8<BF16>(rq[n], valid);
         }
+    }
+    // every value head's gates, one head per wave at a time
+    for (int j = wave; j < a.group; j += 4) {
+        float* gw = reinterpret_cast<float*>(wsb + ws.G) + (unit_v0 + j) * 3 * kC;
+        head_gates(j == wave ? gate0 : load_gate(a, sq, t0, g * a.group + j), gates + j * 2 * kC, gw);
     }
     __syncthreads();
 
-    // 2. K K^T and Q K^T on the lower 16 x 16 tiles (20 jobs over the four waves);
-    //    K and Q -> workspace in fragment order
+    // 2. K K^T and Q K^T on the lower 16 x 16 tiles (20 jobs over the four waves, job
+    //    wave + 4 jj: matrix job / 10, tile job % 10), kept in registers; K and Q ->
+    //    workspace in fragment order
+    f32x4 gram[5];
 #pragma unroll
     for (int jj = 0; jj < 5; ++jj) {
         const int job = wave + 4 * jj;
         const int mat = job / 10, tx = job % 10;
-        const int it = tx < 1 ? 0 : tx < 3 ? 1 : tx < 6 ? 2 : 3;
-        const int jt = tx - it * (it + 1) / 2;
+        const int it = tile_row(tx), jt = tx - it * (it + 1) / 2;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks)
-            acc = mfma16(frag(mat ? L.Qf() : L.Kf(), kLdK, 16 * it, 32 * ks, lane),
-                         frag(L.Kf(), kLdK, 16 * jt, 32 * ks, lane), acc);
-        float* dst = (mat ? L.QK : L.KK)[tx];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[r];
+            acc = mfma16(frag(mat ? Qf : Kf, kLdK, 16 * it, 32 * ks, lane), frag(Kf, kLdK, 16 * jt, 32 * ks, lane), acc);
+        gram[jj] = acc;
     }
     {
         _Float16* kw = reinterpret_cast<_Float16*>(wsb + ws.K) + unit_q * kC * DK;
@@ -443,18 +383,78 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         constexpr int PIECES = DK * kC / 8;
         for (int e = tid; e < 2 * PIECES; e += 256) {
             const int m = e / PIECES, i = e % PIECES;
-            const int f = i / 64, l = i % 64, c = l & 15, lg = l >> 4;
-            const int row = pair_row(f / KSD, c), col = 32 * (f % KSD) + 8 * lg;
-            const h8 v = *reinterpret_cast<const h8*>(&(m == 0 ? L.Kf() : L.Qf())[row * kLdK + col]);
+            const int f = i / 64, l = i % 64, cc = l & 15, gg = l >> 4;
+            const int row = pair_row(f / KSD, cc), col = 32 * (f % KSD) + 8 * gg;
+            const h8 v = *reinterpret_cast<const h8*>(&(m == 0 ? Kf : Qf)[row * kLdK + col]);
             *reinterpret_cast<h8*>((m == 0 ? kw : qw) + 8 * i) = v;
         }
     }
-    __syncthreads();  // K, Q are dead: the per-wave working sets overwrite them
+    __syncthreads();  // K, Q are dead: the value-head working set takes their bytes
 
-    // 3. one value head per wave (waves past the head count only help with steps 1-2)
-    for (int j = wave; j < a.group; j += 4)
-        prepare_head<DK>(L, L.w(wave), a, wsb, ws, sq, ck, g * a.group + j,
-                         j == wave ? gate0 : load_gate(a, sq, t0, g * a.group + j));
+    // 3. the value heads one after another, all four waves on each
+    for (int j = 0; j < a.group; ++j) {
+        const float* gl = gates + j * 2 * kC;  // l2_t [64], beta_t [64]
+        const size_t unit_v = unit_v0 + j;
+        // A and P tiles from this wave's Gram tiles
+#pragma unroll
+        for (int jj = 0; jj < 5; ++jj) {
+            const int job = wave + 4 * jj;
+            const int mat = job / 10, tx = job % 10;
+            const int it = tile_row(tx), jt = tx - it * (it + 1) / 2;
+            const f32x4 lt = *reinterpret_cast<const f32x4*>(gl + 16 * it + 4 * lg);
+            const f32x4 bt = *reinterpret_cast<const f32x4*>(gl + kC + 16 * it + 4 * lg);
+            const float li = gl[16 * jt + c];
+            const int i = 16 * jt + c;
+            float* dst = mat ? W.P[tx] : W.A[tx];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * it + 4 * lg + r;
+                const float e2 = exp2_fast(lt[r] - li);
+                dst[(4 * lg + r) * 16 + c] = mat ? (i <= t ? e2 * gram[jj][r] : 0.f) : (i < t ? bt[r] * e2 * gram[jj][r] : 0.f);
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // diagonal 16 x 16 blocks of T by forward substitution: lane = (block, column)
+            const int bb = lane >> 4, jc = lane & 15;
+            const float* Ab = W.A[tix(bb, bb)];
+            float x[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                float arow[16];
+#pragma unroll
+                for (int m4 = 0; m4 < 4; ++m4) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(Ab + t * 16 + 4 * m4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) arow[4 * m4 + e] = v[e];
+                }
+                float sum = (t == jc) ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < t; ++m) sum = fmaf(-arow[m], x[m], sum);
+                x[t] = sum;
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) W.T(bb, bb)[t * 16 + jc] = x[t];  // after all reads of A_bb
+        } else {
+            // meanwhile the P fragments (two per wave)
+            _Float16* Pw = reinterpret_cast<_Float16*>(wsb + ws.P) + unit_v * kC * kC;
+            write_frag<false>(W, gl, Pw, 2 * (wave - 1));
+            write_frag<false>(W, gl, Pw, 2 * (wave - 1) + 1);
+        }
+        __syncthreads();
+        // off-diagonal blocks by distance, one block per wave
+        if (wave < 3) offdiag_block(W, wave + 1, wave, W.Y[wave]);
+        __syncthreads();
+        if (wave < 2) offdiag_block(W, wave + 2, wave, W.Y[wave]);
+        __syncthreads();
+        if (wave == 0) offdiag_block(W, 3, 0, W.Y[0]);
+        __syncthreads();
+        // T' = T diag(beta) fragments
+        _Float16* Tw = reinterpret_cast<_Float16*>(wsb + ws.T) + unit_v * kC * kC;
+        write_frag<true>(W, gl, Tw, wave);
+        if (wave < 2) write_frag<true>(W, gl, Tw, wave + 4);
+        __syncthreads();  // the next value head overwrites A and P
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1060,7 +1060,7 @@ hipError_t launch_scan(const PrefillArgs& a, const PrefillSeqs& seqs, hipStream_
 
 template <int DK, bool BF16>
 hipError_t launch_dk(const PrefillArgs& a, const PrefillSeqs& seqs, int out_dtype, int prep_grid, hipStream_t st) {
-    const size_t lds = PrepLds<DK>::bytes(a.group < 4 ? a.group : 4);
+    const size_t lds = PrepLds<DK>::bytes(a.group);
     hipError_t e = set_lds(&prefill_prepare_kernel<DK, BF16>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_prepare_kernel<DK, BF16>), dim3(prep_grid), dim3(256), lds, st, a, seqs);

@@ -281,7 +281,8 @@ int gdn_conv_commit(const gdn_conv_shape* shape, const int32_t* parent, int32_t 
  * or BF16), 16-byte aligned.  state[slot(b)] holds the initial state on entry and the state
  * after token T-1 on return (updated in place).  A zero alpha resets the state
  * up to a factor e^-80 (the log-gate is clamped at -80).  d_k must be 32, 64 or
- * 128 and d_v a multiple of 32.  persist_dtype is ignored.  T = 0 or batch = 0
+ * 128, d_v a multiple of 32 and h_v / h_qk at most 128 (else GDN_ERR_UNSUPPORTED).
+ * persist_dtype is ignored.  T = 0 or batch = 0
  * is a no-op.
  *
  * `workspace` is caller-owned device memory of at least
