@@ -176,19 +176,23 @@ __device__ __forceinline__ SeqInfo seq_info(const PrefillArgs& a, const PrefillS
 // the off-diagonal blocks follow by distance (three, two, then one block, one
 // per wave, v_mfma_f32_16x16x4_f32); then all four write T' = T diag(beta).
 // Lower tiles are kept tile-major: tile (it, jt), jt <= it, is tile number
-// it (it + 1) / 2 + jt, element (r, c) at r * 16 + c.  The working set of one
-// value head reuses the LDS of the K, Q chunk, so four workgroups fit a CU.
+// it (it + 1) / 2 + jt, element (r, c) at r * kTS + c: rows padded to 20 floats
+// (16-byte aligned), so the column reads of the matrix-core operands and the
+// row reads of the output fragments fall on different banks.  The working set
+// of one value head reuses the LDS of the K, Q chunk; four workgroups fit a CU.
 __device__ __forceinline__ constexpr int tix(int it, int jt) { return it * (it + 1) / 2 + jt; }
+constexpr int kTS = 20;           // row stride of a 16 x 16 fp32 tile in LDS (floats)
+constexpr int kTile = 16 * kTS;   // floats per tile
 __device__ __forceinline__ constexpr int tile_row(int tx) { return tx < 1 ? 0 : tx < 3 ? 1 : tx < 6 ? 2 : 3; }
 
 // The working set of one value head.  The diagonal tiles of T replace those
 // of A (each is read in full before it is overwritten); the off-diagonal
 // tiles of T have their own slots.
 struct PrepHead {
-    float A[10][256];  // strict lower beta Gamma K K^T; diagonal tiles then hold T
-    float To[6][256];  // off-diagonal tiles of T = (I + A)^-1
-    float P[10][256];  // Gamma o tril(Q K^T)
-    float Y[4][256];   // per-wave scratch tile of the off-diagonal products
+    float A[10][kTile];  // strict lower beta Gamma K K^T; diagonal tiles then hold T
+    float To[6][kTile];  // off-diagonal tiles of T = (I + A)^-1
+    float P[10][kTile];  // Gamma o tril(Q K^T)
+    float Y[4][kTile];   // per-wave scratch tile of the off-diagonal products
     __device__ float* T(int it, int jt) { return it == jt ? A[tix(it, it)] : To[tix(it, jt) - it]; }
 };
 
@@ -256,7 +260,7 @@ __device__ __forceinline__ void write_frag(PrepHead& W, const float* gl, _Float1
     const int it = t >> 4, jt = i0 >> 4;
     h8 v;
     if (jt <= it) {
-        const float* row = (TPRIME ? W.T(it, jt) : W.P[tix(it, jt)]) + (t & 15) * 16 + (i0 & 15);
+        const float* row = (TPRIME ? W.T(it, jt) : W.P[tix(it, jt)]) + (t & 15) * kTS + (i0 & 15);
         const f32x4 xa = *reinterpret_cast<const f32x4*>(row), xb = *reinterpret_cast<const f32x4*>(row + 4);
         if constexpr (TPRIME) {
             const f32x4 ba = *reinterpret_cast<const f32x4*>(gl + kC + i0);
@@ -285,18 +289,18 @@ __device__ __forceinline__ void offdiag_block(PrepHead& W, int ib, int jb, float
         const float* Tb = W.T(kb, jb);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ab[c * 16 + 4 * s + lg], Tb[(4 * s + lg) * 16 + c], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ab[c * kTS + 4 * s + lg], Tb[(4 * s + lg) * kTS + c], acc, 0, 0, 0);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Y[(4 * lg + r) * 16 + c] = acc[r];
+    for (int r = 0; r < 4; ++r) Y[(4 * lg + r) * kTS + c] = acc[r];
     wave_lds_order();
     const float* Ti = W.T(ib, ib);
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        x = __builtin_amdgcn_mfma_f32_16x16x4f32(Ti[c * 16 + 4 * s + lg], Y[(4 * s + lg) * 16 + c], x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(Ti[c * kTS + 4 * s + lg], Y[(4 * s + lg) * kTS + c], x, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) W.T(ib, jb)[(4 * lg + r) * 16 + c] = -x[r];
+    for (int r = 0; r < 4; ++r) W.T(ib, jb)[(4 * lg + r) * kTS + c] = -x[r];
 }
 
 template <int DK, bool BF16>
@@ -410,7 +414,7 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * it + 4 * lg + r;
                 const float e2 = exp2_fast(lt[r] - li);
-                dst[(4 * lg + r) * 16 + c] = mat ? (i <= t ? e2 * gram[jj][r] : 0.f) : (i < t ? bt[r] * e2 * gram[jj][r] : 0.f);
+                dst[(4 * lg + r) * kTS + c] = mat ? (i <= t ? e2 * gram[jj][r] : 0.f) : (i < t ? bt[r] * e2 * gram[jj][r] : 0.f);
             }
         }
         __syncthreads();
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
                 float arow[16];
 #pragma unroll
                 for (int m4 = 0; m4 < 4; ++m4) {
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(Ab + t * 16 + 4 * m4);
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(Ab + t * kTS + 4 * m4);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) arow[4 * m4 + e] = v[e];
                 }
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
                 x[t] = sum;
             }
 #pragma unroll
-            for (int t = 0; t < 16; ++t) W.T(bb, bb)[t * 16 + jc] = x[t];  // after all reads of A_bb
+            for (int t = 0; t < 16; ++t) W.T(bb, bb)[t * kTS + jc] = x[t];  // after all reads of A_bb
         } else {
             // meanwhile the P fragments (two per wave)
             _Float16* Pw = reinterpret_cast<_Float16*>(wsb + ws.P) + unit_v * kC * kC;
