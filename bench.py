@@ -298,6 +298,8 @@ def secondary(torch, gb, wl, dev, args):
     log("index_chain", out["index_chain"])
     out["prefill"] = bench_prefill(torch, gb, wl, dev, max(5, args.steps // 25))
     log("prefill", out["prefill"])
+    out["prefill_varlen"] = bench_prefill_varlen(torch, gb, wl, dev, max(3, args.steps // 100))
+    log("prefill_varlen", out["prefill_varlen"])
     return out
 
 
@@ -413,6 +415,51 @@ def bench_prefill(torch, gb, wl, dev, reps):
     return {"ms": ms, "tokens_per_s": w.batch * w.n_nodes / (ms * 1e-3), "algorithmic_gflop": fl / 1e9,
             "tflops": fl / (ms * 1e-3) / 1e12, "mfma_frac_f16_peak": fl / (ms * 1e-3) / 2.5e15,
             "out_dtype": "f16"}
+
+
+def bench_prefill_varlen(torch, gb, wl, dev, reps, n_seq=8):
+    """Supplementary batched point: n_seq prompts of the prefill workload's
+    shape (4096 tokens each) in one gdn_prefill_varlen call, boundary states
+    every 26 chunks (1664 tokens); the graded prefill number is batch 1."""
+    w = wl.WORKLOADS["prefill"]
+    d = wl.make_inputs(w)
+    t = dev_set(torch, d, dev)
+    T = w.n_nodes
+    q, k, v = (t[n][0].repeat(n_seq, 1, 1) for n in ("q", "k", "v"))
+    alpha, beta = (t[n][0].repeat(n_seq, 1) for n in ("alpha", "beta"))
+    st0 = t["state0"].repeat(n_seq, 1, 1, 1)
+    st = st0.clone()
+    out = torch.empty(n_seq * T, w.h_v, w.d_v, device=dev, dtype=torch.float16)
+    cu = np.arange(0, (n_seq + 1) * T, T, dtype=np.int32)
+    ncs = gb.gdn_prefill_boundary_states(cu, 26)
+    cs = torch.empty(ncs, w.h_v, w.d_v, w.d_k, device=dev)
+    ws = torch.empty(gb.gdn_prefill_varlen_workspace_bytes(cu, q, v, st, out), dtype=torch.uint8, device=dev)
+
+    def run():
+        st.copy_(st0)
+        gb.gdn_prefill_varlen(cu, q, k, v, alpha, beta, st, out, chunk_states=cs, state_interval=26, workspace=ws)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        st.copy_(st0)
+    t1.record()
+    torch.cuda.synchronize()
+    copy_ms = t0.elapsed_time(t1) / reps
+    t0.record()
+    for _ in range(reps):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps - copy_ms
+    fl = prefill_flops(w) * n_seq
+    return {"sequences": n_seq, "tokens": n_seq * T, "ms": ms, "tokens_per_s": n_seq * T / (ms * 1e-3),
+            "tflops": fl / (ms * 1e-3) / 1e12, "mfma_frac_f16_peak": fl / (ms * 1e-3) / 2.5e15,
+            "boundary_states": ncs, "out_dtype": "f16"}
 
 
 def cpu_baseline(wl, w, seconds):

@@ -314,6 +314,15 @@ def gdn_prefill_boundary_states(cu_seqlens, state_interval: int) -> int:
     return int(lib().gdn_prefill_boundary_states(cu.ctypes.data, cu.size - 1, int(state_interval)))
 
 
+def gdn_prefill_varlen_workspace_bytes(cu_seqlens, q, v, state, out, scale: float = 1.0) -> int:
+    cu = _host_cu(cu_seqlens)
+    total, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    sh = GdnShape(cu.size - 1, total, Hqk, Hv, dk, dv, state.shape[0], _dtype_code(q), _dtype_code(out), GDN_F16,
+                  float(scale))
+    return int(lib().gdn_prefill_varlen_workspace_bytes(ctypes.byref(sh), cu.ctypes.data))
+
+
 def gdn_prefill_varlen(cu_seqlens, q, k, v, alpha, beta, state, out, *, chunk_states=None, state_interval: int = 1,
                        state_slot=None, status=None, workspace=None, scale: float = 1.0, stream=None) -> None:
     """Varlen prefill of sequences packed along the token dimension (q [total][h_qk][d_k], ...);
