@@ -9,6 +9,7 @@ namespace gdn {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Workgroups are handed to the 8 XCDs round-robin (block i -> XCD i % 8), and
 // each XCD has its own L2.  This bijection gives every XCD a contiguous range
@@ -84,15 +85,11 @@ __device__ __forceinline__ f16x8 to_f16x8(float x0, float x1, float x2, float x3
     return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// bf16 <-> fp32.  bf16 widening is exact; narrowing rounds to nearest even.
+// bf16 <-> fp32.  bf16 widening is exact; narrowing is the hardware's
+// v_cvt_pk_bf16_f32 (round to nearest even, NaN stays NaN), with no branch.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Load 8 consecutive elements (bf16 or fp32) as fp32.
 __device__ __forceinline__ void load8_as_f32(const void* base, size_t idx, bool bf16, float (&x)[8]) {

@@ -762,11 +762,12 @@ __device__ __forceinline__ h8 get_h8(const unsigned char* base, int i) {
 template <int DK>
 struct ChainRegs {
     using PL = Plan<DK>;
-    h8 sb[PL::KB];
+    h8 (&sb)[PL::KB];  // the chunk's starting state (f16), replaced by the next chunk's at the end
     f32x4 kh[PL::NP], uu[PL::NP];
     h8 rb[PL::VB], ug[PL::VB];
     h8 fa[PL::A_END];
-    float vx[PL::NP][4];
+    float vx[PL::NP][4];  // V at this lane's rows (fp32 V)
+    u32x2 vr[PL::NP];     // the same, two bf16 per word (bf16 V)
     f32x4 gp[PL::NP], gq[PL::NP];
     float gC;
 };
@@ -778,9 +779,22 @@ __device__ __forceinline__ void extra_read(ChainRegs<DK>& x, const unsigned char
     const float* gam = reinterpret_cast<const float*>(blk + CB::G0);
     if constexpr (E < 16) {
         constexpr int p = E / 4, r = E % 4;
-        const unsigned char* vp = blk + CB::V0 + (pair_row(p, 4 * lg) + r) * CB::VROW + (16 * sl + c) * (BF16 ? 2 : 4);
-        if constexpr (BF16) x.vx[p][r] = bf16_lo(*reinterpret_cast<const uint16_t*>(vp));
-        else x.vx[p][r] = *reinterpret_cast<const float*>(vp);
+        if constexpr (BF16) {
+            // one transposing read per row block: lane 4 e + q of the group addresses row
+            // pair_row(p, 4 lg) + e, columns 4 q .. 4 q + 3 of the slice, so lane c receives
+            // its column c of the block's four rows
+            if constexpr (r == 0) {
+                typedef short s4v __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) s4v lds_s4;
+                const int e = (lane >> 2) & 3, q = lane & 3;
+                const unsigned char* vp = blk + CB::V0 + (pair_row(p, 4 * lg) + e) * CB::VROW + (16 * sl + 4 * q) * 2;
+                // kept raw: widened where R is formed, so no wait for the read here
+                x.vr[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)vp));
+            }
+        } else {
+            const unsigned char* vp = blk + CB::V0 + (pair_row(p, 4 * lg) + r) * CB::VROW + (16 * sl + c) * 4;
+            x.vx[p][r] = *reinterpret_cast<const float*>(vp);
+        }
     } else if constexpr (E < 20) {
         x.gp[E - 16] = *reinterpret_cast<const f32x4*>(gam + pair_row(E - 16, 4 * lg));
     } else if constexpr (E < 24) {
@@ -807,6 +821,15 @@ __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16
         if constexpr (S < PL::NKH)
             extra_reads<DK, BF16, NSL, S * PL::NEXTRA / PL::NKH, (S + 1) * PL::NEXTRA / PL::NKH>(x, blk, sl);
         if constexpr (S == PL::A_U) {
+            if constexpr (BF16) {
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    x.vx[p][0] = bf16_lo(x.vr[p][0]);
+                    x.vx[p][1] = bf16_hi(x.vr[p][0]);
+                    x.vx[p][2] = bf16_lo(x.vr[p][1]);
+                    x.vx[p][3] = bf16_hi(x.vr[p][1]);
+                }
+            }
             // R = V - gamma K H at this lane's rows pair_row(p, 4 lg) + r
 #pragma unroll
             for (int v = 0; v < VB; ++v)
@@ -842,9 +865,13 @@ __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16
         __builtin_amdgcn_sched_barrier(0);
         chain_step<DK, BF16, NSL, S + 1>(x, st, blk, xc, sl);
     } else {
-        // the next chunk's starting state as the products' B operand, for the output wave
+        // the next chunk's starting state as the products' B operand, kept for this wave's
+        // next K H and handed to the output wave
 #pragma unroll
-        for (int u = 0; u < KB; ++u) put_h8(xc + Xchg<DK>::SB, u, pack_h8(st[2 * u], st[2 * u + 1]));
+        for (int u = 0; u < KB; ++u) {
+            x.sb[u] = pack_h8(st[2 * u], st[2 * u + 1]);
+            put_h8(xc + Xchg<DK>::SB, u, x.sb[u]);
+        }
     }
 }
 
@@ -900,13 +927,11 @@ __device__ __forceinline__ void out_step(OutRegs<DK>& x, const unsigned char* bl
 }
 
 template <int DK, bool BF16, int NSL>
-__device__ __forceinline__ void chain_chunk(f32x4 (&st)[DK / 16], const unsigned char* blk, unsigned char* xc,
-                                            int sl) {
+__device__ __forceinline__ void chain_chunk(f32x4 (&st)[DK / 16], h8 (&sb)[DK / 32], const unsigned char* blk,
+                                            unsigned char* xc, int sl) {
     using PL = Plan<DK>;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    ChainRegs<DK> x;
-#pragma unroll
-    for (int u = 0; u < PL::KB; ++u) x.sb[u] = pack_h8(st[2 * u], st[2 * u + 1]);
+    ChainRegs<DK> x{sb};
 #pragma unroll
     for (int p = 0; p < PL::NP; ++p) x.kh[p] = x.uu[p] = z;
     x.fa[0] = chain_operand<DK, 0>(blk);
@@ -987,13 +1012,17 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
     // chain wave: lane (c, g) holds H[d_k][j] = S[j][d_k] for d_k = pair_row(t, 4g + r)
     float* stp = a.state + (((size_t)s * a.h_v + X.h) * a.d_v + X.col0 + 16 * sl + c) * DK;
     f32x4 st[NT];
+    h8 sb[DK / 32];  // st in f16, the B operand of K H and Q H
     if (chain) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) st[t][r] = stp[pair_row(t, 4 * lg) + r];
 #pragma unroll
-        for (int u = 0; u < DK / 32; ++u) put_h8(xc + Xchg<DK>::SB, u, pack_h8(st[2 * u], st[2 * u + 1]));
+        for (int u = 0; u < DK / 32; ++u) {
+            sb[u] = pack_h8(st[2 * u], st[2 * u + 1]);
+            put_h8(xc + Xchg<DK>::SB, u, sb[u]);
+        }
     } else {
         const DmaCtx d0 = dma_ctx<DK, BF16, NSL>(X, 0, lds_raw, sl);
         dma_slots<DK, BF16, NSL, 0, ChunkBlock<DK, BF16, NSL>::NLOAD / NSL>(d0);
@@ -1007,7 +1036,7 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
         __syncthreads();
         const unsigned char* cur = lds_raw + (ck & 1) * L::BLK;
         if (chain) {
-            chain_chunk<DK, BF16, NSL>(st, cur, xc, sl);
+            chain_chunk<DK, BF16, NSL>(st, sb, cur, xc, sl);
             // the state after every state_interval-th full chunk, for prefix caching
             if (a.chunk_states != nullptr && (ck + 1) % a.state_interval == 0 && (ck + 1) * kC <= X.T) {
                 const size_t m = (size_t)sq.cst0 + (ck + 1) / a.state_interval - 1;
