@@ -211,6 +211,16 @@ struct PrepLds {
 // through LDS (the hardware keeps one wave's LDS operations in order).
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 
+// A workgroup barrier for data exchanged through plain LDS stores: waits for
+// this wave's LDS operations only, so its loads (the next chunk's operands)
+// and its global stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // The gates of token t0 + lane of value head hv (alpha = 1, beta = 0 past the
 // sequence's end: no-op tokens).
 struct Gate {
@@ -508,17 +518,19 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-// One chunk's block in LDS.  Fragments (1 KB each): K [p][u], Q [p][u], then
-// T' and P over the six lower-triangular (p, v <= p / 2) pairs (each rounded
-// up to a multiple of NSL fragments); then V rows [64][the workgroup's 16 NSL
-// columns] in the input dtype, then gamma_t and Gamma_{C,t}.  K^T is not stored: the chain
-// wave reads it from the K fragments with transposing LDS reads.
+// One chunk's block in LDS, the chain waves' operands.  Fragments (1 KB each):
+// K [p][u], then T' over the six lower-triangular (p, v <= p / 2) pairs
+// (rounded up to a multiple of NSL fragments); then V rows [64][the
+// workgroup's 16 NSL columns] in the input dtype, then gamma_t and
+// Gamma_{C,t}.  K^T is not stored: the chain wave reads it from the K
+// fragments with transposing LDS reads.  Q and P, which only the output
+// waves read, go to their registers instead (OutOps).
 template <int DK, bool BF16, int NSL>
 struct ChunkBlock {
     static constexpr int NT = DK / 16, KB = DK / 32, NP = kC / 16, VB = kC / 32;
     static constexpr int NTRI = (6 + NSL - 1) / NSL * NSL;
-    static constexpr int K0 = 0, Q0 = K0 + NP * KB, T0 = Q0 + NP * KB, P0 = T0 + NTRI;
-    static constexpr int NFRAG = P0 + NTRI;
+    static constexpr int K0 = 0, T0 = K0 + NP * KB;
+    static constexpr int NFRAG = T0 + NTRI;
     static constexpr int COLS = 16 * NSL;              // value columns of the workgroup
     static constexpr int VROW = COLS * (BF16 ? 2 : 4);  // bytes of one V row
     static constexpr int NVI = kC * VROW / 1024;       // V loads
@@ -528,8 +540,7 @@ struct ChunkBlock {
     // load instructions per chunk, NSL per slot (one per output wave): every
     // boundary between matrices falls on a slot boundary
     static constexpr int NLOAD = NFRAG + NVI + NSL;
-    static_assert(Q0 % NSL == 0 && T0 % NSL == 0 && P0 % NSL == 0 && NFRAG % NSL == 0 && NVI % NSL == 0,
-                  "slot boundaries");
+    static_assert(T0 % NSL == 0 && NFRAG % NSL == 0 && NVI % NSL == 0, "slot boundaries");
 };
 __device__ __forceinline__ constexpr int tri(int p, int v) { return p < 2 ? p : 2 * p - 2 + v; }
 
@@ -571,7 +582,7 @@ struct ScanCtx {
 // for every wave; the wave enters only through per-lane offsets and a uniform
 // LDS base.
 struct DmaCtx {
-    rsrc_t kw, qw, tw, pw, gw, vw;
+    rsrc_t kw, tw, gw, vw;
     uint32_t vf, vv, vg;  // per-lane source offsets of fragment, V and gate loads (this wave's)
     uint32_t vstep;       // source bytes between this wave's consecutive V loads
     unsigned char* dst;   // LDS block + 1 KB sl
@@ -588,9 +599,7 @@ __device__ __forceinline__ DmaCtx dma_ctx(const ScanCtx<DK>& X, int ck, unsigned
     const uint32_t rowb = (uint32_t)(a.h_v * a.d_v * VSZ);
     DmaCtx d;
     d.kw = X.ws_q(X.ws.K, kC * DK * 2, ck);
-    d.qw = X.ws_q(X.ws.Q, kC * DK * 2, ck);
     d.tw = X.ws_v(X.ws.T, kC * kC * 2, ck);
-    d.pw = X.ws_v(X.ws.P, kC * kC * 2, ck);
     d.gw = X.ws_v(X.ws.G, 3 * kC * 4, ck);
     d.vw = X.rows(a.v, VSZ, ck);
     // fragments are stored in load order: lane l of fragment f at f KB + 16 l
@@ -610,8 +619,8 @@ __device__ __forceinline__ void dma_slot(const DmaCtx& d) {
     using CB = ChunkBlock<DK, BF16, NSL>;
     constexpr int i0 = NSL * K;  // this slot's first instruction
     if constexpr (i0 < CB::NFRAG) {
-        constexpr int base = i0 < CB::Q0 ? CB::K0 : i0 < CB::T0 ? CB::Q0 : i0 < CB::P0 ? CB::T0 : CB::P0;
-        const rsrc_t r = i0 < CB::Q0 ? d.kw : i0 < CB::T0 ? d.qw : i0 < CB::P0 ? d.tw : d.pw;
+        constexpr int base = i0 < CB::T0 ? CB::K0 : CB::T0;
+        const rsrc_t r = i0 < CB::T0 ? d.kw : d.tw;
         if constexpr (NSL * 1024 < 4096) {
             // slots pair up inside a matrix and share one LDS base: the instruction offset
             // (the second of a pair) moves the source and the LDS address alike
@@ -735,13 +744,37 @@ __device__ __forceinline__ h8 chain_operand(const unsigned char* blk) {
     else if constexpr (S < PL::A_ST) return frag_at(blk, CB::T0 + tri(tri_p(S - PL::A_U), tri_v(S - PL::A_U)));
     else return kt_frag<DK>(blk, (S - PL::A_ST) % PL::NT, (S - PL::A_ST) / PL::NT);
 }
-// output wave: the A operand fragment of step s
+// The output wave's A operands of one chunk -- Q's fragments in product order,
+// then P's six -- in registers.  Only the output wave reads them, so they come
+// from the workspace straight into its registers, one chunk ahead, instead of
+// through LDS: each register takes the next chunk's fragment right after the
+// product that reads it has been issued.
 template <int DK>
-__device__ __forceinline__ constexpr int frag_b(int s) {
+struct OutOps {
+    h8 f[Plan<DK>::B_END];
+};
+struct OutSrc {
+    rsrc_t q, p;  // the chunk's Q (per q/k head) and P (per value head) in the workspace
+};
+template <int DK>
+__device__ __forceinline__ OutSrc out_src(const ScanCtx<DK>& X, int ck) {
+    return {X.ws_q(X.ws.Q, kC * DK * 2, ck), X.ws_v(X.ws.P, kC * kC * 2, ck)};
+}
+template <int DK, int S>
+__device__ __forceinline__ h8 load_out_op(const OutSrc& r) {
     using PL = Plan<DK>;
-    using CB = ChunkBlock<DK, true, 2>;
-    if (s < PL::B_PU) return CB::Q0 + (s % PL::NP) * PL::KB + s / PL::NP;
-    return CB::P0 + tri(tri_p(s - PL::B_PU), tri_v(s - PL::B_PU));
+    const int lo = 16 * (threadIdx.x & 63);
+    u32x4 w;
+    if constexpr (S < PL::B_PU) w = __builtin_amdgcn_raw_buffer_load_b128(r.q, lo + 1024 * ((S % PL::NP) * PL::KB + S / PL::NP), 0, 0);
+    else w = __builtin_amdgcn_raw_buffer_load_b128(r.p, lo + 1024 * tri(tri_p(S - PL::B_PU), tri_v(S - PL::B_PU)), 0, 0);
+    return __builtin_bit_cast(h8, w);
+}
+template <int DK, int S>
+__device__ __forceinline__ void load_out_ops(OutOps<DK>& ops, const OutSrc& r) {
+    if constexpr (S < Plan<DK>::B_END) {
+        ops.f[S] = load_out_op<DK, S>(r);
+        load_out_ops<DK, S + 1>(ops, r);
+    }
 }
 
 // The state (f16, as the products' B operand) and U (f16) handed from the
@@ -848,7 +881,7 @@ __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16
                 put_h8(xc + Xchg<DK>::UB, v, pack_h8(x.uu[2 * v], x.uu[2 * v + 1]));
                 x.ug[v] = pack_h8(x.gq[2 * v] * x.uu[2 * v], x.gq[2 * v + 1] * x.uu[2 * v + 1]);
             }
-            __syncthreads();  // U published (the output waves wait here for it)
+            lds_barrier();  // U published (the output waves wait here for it)
 #pragma unroll
             for (int t = 0; t < NT; ++t) st[t] = x.gC * st[t];
         }
@@ -880,13 +913,13 @@ struct OutRegs {
     using PL = Plan<DK>;
     h8 sb[PL::KB], ub[PL::VB];
     f32x4 o[PL::NP];
-    h8 fa[PL::B_END];
     f32x4 gp[PL::NP];
 };
 
 template <int DK, int OUT, bool BF16, int NSL, int S>
-__device__ __forceinline__ void out_step(OutRegs<DK>& x, const unsigned char* blk, const unsigned char* xc,
-                                         unsigned char* ost, float scale, const DmaCtx& d) {
+__device__ __forceinline__ void out_step(OutRegs<DK>& x, OutOps<DK>& ops, const OutSrc& nsrc,
+                                         const unsigned char* blk, const unsigned char* xc, unsigned char* ost,
+                                         float scale, const DmaCtx& d) {
     using PL = Plan<DK>;
     using CB = ChunkBlock<DK, BF16, NSL>;
     constexpr int NP = PL::NP, VB = PL::VB;
@@ -894,7 +927,6 @@ __device__ __forceinline__ void out_step(OutRegs<DK>& x, const unsigned char* bl
     if constexpr (S < PL::B_END) {
         // the next chunk's loads due at this step
         dma_slots<DK, BF16, NSL, S * NSLOT / PL::B_END, (S + 1) * NSLOT / PL::B_END>(d);
-        if constexpr (S + PL::D < PL::B_END) x.fa[S + PL::D] = frag_at(blk, frag_b<DK>(S + PL::D));
         if constexpr (S == PL::B_PU) {
             const int lg = (threadIdx.x & 63) >> 4;
             const float* gam = reinterpret_cast<const float*>(blk + CB::G0);
@@ -903,19 +935,20 @@ __device__ __forceinline__ void out_step(OutRegs<DK>& x, const unsigned char* bl
                 x.gp[p] = *reinterpret_cast<const f32x4*>(gam + pair_row(p, 4 * lg));
                 x.o[p] = x.gp[p] * x.o[p];  // gamma Q H
             }
-            __syncthreads();  // U from the chain wave
+            lds_barrier();  // U from the chain wave (the next chunk's loads stay in flight)
 #pragma unroll
             for (int v = 0; v < VB; ++v) x.ub[v] = get_h8(xc + Xchg<DK>::UB, v);
         }
         if constexpr (S < PL::B_PU) {
             constexpr int p = S % NP, u = S / NP;
-            x.o[p] = mfma16(x.fa[S], x.sb[u], x.o[p]);
+            x.o[p] = mfma16(ops.f[S], x.sb[u], x.o[p]);
         } else {
             constexpr int p = tri_p(S - PL::B_PU), v = tri_v(S - PL::B_PU);
-            x.o[p] = mfma16(x.fa[S], x.ub[v], x.o[p]);
+            x.o[p] = mfma16(ops.f[S], x.ub[v], x.o[p]);
         }
+        ops.f[S] = load_out_op<DK, S>(nsrc);  // the next chunk's operand
         __builtin_amdgcn_sched_barrier(0);
-        out_step<DK, OUT, BF16, NSL, S + 1>(x, blk, xc, ost, scale, d);
+        out_step<DK, OUT, BF16, NSL, S + 1>(x, ops, nsrc, blk, xc, ost, scale, d);
     } else {
         // O -> staging (written out at the start of the next chunk)
         const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
@@ -945,8 +978,8 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&st)[DK / 16], h8 (&sb)[DK / 
 }
 
 template <int DK, int OUT, bool BF16, int NSL>
-__device__ __forceinline__ void out_chunk(const unsigned char* blk, const unsigned char* xc, unsigned char* ost,
-                                          float scale, const DmaCtx& d) {
+__device__ __forceinline__ void out_chunk(OutOps<DK>& ops, const OutSrc& nsrc, const unsigned char* blk,
+                                          const unsigned char* xc, unsigned char* ost, float scale, const DmaCtx& d) {
     using PL = Plan<DK>;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     OutRegs<DK> x;
@@ -954,9 +987,7 @@ __device__ __forceinline__ void out_chunk(const unsigned char* blk, const unsign
     for (int u = 0; u < PL::KB; ++u) x.sb[u] = get_h8(xc + Xchg<DK>::SB, u);
 #pragma unroll
     for (int p = 0; p < PL::NP; ++p) x.o[p] = z;
-#pragma unroll
-    for (int s = 0; s < PL::D; ++s) x.fa[s] = frag_at(blk, frag_b<DK>(s));
-    out_step<DK, OUT, BF16, NSL, 0>(x, blk, xc, ost, scale, d);
+    out_step<DK, OUT, BF16, NSL, 0>(x, ops, nsrc, blk, xc, ost, scale, d);
 }
 
 template <int DK, int OUT, bool BF16, int NSL>
@@ -1009,11 +1040,17 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
     }
     unsigned char* xc = lds_raw + 2 * L::BLK + sl * L::XC;
     unsigned char* ost = lds_raw + 2 * L::BLK + NSL * L::XC + sl * L::OST;
-    // chain wave: lane (c, g) holds H[d_k][j] = S[j][d_k] for d_k = pair_row(t, 4g + r)
     float* stp = a.state + (((size_t)s * a.h_v + X.h) * a.d_v + X.col0 + 16 * sl + c) * DK;
-    f32x4 st[NT];
-    h8 sb[DK / 32];  // st in f16, the B operand of K H and Q H
+    // Each role runs its own loop (the same barriers per chunk), so the registers of one role's
+    // loop-carried values are not held by the other.  Every chunk starts with the output waves'
+    // wait for their loads of the chunk (loads into LDS and registers count as vector-memory
+    // operations, which the barrier alone does not wait for) and a barrier that publishes the
+    // chunk with the chain waves' starting state; every wave is then done with the other half
+    // of the double buffer.
     if (chain) {
+        // lane (c, g) holds H[d_k][j] = S[j][d_k] for d_k = pair_row(t, 4g + r)
+        f32x4 st[NT];
+        h8 sb[DK / 32];  // st in f16, the B operand of K H and Q H
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -1023,20 +1060,10 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
             sb[u] = pack_h8(st[2 * u], st[2 * u + 1]);
             put_h8(xc + Xchg<DK>::SB, u, sb[u]);
         }
-    } else {
-        const DmaCtx d0 = dma_ctx<DK, BF16, NSL>(X, 0, lds_raw, sl);
-        dma_slots<DK, BF16, NSL, 0, ChunkBlock<DK, BF16, NSL>::NLOAD / NSL>(d0);
-    }
-    for (int ck = 0; ck < X.nch; ++ck) {
-        // the output waves' loads of chunk ck have landed (the wait: loads into LDS count as
-        // vector-memory operations, which the barrier alone does not wait for) and are
-        // published by the barrier, with the chain waves' starting state; every wave is
-        // done with the other half of the double buffer
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        const unsigned char* cur = lds_raw + (ck & 1) * L::BLK;
-        if (chain) {
-            chain_chunk<DK, BF16, NSL>(st, sb, cur, xc, sl);
+        for (int ck = 0; ck < X.nch; ++ck) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            chain_chunk<DK, BF16, NSL>(st, sb, lds_raw + (ck & 1) * L::BLK, xc, sl);
             // the state after every state_interval-th full chunk, for prefix caching
             if (a.chunk_states != nullptr && (ck + 1) % a.state_interval == 0 && (ck + 1) * kC <= X.T) {
                 const size_t m = (size_t)sq.cst0 + (ck + 1) / a.state_interval - 1;
@@ -1046,24 +1073,27 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
 #pragma unroll
                     for (int r = 0; r < 4; ++r) csp[pair_row(t, 4 * lg) + r] = st[t][r];
             }
-        } else {
-            if (ck > 0) write_out<DK, OUT>(X, ost, ck - 1, sl);
-            unsigned char* nxt = lds_raw + ((ck + 1) & 1) * L::BLK;
-            // the next chunk (the last chunk loads itself again into the idle block: harmless)
-            const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + 1, nxt, sl);
-            out_chunk<DK, OUT, BF16, NSL>(cur, xc, ost, a.scale, d);
         }
-    }
-    if (chain) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) stp[pair_row(t, 4 * lg) + r] = st[t][r];
     } else {
+        OutOps<DK> ops;
+        load_out_ops<DK, 0>(ops, out_src(X, 0));
+        const DmaCtx d0 = dma_ctx<DK, BF16, NSL>(X, 0, lds_raw, sl);
+        dma_slots<DK, BF16, NSL, 0, ChunkBlock<DK, BF16, NSL>::NLOAD / NSL>(d0);
+        for (int ck = 0; ck < X.nch; ++ck) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (ck > 0) write_out<DK, OUT>(X, ost, ck - 1, sl);
+            // the next chunk (the last chunk loads itself again: harmless)
+            const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + 1, lds_raw + ((ck + 1) & 1) * L::BLK, sl);
+            out_chunk<DK, OUT, BF16, NSL>(ops, out_src(X, ck + 1), lds_raw + (ck & 1) * L::BLK, xc, ost, a.scale, d);
+        }
         write_out<DK, OUT>(X, ost, X.nch - 1, sl);
     }
 }
-
 template <typename K>
 hipError_t set_lds(K kernel, size_t lds) {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
