@@ -925,8 +925,6 @@ __device__ __forceinline__ void out_step(OutRegs<DK>& x, OutOps<DK>& ops, const 
     constexpr int NP = PL::NP, VB = PL::VB;
     constexpr int NSLOT = CB::NLOAD / NSL;
     if constexpr (S < PL::B_END) {
-        // the next chunk's loads due at this step
-        dma_slots<DK, BF16, NSL, S * NSLOT / PL::B_END, (S + 1) * NSLOT / PL::B_END>(d);
         if constexpr (S == PL::B_PU) {
             const int lg = (threadIdx.x & 63) >> 4;
             const float* gam = reinterpret_cast<const float*>(blk + CB::G0);
@@ -956,6 +954,9 @@ __device__ __forceinline__ void out_step(OutRegs<DK>& x, OutOps<DK>& ops, const 
         for (int p = 0; p < NP; ++p)
 #pragma unroll
             for (int r = 0; r < 4; ++r) stage_o<OUT>(ost, pair_row(p, 4 * lg) + r, c, scale * x.o[p][r]);
+        // the loads of the chunk after next into LDS, after this chunk's register loads, so
+        // that the next chunk's in-order wait for those leaves these in flight
+        dma_slots<DK, BF16, NSL, 0, NSLOT>(d);
     }
 }
 
@@ -992,10 +993,11 @@ __device__ __forceinline__ void out_chunk(OutOps<DK>& ops, const OutSrc& nsrc, c
 
 template <int DK, int OUT, bool BF16, int NSL>
 struct ScanLayout {
+    static constexpr int NBUF = 3;  // chunk c in use, c + 1 landed or landing, c + 2 being loaded
     static constexpr int BLK = ChunkBlock<DK, BF16, NSL>::BYTES;
     static constexpr int XC = Xchg<DK>::BYTES;
     static constexpr int OST = OStage<OUT>::BYTES;
-    static constexpr int BYTES = 2 * BLK + NSL * (XC + OST);
+    static constexpr int BYTES = NBUF * BLK + NSL * (XC + OST);
 };
 
 // One workgroup of 2 NSL waves per (sequence, value head, 16 NSL value
@@ -1038,8 +1040,8 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
             return;  // uniform over the workgroup: every wave leaves before any barrier
         }
     }
-    unsigned char* xc = lds_raw + 2 * L::BLK + sl * L::XC;
-    unsigned char* ost = lds_raw + 2 * L::BLK + NSL * L::XC + sl * L::OST;
+    unsigned char* xc = lds_raw + L::NBUF * L::BLK + sl * L::XC;
+    unsigned char* ost = lds_raw + L::NBUF * L::BLK + NSL * L::XC + sl * L::OST;
     float* stp = a.state + (((size_t)s * a.h_v + X.h) * a.d_v + X.col0 + 16 * sl + c) * DK;
     // Each role runs its own loop (the same barriers per chunk), so the registers of one role's
     // loop-carried values are not held by the other.  Every chunk starts with the output waves'
@@ -1063,7 +1065,7 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
         for (int ck = 0; ck < X.nch; ++ck) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            chain_chunk<DK, BF16, NSL>(st, sb, lds_raw + (ck & 1) * L::BLK, xc, sl);
+            chain_chunk<DK, BF16, NSL>(st, sb, lds_raw + (ck % L::NBUF) * L::BLK, xc, sl);
             // the state after every state_interval-th full chunk, for prefix caching
             if (a.chunk_states != nullptr && (ck + 1) % a.state_interval == 0 && (ck + 1) * kC <= X.T) {
                 const size_t m = (size_t)sq.cst0 + (ck + 1) / a.state_interval - 1;
@@ -1079,17 +1081,24 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
 #pragma unroll
             for (int r = 0; r < 4; ++r) stp[pair_row(t, 4 * lg) + r] = st[t][r];
     } else {
+        constexpr int NDMA = ChunkBlock<DK, BF16, NSL>::NLOAD / NSL;  // LDS loads per chunk and output wave
+        static_assert(NDMA < 64, "vmcnt field of the top wait");
         OutOps<DK> ops;
         load_out_ops<DK, 0>(ops, out_src(X, 0));
-        const DmaCtx d0 = dma_ctx<DK, BF16, NSL>(X, 0, lds_raw, sl);
-        dma_slots<DK, BF16, NSL, 0, ChunkBlock<DK, BF16, NSL>::NLOAD / NSL>(d0);
+        dma_slots<DK, BF16, NSL, 0, NDMA>(dma_ctx<DK, BF16, NSL>(X, 0, lds_raw, sl));
+        dma_slots<DK, BF16, NSL, 0, NDMA>(dma_ctx<DK, BF16, NSL>(X, 1, lds_raw + L::BLK, sl));
         for (int ck = 0; ck < X.nch; ++ck) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+            // everything but the last NDMA loads -- those of chunk ck + 1, issued last -- has
+            // landed: this chunk's LDS block and registers, and the previous chunk's stores
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt((NDMA & 15) | (NDMA >> 4) << 14 | 0x0070);  // vmcnt(NDMA) lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
             if (ck > 0) write_out<DK, OUT>(X, ost, ck - 1, sl);
-            // the next chunk (the last chunk loads itself again: harmless)
-            const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + 1, lds_raw + ((ck + 1) & 1) * L::BLK, sl);
-            out_chunk<DK, OUT, BF16, NSL>(ops, out_src(X, ck + 1), lds_raw + (ck & 1) * L::BLK, xc, ost, a.scale, d);
+            // the chunk after next (the last chunks load themselves again into an idle block: harmless)
+            const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + 2, lds_raw + ((ck + 2) % L::NBUF) * L::BLK, sl);
+            out_chunk<DK, OUT, BF16, NSL>(ops, out_src(X, ck + 1), lds_raw + (ck % L::NBUF) * L::BLK, xc, ost, a.scale,
+                                          d);
         }
         write_out<DK, OUT>(X, ost, X.nch - 1, sl);
     }
