@@ -489,16 +489,17 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
 // takes R = V - gamma K H, and O and the state update take U, all without
 // moving data between lanes.
 //
-// All slices of a workgroup read the same A operands (K, Q, T', P of their
-// head), so the workgroup brings each chunk's operands into LDS once: buffer
-// loads that write LDS directly (no registers), split between the output
-// waves, one chunk ahead into the other half of a double buffer.  The LDS
-// copy is in fragment order -- fragment f, lane l at f * 1 KB + 16 l -- so
-// an operand read is one conflict-free 16-byte LDS read (K^T: two transposing
-// reads of the K fragments).  Two barriers per chunk: at the top, after each
-// output wave's wait for its own loads (publishing the chunk, and telling
-// every wave that the other half of the buffer is free), and in the middle,
-// where the chain waves hand U to the output waves.
+// All slices of a workgroup read the same A operands of their head.  The
+// chain waves' (K, T', with V and the gates) come into LDS once per workgroup:
+// buffer loads that write LDS directly (no registers), split between the
+// output waves, two chunks ahead into one of three LDS blocks.  The LDS copy
+// is in fragment order -- fragment f, lane l at f * 1 KB + 16 l -- so an
+// operand read is one conflict-free 16-byte LDS read (K^T: two transposing
+// reads of the K fragments).  The output waves' Q and P go straight into
+// their registers one chunk ahead.  Two barriers per chunk: at the top, after
+// each output wave's wait for its loads of the chunk (publishing the chunk,
+// and telling every wave that the block of the chunk before is free), and in
+// the middle, where the chain waves hand U to the output waves.
 __device__ __forceinline__ h8 pack_h8(const f32x4& lo, const f32x4& hi) {
     h8 r;
 #pragma unroll
@@ -1047,8 +1048,8 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
     // loop-carried values are not held by the other.  Every chunk starts with the output waves'
     // wait for their loads of the chunk (loads into LDS and registers count as vector-memory
     // operations, which the barrier alone does not wait for) and a barrier that publishes the
-    // chunk with the chain waves' starting state; every wave is then done with the other half
-    // of the double buffer.
+    // chunk with the chain waves' starting state; every wave is then done with the LDS block of
+    // the chunk before, which the chunk after next is loaded into.
     if (chain) {
         // lane (c, g) holds H[d_k][j] = S[j][d_k] for d_k = pair_row(t, 4g + r)
         f32x4 st[NT];
