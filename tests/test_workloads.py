@@ -54,3 +54,15 @@ def test_ledger_matches_hand_count():
     assert led["verify_total"] == 32_184_320
     assert led["commit"] == 4_718_592
     assert led["total"] == 36_902_912
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; asking for more exits with a message before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout + r.stderr
