@@ -1102,6 +1102,8 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
                                           d);
         }
         write_out<DK, OUT>(X, ost, X.nch - 1, sl);
+        // the last chunks' repeated loads into LDS land before the workgroup's LDS is released
+        __builtin_amdgcn_s_waitcnt(0);
     }
 }
 template <typename K>
