@@ -420,11 +420,15 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
             const float li = gl[16 * jt + c];
             const int i = 16 * jt + c;
             float* dst = mat ? W.P[tx] : W.A[tx];
+            // P keeps the diagonal (i <= t); A is strictly lower (i < t) and carries beta_t.
+            // Selects, not branches: mat is uniform over the wave, i and t are not.
+            const int below = mat ? 0 : 1;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * it + 4 * lg + r;
                 const float e2 = exp2_fast(lt[r] - li);
-                dst[(4 * lg + r) * kTS + c] = mat ? (i <= t ? e2 * gram[jj][r] : 0.f) : (i < t ? bt[r] * e2 * gram[jj][r] : 0.f);
+                const float v = (mat ? e2 : bt[r] * e2) * gram[jj][r];
+                dst[(4 * lg + r) * kTS + c] = i + below <= t ? v : 0.f;
             }
         }
         __syncthreads();
