@@ -446,10 +446,12 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
 #pragma unroll
                     for (int e = 0; e < 4; ++e) arow[4 * m4 + e] = v[e];
                 }
-                float sum = (t == jc) ? 1.f : 0.f;
+                // four independent partial sums: x[t] waits on x[t - 1] through one product and
+                // two additions instead of a chain of t products
+                float ps[4] = {(t == jc) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int m = 0; m < t; ++m) sum = fmaf(-arow[m], x[m], sum);
-                x[t] = sum;
+                for (int m = 0; m < t; ++m) ps[m & 3] = fmaf(-arow[m], x[m], ps[m & 3]);
+                x[t] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
             }
 #pragma unroll
             for (int t = 0; t < 16; ++t) W.T(bb, bb)[t * kTS + jc] = x[t];  // after all reads of A_bb
