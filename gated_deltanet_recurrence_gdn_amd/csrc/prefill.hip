@@ -192,7 +192,6 @@ struct PrepHead {
     float A[10][kTile];  // strict lower beta Gamma K K^T; diagonal tiles then hold T
     float To[6][kTile];  // off-diagonal tiles of T = (I + A)^-1
     float P[10][kTile];  // Gamma o tril(Q K^T)
-    float Y[4][kTile];   // per-wave scratch tile of the off-diagonal products
     __device__ float* T(int it, int jt) { return it == jt ? A[tix(it, it)] : To[tix(it, jt) - it]; }
 };
 
@@ -289,9 +288,10 @@ __device__ __forceinline__ void write_frag(PrepHead& W, const float* gl, _Float1
     *reinterpret_cast<h8*>(dst + (f * 64 + lane) * 8) = v;
 }
 
-// Off-diagonal block (ib, jb) of T on one wave: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
-// (v_mfma_f32_16x16x4_f32: A[i][4 s + lg], B[4 s + lg][c], D rows 4 lg + r).
-__device__ __forceinline__ void offdiag_block(PrepHead& W, int ib, int jb, float* Y) {
+// Off-diagonal block (ib, jb) of T on one wave: T_ij = -T_ii Y with
+// Y = sum_{k=j}^{i-1} A_ik T_kj (v_mfma_f32_16x16x4_f32: A[i][4 s + lg],
+// B[4 s + lg][c], D rows 4 lg + r).
+__device__ __forceinline__ void offdiag_block(PrepHead& W, int ib, int jb) {
     const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int kb = jb; kb < ib; ++kb) {
@@ -301,14 +301,13 @@ __device__ __forceinline__ void offdiag_block(PrepHead& W, int ib, int jb, float
         for (int s = 0; s < 4; ++s)
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ab[c * kTS + 4 * s + lg], Tb[(4 * s + lg) * kTS + c], acc, 0, 0, 0);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Y[(4 * lg + r) * kTS + c] = acc[r];
-    wave_lds_order();
+    // T_ii Y with Y straight from its accumulator: step s contracts over k = 4 lg + s, so
+    // lane (c, lg) supplies Y[4 lg + s][c] -- its own register s -- and T_ii[c][4 lg + s]
     const float* Ti = W.T(ib, ib);
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        x = __builtin_amdgcn_mfma_f32_16x16x4f32(Ti[c * kTS + 4 * s + lg], Y[(4 * s + lg) * kTS + c], x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(Ti[c * kTS + 4 * lg + s], acc[s], x, 0, 0, 0);
 #pragma unroll
     for (int r = 0; r < 4; ++r) W.T(ib, jb)[(4 * lg + r) * kTS + c] = -x[r];
 }
@@ -463,11 +462,11 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         }
         __syncthreads();
         // off-diagonal blocks by distance, one block per wave
-        if (wave < 3) offdiag_block(W, wave + 1, wave, W.Y[wave]);
+        if (wave < 3) offdiag_block(W, wave + 1, wave);
         __syncthreads();
-        if (wave < 2) offdiag_block(W, wave + 2, wave, W.Y[wave]);
+        if (wave < 2) offdiag_block(W, wave + 2, wave);
         __syncthreads();
-        if (wave == 0) offdiag_block(W, 3, 0, W.Y[0]);
+        if (wave == 0) offdiag_block(W, 3, 0);
         __syncthreads();
         // T' = T diag(beta) fragments
         _Float16* Tw = reinterpret_cast<_Float16*>(wsb + ws.T) + unit_v * kC * kC;
