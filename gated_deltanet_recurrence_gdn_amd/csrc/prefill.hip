@@ -436,21 +436,22 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
             const int bb = lane >> 4, jc = lane & 15;
             const float* Ab = W.A[tix(bb, bb)];
             float x[16];
+            // row t's first t entries, read one row ahead of their use
+            f32x4 row[2][4];
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                float arow[16];
+                if (t + 1 < 16) {
 #pragma unroll
-                for (int m4 = 0; m4 < 4; ++m4) {
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(Ab + t * kTS + 4 * m4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) arow[4 * m4 + e] = v[e];
+                    for (int q = 0; q < 4; ++q)
+                        if (4 * q < t + 1) row[(t + 1) & 1][q] = *reinterpret_cast<const f32x4*>(Ab + (t + 1) * kTS + 4 * q);
                 }
                 // four independent partial sums: x[t] waits on x[t - 1] through one product and
                 // two additions instead of a chain of t products
                 float ps[4] = {(t == jc) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int m = 0; m < t; ++m) ps[m & 3] = fmaf(-arow[m], x[m], ps[m & 3]);
+                for (int m = 0; m < t; ++m) ps[m & 3] = fmaf(-row[t & 1][m / 4][m % 4], x[m], ps[m & 3]);
                 x[t] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int t = 0; t < 16; ++t) W.T(bb, bb)[t * kTS + jc] = x[t];  // after all reads of A_bb
