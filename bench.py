@@ -294,6 +294,9 @@ def secondary(torch, gb, wl, dev, args):
     torch.cuda.empty_cache()
     out["replay_chain"] = bench_replay(torch, gb, wl, dev, args)
     log("replay_chain", out["replay_chain"])
+    out["replay_batched_chain"] = bench_replay(torch, gb, wl, dev, args, "batched_chain", 1, n,
+                                               max(2, args.warmup // 25))
+    log("replay_batched_chain", out["replay_batched_chain"])
     out["index_chain"] = bench_index(torch, gb, wl, dev, args)
     log("index_chain", out["index_chain"])
     out["prefill"] = bench_prefill(torch, gb, wl, dev, max(5, args.steps // 25))
@@ -303,15 +306,16 @@ def secondary(torch, gb, wl, dev, args):
     return out
 
 
-def bench_replay(torch, gb, wl, dev, args):
-    """Decode step with commit by replay at the chain workload: one launch
-    replays the previous block's accepted prefix from the cached fp32 state,
-    writes the committed state and verifies the next block (outputs only, no
-    persisted node states).  Same rotation over buffer sets as the headline."""
-    w = wl.WORKLOADS["chain"]
+def bench_replay(torch, gb, wl, dev, args, name="chain", n_sets=None, steps=None, warmup=None):
+    """Decode step with commit by replay: one launch replays the previous
+    block's accepted prefix from the cached fp32 state, writes the committed
+    state and verifies the next block (outputs only, no persisted node
+    states).  At the chain workload the same rotation over buffer sets as the
+    headline; at the batched workload one set."""
+    w = wl.WORKLOADS[name]
     led = wl.algorithmic_bytes_replay(w)
     sets = []
-    for i in range(args.sets):
+    for i in range(args.sets if n_sets is None else n_sets):
         base = wl.WORKLOAD_SEEDS[w.name] + 7919 * i
         prev = dev_set(torch, wl.make_inputs(w, seed=base), dev)
         cur = dev_set(torch, wl.make_inputs(w, seed=base + 1), dev)
@@ -324,12 +328,14 @@ def bench_replay(torch, gb, wl, dev, args):
         gb.gdn_replay_verify_chain(p["accepted"], p["q"], p["k"], p["v"], p["alpha"], p["beta"], s["q"], s["k"],
                                    s["v"], s["alpha"], s["beta"], s["state0"], out=s["out"])
 
-    sm, km = time_steps(torch, sets, step, step, args.steps, args.warmup)
+    sm, km = time_steps(torch, sets, step, step, args.steps if steps is None else steps,
+                        args.warmup if warmup is None else warmup)
     res = {"tokens_per_s_per_layer": w.batch * w.n_nodes / (sm * 1e-3), "ms_per_step": sm,
            "kernel_us": km * 1e3, "step_bytes": led["total"],
            "achieved_gbs": led["total"] / (km * 1e-3) / 1e9,
            "hbm_frac": led["total"] / (km * 1e-3) / 1e9 / HBM_PEAK_GBS,
-           "kernel": "replay_verify_chain_kernel<128,1,no persist,f32 out,nt>"}
+           "kernel": ("replay_verify_chain_kernel<128,1,no persist,f32 out,nt>" if w.batch == 1 else
+                      "replay_verify_chain_kernel<128,2,no persist,f32 out>")}
     del sets
     torch.cuda.empty_cache()
     return res

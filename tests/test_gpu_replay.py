@@ -152,6 +152,40 @@ def test_replay_verify_equals_replay_then_verify(persist_dtype):
         assert torch.equal(per, per_r)
 
 
+def test_replay_verify_batched_full_size():
+    """384 units in one launch (two row groups per wave, both blocks staged):
+    the fused replay + verify equals the replay followed by a verify, bit for
+    bit, for the committed state and every output; sampled units against the
+    oracle."""
+    w = wl.WORKLOADS["batched_chain"]
+    d1 = wl.make_inputs(w)
+    d2 = wl.make_inputs(w, seed=wl.WORKLOAD_SEEDS[w.name] + 1)
+    t1, t2 = dev_inputs(d1), dev_inputs(d2)
+    acc = torch.from_numpy(np.ascontiguousarray(d1["accepted"], dtype=np.int32)).to(DEV)
+    st_ref = t1["state0"].clone()
+    assert _replay(t1, d1["accepted"], st_ref) == 0
+    out_r, _, _ = run_chain(t2, w.n_nodes, persist_dtype=None, final=False, state=st_ref)
+    st = t1["state0"].clone()
+    out = torch.full_like(out_r, float("nan"))
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gb.gdn_replay_verify_chain(acc, t1["q"], t1["k"], t1["v"], t1["alpha"], t1["beta"], t2["q"], t2["k"], t2["v"],
+                               t2["alpha"], t2["beta"], st, out=out, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(st, st_ref)
+    assert torch.equal(out, out_r)
+    for b in (0, 191, 383):
+        sl = slice(b, b + 1)
+        a = int(d1["accepted"][b])
+        ref1 = oracle.chain(d1["q"][sl], d1["k"][sl], d1["v"][sl], d1["alpha"][sl], d1["beta"][sl], d1["state0"][sl])
+        s1 = np.ascontiguousarray(ref1["nodes"][:, a])
+        ref2 = oracle.chain(d2["q"][sl], d2["k"][sl], d2["v"][sl], d2["alpha"][sl], d2["beta"][sl], s1)
+        e_s = max_rel(to_host(st[sl]), s1)
+        e_o = max_rel(to_host(out[sl]), ref2["out"])
+        say(f"batched replay+verify unit {b} acc={a}: state {e_s:.2e} out {e_o:.2e}")
+        assert e_s <= STATE_TOL and e_o <= OUT_TOL
+
+
 def test_replay_decode_loop_matches_oracle():
     """Four decode steps with one replay + verify launch each (accepted lengths
     vary per sequence) against the oracle applied step by step; the state
