@@ -507,13 +507,10 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
 // and telling every wave that the block of the chunk before is free), and in
 // the middle, where the chain waves hand U to the output waves.
 __device__ __forceinline__ h8 pack_h8(const f32x4& lo, const f32x4& hi) {
-    h8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[i] = (_Float16)lo[i];
-        r[4 + i] = (_Float16)hi[i];
-    }
-    return r;
+    // whole-vector conversions (one packed convert per pair, round to nearest even)
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 a = __builtin_convertvector(lo, h4), b = __builtin_convertvector(hi, h4);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Buffer resources: a uniform base per matrix and chunk, bounded by its size,
@@ -812,9 +809,12 @@ struct ChainRegs {
     float gC;
 };
 
-template <int DK, bool BF16, int NSL, int E>
+// The chain wave's reads besides its A operands, in issue order: gamma_C first
+// (the state decays during K H), then V, gamma and Gamma_C at this lane's rows.
+template <int DK, bool BF16, int NSL, int EI>
 __device__ __forceinline__ void extra_read(ChainRegs<DK>& x, const unsigned char* blk, int sl) {
     using CB = ChunkBlock<DK, BF16, NSL>;
+    constexpr int E = EI == 0 ? 24 : EI - 1;
     const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
     const float* gam = reinterpret_cast<const float*>(blk + CB::G0);
     if constexpr (E < 16) {
@@ -860,16 +860,20 @@ __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16
         if constexpr (S + PL::D < PL::A_END) x.fa[S + PL::D] = chain_operand<DK, S + PL::D>(blk);
         if constexpr (S < PL::NKH)
             extra_reads<DK, BF16, NSL, S * PL::NEXTRA / PL::NKH, (S + 1) * PL::NEXTRA / PL::NKH>(x, blk, sl);
-        if constexpr (S == PL::A_U) {
-            if constexpr (BF16) {
+        // the state decays by gamma_C, one tile per step while K H runs (its products read
+        // the f16 copy), so the multiplies issue under the products instead of before the update
+        static_assert(2 + NT <= PL::A_ST, "decay steps end before the update");
+        if constexpr (S >= 2 && S - 2 < NT) st[S - 2] = x.gC * st[S - 2];
+        if constexpr (BF16 && S == PL::NKH - 1) {
 #pragma unroll
-                for (int p = 0; p < NP; ++p) {
-                    x.vx[p][0] = bf16_lo(x.vr[p][0]);
-                    x.vx[p][1] = bf16_hi(x.vr[p][0]);
-                    x.vx[p][2] = bf16_lo(x.vr[p][1]);
-                    x.vx[p][3] = bf16_hi(x.vr[p][1]);
-                }
+            for (int p = 0; p < NP; ++p) {
+                x.vx[p][0] = bf16_lo(x.vr[p][0]);
+                x.vx[p][1] = bf16_hi(x.vr[p][0]);
+                x.vx[p][2] = bf16_lo(x.vr[p][1]);
+                x.vx[p][3] = bf16_hi(x.vr[p][1]);
             }
+        }
+        if constexpr (S == PL::A_U) {
             // R = V - gamma K H at this lane's rows pair_row(p, 4 lg) + r
 #pragma unroll
             for (int v = 0; v < VB; ++v)
@@ -882,15 +886,13 @@ __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16
                     }
         }
         if constexpr (S == PL::A_ST) {
-            // U in f16 to the output wave; U scaled by Gamma_{C,t} here; the state decays
+            // U in f16 to the output wave; U scaled by Gamma_{C,t} here
 #pragma unroll
             for (int v = 0; v < VB; ++v) {
                 put_h8(xc + Xchg<DK>::UB, v, pack_h8(x.uu[2 * v], x.uu[2 * v + 1]));
                 x.ug[v] = pack_h8(x.gq[2 * v] * x.uu[2 * v], x.gq[2 * v + 1] * x.uu[2 * v + 1]);
             }
             lds_barrier();  // U published (the output waves wait here for it)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) st[t] = x.gC * st[t];
         }
         if constexpr (S < PL::A_U) {
             constexpr int p = S % NP, u = S / NP;
