@@ -753,9 +753,23 @@ __device__ __forceinline__ h8 chain_operand(const unsigned char* blk) {
 // from the workspace straight into its registers, one chunk ahead, instead of
 // through LDS: each register takes the next chunk's fragment right after the
 // product that reads it has been issued.
-template <int DK>
+// The two output waves of a workgroup split the chunk by rows: wave H owns
+// output rows 32 H .. 32 H + 31 (row tiles 2 H and 2 H + 1) of both slices, so
+// each Q and P fragment is loaded by one wave only and serves both slices'
+// products.  Steps j < NQ: Q H with tile 2 H + j % 2 and state block j / 2;
+// then P U over the (tile, U block) pairs of the half's tiles.
+template <int DK, int H>
+struct OutPlan {
+    static constexpr int KB = DK / 32;
+    static constexpr int NQ = 2 * KB, NPU = H == 0 ? 2 : 4;
+    static constexpr int B_PU = NQ, B_END = NQ + NPU;
+    static constexpr int NUB = H == 0 ? 1 : 2;  // U blocks the half's products read
+    __device__ static constexpr int pu_p(int k) { return H == 0 ? k : 2 + k % 2; }
+    __device__ static constexpr int pu_v(int k) { return H == 0 ? 0 : k / 2; }
+};
+template <int DK, int H>
 struct OutOps {
-    h8 f[Plan<DK>::B_END];
+    h8 f[OutPlan<DK, H>::B_END];
 };
 struct OutSrc {
     rsrc_t q, p;  // the chunk's Q (per q/k head) and P (per value head) in the workspace
@@ -764,20 +778,23 @@ template <int DK>
 __device__ __forceinline__ OutSrc out_src(const ScanCtx<DK>& X, int ck) {
     return {X.ws_q(X.ws.Q, kC * DK * 2, ck), X.ws_v(X.ws.P, kC * kC * 2, ck)};
 }
-template <int DK, int S>
+template <int DK, int H, int S>
 __device__ __forceinline__ h8 load_out_op(const OutSrc& r) {
-    using PL = Plan<DK>;
+    using OP = OutPlan<DK, H>;
     const int lo = 16 * (threadIdx.x & 63);
     u32x4 w;
-    if constexpr (S < PL::B_PU) w = __builtin_amdgcn_raw_buffer_load_b128(r.q, lo + 1024 * ((S % PL::NP) * PL::KB + S / PL::NP), 0, 0);
-    else w = __builtin_amdgcn_raw_buffer_load_b128(r.p, lo + 1024 * tri(tri_p(S - PL::B_PU), tri_v(S - PL::B_PU)), 0, 0);
+    if constexpr (S < OP::B_PU)
+        w = __builtin_amdgcn_raw_buffer_load_b128(r.q, lo + 1024 * ((2 * H + S % 2) * OP::KB + S / 2), 0, 0);
+    else
+        w = __builtin_amdgcn_raw_buffer_load_b128(r.p, lo + 1024 * tri(OP::pu_p(S - OP::B_PU), OP::pu_v(S - OP::B_PU)),
+                                                  0, 0);
     return __builtin_bit_cast(h8, w);
 }
-template <int DK, int S>
-__device__ __forceinline__ void load_out_ops(OutOps<DK>& ops, const OutSrc& r) {
-    if constexpr (S < Plan<DK>::B_END) {
-        ops.f[S] = load_out_op<DK, S>(r);
-        load_out_ops<DK, S + 1>(ops, r);
+template <int DK, int H, int S>
+__device__ __forceinline__ void load_out_ops(OutOps<DK, H>& ops, const OutSrc& r) {
+    if constexpr (S < OutPlan<DK, H>::B_END) {
+        ops.f[S] = load_out_op<DK, H, S>(r);
+        load_out_ops<DK, H, S + 1>(ops, r);
     }
 }
 
@@ -917,52 +934,69 @@ __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16
     }
 }
 
-template <int DK>
+template <int DK, int NSL>
 struct OutRegs {
-    using PL = Plan<DK>;
-    h8 sb[PL::KB], ub[PL::VB];
-    f32x4 o[PL::NP];
-    f32x4 gp[PL::NP];
+    h8 sb[NSL][DK / 32], ub[NSL][kC / 32];
+    f32x4 o[NSL][2];
+    f32x4 gp[2];
 };
 
-template <int DK, int OUT, bool BF16, int NSL, int S>
-__device__ __forceinline__ void out_step(OutRegs<DK>& x, OutOps<DK>& ops, const OutSrc& nsrc,
-                                         const unsigned char* blk, const unsigned char* xc, unsigned char* ost,
-                                         float scale, const DmaCtx& d) {
-    using PL = Plan<DK>;
+// The output wave's view of the hand-off areas and output staging: slice s's
+// at xc + s * XC and ost + s * OST.
+struct OutPlaces {
+    const unsigned char* xc;
+    unsigned char* ost;
+};
+
+template <int DK, int OUT, bool BF16, int NSL>
+struct ScanLayout;
+
+template <int DK, int OUT, bool BF16, int NSL, int H, int S>
+__device__ __forceinline__ void out_step(OutRegs<DK, NSL>& x, OutOps<DK, H>& ops, const OutSrc& nsrc,
+                                         const unsigned char* blk, const OutPlaces& pl, float scale, const DmaCtx& d) {
+    using OP = OutPlan<DK, H>;
     using CB = ChunkBlock<DK, BF16, NSL>;
-    constexpr int NP = PL::NP, VB = PL::VB;
+    using L = ScanLayout<DK, OUT, BF16, NSL>;
     constexpr int NSLOT = CB::NLOAD / NSL;
-    if constexpr (S < PL::B_END) {
-        if constexpr (S == PL::B_PU) {
+    if constexpr (S < OP::B_END) {
+        if constexpr (S == OP::B_PU) {
             const int lg = (threadIdx.x & 63) >> 4;
             const float* gam = reinterpret_cast<const float*>(blk + CB::G0);
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                x.gp[p] = *reinterpret_cast<const f32x4*>(gam + pair_row(p, 4 * lg));
-                x.o[p] = x.gp[p] * x.o[p];  // gamma Q H
-            }
-            lds_barrier();  // U from the chain wave (the next chunk's loads stay in flight)
+            for (int i = 0; i < 2; ++i) {
+                x.gp[i] = *reinterpret_cast<const f32x4*>(gam + pair_row(2 * H + i, 4 * lg));
 #pragma unroll
-            for (int v = 0; v < VB; ++v) x.ub[v] = get_h8(xc + Xchg<DK>::UB, v);
+                for (int q = 0; q < NSL; ++q) x.o[q][i] = x.gp[i] * x.o[q][i];  // gamma Q H
+            }
+            lds_barrier();  // U from the chain waves (the next chunk's loads stay in flight)
+#pragma unroll
+            for (int q = 0; q < NSL; ++q)
+#pragma unroll
+                for (int v = 0; v < OP::NUB; ++v) x.ub[q][v] = get_h8(pl.xc + q * L::XC + Xchg<DK>::UB, v);
         }
-        if constexpr (S < PL::B_PU) {
-            constexpr int p = S % NP, u = S / NP;
-            x.o[p] = mfma16(ops.f[S], x.sb[u], x.o[p]);
+        // one operand, the products of every slice
+        if constexpr (S < OP::B_PU) {
+            constexpr int i = S % 2, u = S / 2;
+#pragma unroll
+            for (int q = 0; q < NSL; ++q) x.o[q][i] = mfma16(ops.f[S], x.sb[q][u], x.o[q][i]);
         } else {
-            constexpr int p = tri_p(S - PL::B_PU), v = tri_v(S - PL::B_PU);
-            x.o[p] = mfma16(ops.f[S], x.ub[v], x.o[p]);
+            constexpr int i = OP::pu_p(S - OP::B_PU) - 2 * H, v = OP::pu_v(S - OP::B_PU);
+#pragma unroll
+            for (int q = 0; q < NSL; ++q) x.o[q][i] = mfma16(ops.f[S], x.ub[q][v], x.o[q][i]);
         }
-        ops.f[S] = load_out_op<DK, S>(nsrc);  // the next chunk's operand
+        ops.f[S] = load_out_op<DK, H, S>(nsrc);  // the next chunk's operand
         __builtin_amdgcn_sched_barrier(0);
-        out_step<DK, OUT, BF16, NSL, S + 1>(x, ops, nsrc, blk, xc, ost, scale, d);
+        out_step<DK, OUT, BF16, NSL, H, S + 1>(x, ops, nsrc, blk, pl, scale, d);
     } else {
         // O -> staging (written out at the start of the next chunk)
         const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
+        for (int q = 0; q < NSL; ++q)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) stage_o<OUT>(ost, pair_row(p, 4 * lg) + r, c, scale * x.o[p][r]);
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    stage_o<OUT>(pl.ost + q * L::OST, pair_row(2 * H + i, 4 * lg) + r, c, scale * x.o[q][i][r]);
         // the loads of the chunk after next into LDS, after this chunk's register loads, so
         // that the next chunk's in-order wait for those leaves these in flight
         dma_slots<DK, BF16, NSL, 0, NSLOT>(d);
@@ -987,17 +1021,19 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&st)[DK / 16], h8 (&sb)[DK / 
     chain_step<DK, BF16, NSL, 0>(x, st, blk, xc, sl);
 }
 
-template <int DK, int OUT, bool BF16, int NSL>
-__device__ __forceinline__ void out_chunk(OutOps<DK>& ops, const OutSrc& nsrc, const unsigned char* blk,
-                                          const unsigned char* xc, unsigned char* ost, float scale, const DmaCtx& d) {
-    using PL = Plan<DK>;
+template <int DK, int OUT, bool BF16, int NSL, int H>
+__device__ __forceinline__ void out_chunk(OutOps<DK, H>& ops, const OutSrc& nsrc, const unsigned char* blk,
+                                          const OutPlaces& pl, float scale, const DmaCtx& d) {
+    using L = ScanLayout<DK, OUT, BF16, NSL>;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    OutRegs<DK> x;
+    OutRegs<DK, NSL> x;
 #pragma unroll
-    for (int u = 0; u < PL::KB; ++u) x.sb[u] = get_h8(xc + Xchg<DK>::SB, u);
+    for (int q = 0; q < NSL; ++q) {
 #pragma unroll
-    for (int p = 0; p < PL::NP; ++p) x.o[p] = z;
-    out_step<DK, OUT, BF16, NSL, 0>(x, ops, nsrc, blk, xc, ost, scale, d);
+        for (int u = 0; u < DK / 32; ++u) x.sb[q][u] = get_h8(pl.xc + q * L::XC + Xchg<DK>::SB, u);
+        x.o[q][0] = x.o[q][1] = z;
+    }
+    out_step<DK, OUT, BF16, NSL, H, 0>(x, ops, nsrc, blk, pl, scale, d);
 }
 
 template <int DK, int OUT, bool BF16, int NSL>
@@ -1009,9 +1045,48 @@ struct ScanLayout {
     static constexpr int BYTES = NBUF * BLK + NSL * (XC + OST);
 };
 
+// Output wave H (rows 32 H .. 32 H + 31 of both slices; it writes out slice H's
+// staged outputs, which both output waves stage).  Every chunk starts with its
+// wait for its loads of the chunk (loads into LDS and registers count as
+// vector-memory operations, which the barrier alone does not wait for) and the
+// barrier that publishes the chunk with the chain waves' starting state.
+template <int DK, int OUT, bool BF16, int NSL, int H>
+__device__ __forceinline__ void out_wave(const ScanCtx<DK>& X, unsigned char* lds_raw, float scale) {
+    using L = ScanLayout<DK, OUT, BF16, NSL>;
+    static_assert(NSL == 2 && kC == 64, "two output waves, one per 32-row half of a chunk");
+    constexpr int NDMA = ChunkBlock<DK, BF16, NSL>::NLOAD / NSL;  // LDS loads per chunk and output wave
+    static_assert(NDMA < 64, "vmcnt field of the top wait");
+    const OutPlaces pl = {lds_raw + L::NBUF * L::BLK, lds_raw + L::NBUF * L::BLK + NSL * L::XC};
+    OutOps<DK, H> ops;
+    load_out_ops<DK, H, 0>(ops, out_src(X, 0));
+    dma_slots<DK, BF16, NSL, 0, NDMA>(dma_ctx<DK, BF16, NSL>(X, 0, lds_raw, H));
+    dma_slots<DK, BF16, NSL, 0, NDMA>(dma_ctx<DK, BF16, NSL>(X, 1, lds_raw + L::BLK, H));
+    for (int ck = 0; ck < X.nch; ++ck) {
+        // everything but the last NDMA loads -- those of chunk ck + 1, issued last -- has
+        // landed: this chunk's LDS block and registers, and the previous chunk's stores
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((NDMA & 15) | (NDMA >> 4) << 14 | 0x0070);  // vmcnt(NDMA) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (ck > 0) write_out<DK, OUT>(X, pl.ost + H * L::OST, ck - 1, H);
+        // the chunk after next (the last chunks load themselves again into an idle block: harmless)
+        const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + 2, lds_raw + ((ck + 2) % L::NBUF) * L::BLK, H);
+        out_chunk<DK, OUT, BF16, NSL, H>(ops, out_src(X, ck + 1), lds_raw + (ck % L::NBUF) * L::BLK, pl, scale, d);
+    }
+    // both output waves' staging of the last chunk is in place
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    write_out<DK, OUT>(X, pl.ost + H * L::OST, X.nch - 1, H);
+    // the last chunks' repeated loads into LDS land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
 // One workgroup of 2 NSL waves per (sequence, value head, 16 NSL value
 // columns): waves 0 .. NSL-1 are the chain waves of the NSL 16-column slices,
-// waves NSL .. 2 NSL - 1 their output waves.
+// waves NSL .. 2 NSL - 1 the output waves (each one half of every slice's
+// output rows).
 template <int DK, int OUT, bool BF16, int NSL>
 __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillArgs a, const PrefillSeqs seqs) {
     using L = ScanLayout<DK, OUT, BF16, NSL>;
@@ -1020,7 +1095,7 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const bool chain = w < NSL;
-    const int sl = chain ? w : w - NSL;  // slice: value columns col0 + 16 sl ..
+    const int sl = chain ? w : w - NSL;  // chain wave: slice (value columns col0 + 16 sl ..); output wave: half
     const int c = lane & 15, lg = lane >> 4;
     int blk = xcd_logical_block(blockIdx.x, gridDim.x);
     const int grp = blk % a.slices;
@@ -1050,7 +1125,6 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
         }
     }
     unsigned char* xc = lds_raw + L::NBUF * L::BLK + sl * L::XC;
-    unsigned char* ost = lds_raw + L::NBUF * L::BLK + NSL * L::XC + sl * L::OST;
     float* stp = a.state + (((size_t)s * a.h_v + X.h) * a.d_v + X.col0 + 16 * sl + c) * DK;
     // Each role runs its own loop (the same barriers per chunk), so the registers of one role's
     // loop-carried values are not held by the other.  Every chunk starts with the output waves'
@@ -1085,33 +1159,14 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
                     for (int r = 0; r < 4; ++r) csp[pair_row(t, 4 * lg) + r] = st[t][r];
             }
         }
+        __syncthreads();  // the output waves' last barrier (their last chunk's staging is complete)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) stp[pair_row(t, 4 * lg) + r] = st[t][r];
     } else {
-        constexpr int NDMA = ChunkBlock<DK, BF16, NSL>::NLOAD / NSL;  // LDS loads per chunk and output wave
-        static_assert(NDMA < 64, "vmcnt field of the top wait");
-        OutOps<DK> ops;
-        load_out_ops<DK, 0>(ops, out_src(X, 0));
-        dma_slots<DK, BF16, NSL, 0, NDMA>(dma_ctx<DK, BF16, NSL>(X, 0, lds_raw, sl));
-        dma_slots<DK, BF16, NSL, 0, NDMA>(dma_ctx<DK, BF16, NSL>(X, 1, lds_raw + L::BLK, sl));
-        for (int ck = 0; ck < X.nch; ++ck) {
-            // everything but the last NDMA loads -- those of chunk ck + 1, issued last -- has
-            // landed: this chunk's LDS block and registers, and the previous chunk's stores
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt((NDMA & 15) | (NDMA >> 4) << 14 | 0x0070);  // vmcnt(NDMA) lgkmcnt(0)
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            if (ck > 0) write_out<DK, OUT>(X, ost, ck - 1, sl);
-            // the chunk after next (the last chunks load themselves again into an idle block: harmless)
-            const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + 2, lds_raw + ((ck + 2) % L::NBUF) * L::BLK, sl);
-            out_chunk<DK, OUT, BF16, NSL>(ops, out_src(X, ck + 1), lds_raw + (ck % L::NBUF) * L::BLK, xc, ost, a.scale,
-                                          d);
-        }
-        write_out<DK, OUT>(X, ost, X.nch - 1, sl);
-        // the last chunks' repeated loads into LDS land before the workgroup's LDS is released
-        __builtin_amdgcn_s_waitcnt(0);
+        if (sl == 0) out_wave<DK, OUT, BF16, NSL, 0>(X, lds_raw, a.scale);
+        else out_wave<DK, OUT, BF16, NSL, 1>(X, lds_raw, a.scale);
     }
 }
 template <typename K>
