@@ -173,8 +173,8 @@ __device__ __forceinline__ SeqInfo seq_info(const PrefillArgs& a, const PrefillS
 // A = strict_lower(beta_t Gamma_{t,i} k_t.k_i) and its Q K^T tiles into tiles of
 // P = Gamma o tril(Q K^T); one wave forms the diagonal 16 x 16 blocks of
 // T = (I + A)^-1 by forward substitution while the others write P's fragments;
-// the off-diagonal blocks follow by distance (three, two, then one block, one
-// per wave, v_mfma_f32_16x16x4_f32); then all four write T' = T diag(beta).
+// the off-diagonal blocks follow one column per wave (three, two and one
+// blocks, v_mfma_f32_16x16x4_f32); then all four write T' = T diag(beta).
 // Lower tiles are kept tile-major: tile (it, jt), jt <= it, is tile number
 // it (it + 1) / 2 + jt, element (r, c) at r * kTS + c: rows padded to 20 floats
 // (16-byte aligned), so the column reads of the matrix-core operands and the
@@ -288,28 +288,46 @@ __device__ __forceinline__ void write_frag(PrepHead& W, const float* gl, _Float1
     *reinterpret_cast<h8*>(dst + (f * 64 + lane) * 8) = v;
 }
 
-// Off-diagonal block (ib, jb) of T on one wave: T_ij = -T_ii Y with
-// Y = sum_{k=j}^{i-1} A_ik T_kj (v_mfma_f32_16x16x4_f32: A[i][4 s + lg],
-// B[4 s + lg][c], D rows 4 lg + r).
-__device__ __forceinline__ void offdiag_block(PrepHead& W, int ib, int jb) {
+// Column JB of T below the diagonal on one wave, top to bottom:
+// T_ij = -T_ii Y_i with Y_i = A_iJ T_JJ + sum_{J<k<i} A_ik T_kJ.  The column's
+// blocks stay in this wave's registers (accumulator layout: lane (c, lg) holds
+// rows 4 lg + r, column c), so each one feeds the next as the products' B
+// operand by contracting over k = 4 lg + s (lane (c, lg) supplies its own
+// register s); the terms with T_JJ contract over k = 4 s + lg from LDS.  The
+// columns need only the diagonal blocks, so they run side by side on three
+// waves (v_mfma_f32_16x16x4_f32).
+template <int JB>
+__device__ __forceinline__ void offdiag_column(PrepHead& W) {
     const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int kb = jb; kb < ib; ++kb) {
-        const float* Ab = W.A[tix(ib, kb)];
-        const float* Tb = W.T(kb, jb);
+    constexpr int N = 3 - JB;  // blocks below the diagonal
+    const float* Tjj = W.T(JB, JB);
+    f32x4 tcol[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const int ib = JB + 1 + n;
+        const float* Aij = W.A[tix(ib, JB)];
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ab[c * kTS + 4 * s + lg], Tb[(4 * s + lg) * kTS + c], acc, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(Aij[c * kTS + 4 * s + lg], Tjj[(4 * s + lg) * kTS + c], y, 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < n; ++m) {
+            const float* Aik = W.A[tix(ib, JB + 1 + m)];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(Aik[c * kTS + 4 * lg + s], tcol[m][s], y, 0, 0, 0);
+        }
+        const float* Ti = W.T(ib, ib);
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(Ti[c * kTS + 4 * lg + s], y[s], x, 0, 0, 0);
+        tcol[n] = -x;
     }
-    // T_ii Y with Y straight from its accumulator: step s contracts over k = 4 lg + s, so
-    // lane (c, lg) supplies Y[4 lg + s][c] -- its own register s -- and T_ii[c][4 lg + s]
-    const float* Ti = W.T(ib, ib);
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        x = __builtin_amdgcn_mfma_f32_16x16x4f32(Ti[c * kTS + 4 * lg + s], acc[s], x, 0, 0, 0);
+    for (int n = 0; n < N; ++n)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) W.T(ib, jb)[(4 * lg + r) * kTS + c] = -x[r];
+        for (int r = 0; r < 4; ++r) W.T(JB + 1 + n, JB)[(4 * lg + r) * kTS + c] = tcol[n][r];
 }
 
 template <int DK, bool BF16>
@@ -462,12 +480,10 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
             write_frag<false>(W, gl, Pw, 2 * (wave - 1) + 1);
         }
         __syncthreads();
-        // off-diagonal blocks by distance, one block per wave
-        if (wave < 3) offdiag_block(W, wave + 1, wave);
-        __syncthreads();
-        if (wave < 2) offdiag_block(W, wave + 2, wave);
-        __syncthreads();
-        if (wave == 0) offdiag_block(W, 3, 0);
+        // the off-diagonal blocks, one column per wave
+        if (wave == 0) offdiag_column<0>(W);
+        else if (wave == 1) offdiag_column<1>(W);
+        else if (wave == 2) offdiag_column<2>(W);
         __syncthreads();
         // T' = T diag(beta) fragments
         _Float16* Tw = reinterpret_cast<_Float16*>(wsb + ws.T) + unit_v * kC * kC;
