@@ -75,6 +75,24 @@ def test_prefill_shapes_and_ragged_tails(B, T, Hqk, Hv, dk, dv, bf16):
     assert max_rel(to_host(st), ref["final"]) <= STATE_TOL
 
 
+@pytest.mark.parametrize("alpha_lo,T", [(0.99, 1024), (1.0, 1000)])
+def test_prefill_slow_decay_carries_state_across_chunks(alpha_lo, T):
+    """Gates near or at 1: the state entering a chunk is not damped away within
+    it, so every chunk's output and the final state depend on all earlier
+    chunks (the workload's gates decay by about half per token)."""
+    w = wl.Workload("custom", 1, T, 2, 4, 128, 128)
+    d = wl.make_inputs(w, seed=11)
+    rng = np.random.default_rng(5)
+    d["alpha"] = (alpha_lo + (1.0 - alpha_lo) * rng.random(d["alpha"].shape)).astype(np.float32)
+    d["beta"] = rng.random(d["beta"].shape).astype(np.float32)
+    t = dev_inputs(d)
+    out, st = run_prefill(t)
+    ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], nodes=False)
+    eo, es = max_rel(to_host(out), ref["out"]), max_rel(to_host(st), ref["final"])
+    say(f"slow decay alpha >= {alpha_lo}, T={T}: out {eo:.2e} state {es:.2e}")
+    assert eo <= OUT_TOL and es <= STATE_TOL
+
+
 def test_prefill_resume_equals_one_pass():
     w = wl.Workload("custom", 1, 257, 2, 4, 128, 64)
     d = wl.make_inputs(w, seed=3)
