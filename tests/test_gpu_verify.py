@@ -79,6 +79,28 @@ def test_tree_parity_and_commit():
     assert max_rel(to_host(state), new) <= STATE_TOL
 
 
+@pytest.mark.parametrize("tree", [False, True])
+def test_slow_decay_gates(tree):
+    """Gates in [0.99, 1] and beta in [0, 1]: no node's state is damped toward
+    zero, so every node depends on the cached state and on all its ancestors
+    (the workloads' gates decay by about half per node)."""
+    w, d = small_inputs(33, 2, 22 if tree else 16, 2, 6, 128, 128, tree=tree)
+    rng = np.random.default_rng(6)
+    d["alpha"] = (0.99 + 0.01 * rng.random(d["alpha"].shape)).astype(np.float32)
+    d["beta"] = rng.random(d["beta"].shape).astype(np.float32)
+    t = dev_inputs(d)
+    if tree:
+        out, persist = run_tree(t, d["parent"], w.n_nodes, persist_dtype=torch.float32)
+        ref = oracle.tree(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], d["parent"])
+    else:
+        out, persist, fin = run_chain(t, w.n_nodes, persist_dtype=torch.float32)
+        ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"])
+        assert max_rel(to_host(fin), ref["final"]) <= STATE_TOL
+    e_out, e_p = max_rel(to_host(out), ref["out"]), max_rel(to_host(persist), ref["nodes"])
+    say(f"slow decay {'tree' if tree else 'chain'}: out {e_out:.2e} node states {e_p:.2e}")
+    assert e_out <= OUT_TOL and e_p <= STATE_TOL
+
+
 def test_batched_chain_full_size_sampled():
     """8 sequences x 48 layers in one launch (the benchmark's configuration);
     the oracle checks a sample of whole (sequence x layer) units."""
