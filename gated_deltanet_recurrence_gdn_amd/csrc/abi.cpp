@@ -177,7 +177,7 @@ const char* gdn_status_string(int status) {
         case GDN_ERR_PARENT: return "parent array is not a valid tree";
         case GDN_ERR_NODE: return "accepted node out of range";
         case GDN_ERR_WORKSPACE: return "workspace missing or too small";
-        case GDN_ERR_UNSUPPORTED: return "request not supported by this build";
+        case GDN_ERR_UNSUPPORTED: return "request not supported by this library";
         case GDN_ERR_HIP: return "HIP launch failed";
         case GDN_ERR_SLOT: return "state slot out of range";
         default: return "unknown status";

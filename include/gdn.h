@@ -65,7 +65,7 @@ typedef enum gdn_status {
     GDN_ERR_PARENT = -5,      /* the parent array is not a valid tree */
     GDN_ERR_NODE = -6,        /* device: accepted node outside [0, N) */
     GDN_ERR_WORKSPACE = -7,   /* workspace missing or too small */
-    GDN_ERR_UNSUPPORTED = -8, /* valid request this build does not implement */
+    GDN_ERR_UNSUPPORTED = -8, /* valid request this library does not implement */
     GDN_ERR_HIP = -9,         /* the HIP runtime refused the launch */
     GDN_ERR_SLOT = -10        /* device: state slot outside [0, n_slots) */
 } gdn_status;
