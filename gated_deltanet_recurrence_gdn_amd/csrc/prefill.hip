@@ -696,9 +696,9 @@ __device__ __forceinline__ h8 kt_frag(const unsigned char* blk, int t, int v) {
     return r;
 }
 
-// Output rows staged in LDS per output wave: row t at t * RB + (t / 8) * 32
-// (the skew keeps the four rows one store instruction touches on different
-// banks).
+// Output rows staged in LDS per slice (both output waves stage their halves):
+// row t at t * RB + (t / 8) * 32 (the skew keeps the four rows one store
+// instruction touches on different banks).
 template <int OUT>
 struct OStage {
     static constexpr int ESZ = OUT == 0 ? 4 : 2;
@@ -732,14 +732,16 @@ __device__ __forceinline__ void stage_o(unsigned char* ost, int t, int c, float 
     else *reinterpret_cast<uint16_t*>(p) = f32_to_bf16(o);
 }
 
-// The products of one chunk, split between two waves per 16-column slice so
-// that each runs on its own SIMD:
-//   chain wave:  K H (u-major) | R = V - gamma K H | U = T' R | U -> LDS |
+// The products of one chunk, split so that each wave runs on its own SIMD:
+//   chain wave (one per 16-column slice):
+//                K H (u-major) | R = V - gamma K H | U = T' R | U -> LDS |
 //                barrier | state update (v-major) | next state -> LDS
-//   output wave: Q H (from the state in LDS) | barrier | U <- LDS | O += P U |
-//                outputs staged; it also issues the next chunk's loads.
-// Each wave's steps are one static sequence, each MFMA with its A operand
-// from LDS read D steps ahead; the order is pinned with scheduling barriers.
+//   output wave (one per 32-row half of the chunk, both slices):
+//                Q H (the states from LDS) | barrier | U <- LDS | O += P U |
+//                outputs staged; it also issues the loads of the chunk after next.
+// Each wave's steps are one static sequence (the chain wave's A operands read
+// from LDS D steps ahead, the output wave's from its registers); the order is
+// pinned with scheduling barriers.
 template <int DK>
 struct Plan {
     static constexpr int NT = DK / 16, KB = DK / 32, NP = kC / 16, VB = kC / 32;
