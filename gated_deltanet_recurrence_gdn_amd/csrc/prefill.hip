@@ -60,10 +60,10 @@ __device__ __forceinline__ h8 frag(const _Float16* X, int ld, int row0, int k0, 
 }
 
 __device__ __forceinline__ h8 to_h8(const float (&x)[8]) {
-    h8 r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (_Float16)x[i];
-    return r;
+    // a whole-vector conversion: one packed convert per pair
+    typedef float f8 __attribute__((ext_vector_type(8)));
+    const f8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+    return __builtin_convertvector(v, h8);
 }
 
 // Raw 16-byte loads of 8 elements (bf16 or fp32 source, BF16 fixed at compile
@@ -271,16 +271,17 @@ __device__ __forceinline__ void write_frag(PrepHead& W, const float* gl, _Float1
     if (jt <= it) {
         const float* row = (TPRIME ? W.T(it, jt) : W.P[tix(it, jt)]) + (t & 15) * kTS + (i0 & 15);
         const f32x4 xa = *reinterpret_cast<const f32x4*>(row), xb = *reinterpret_cast<const f32x4*>(row + 4);
+        float x[8];
         if constexpr (TPRIME) {
             const f32x4 ba = *reinterpret_cast<const f32x4*>(gl + kC + i0);
             const f32x4 bb = *reinterpret_cast<const f32x4*>(gl + kC + i0 + 4);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                v[e] = (_Float16)(i0 + e <= t ? (e < 4 ? xa[e] * ba[e] : xb[e - 4] * bb[e - 4]) : 0.f);
+            for (int e = 0; e < 8; ++e) x[e] = i0 + e <= t ? (e < 4 ? xa[e] * ba[e] : xb[e - 4] * bb[e - 4]) : 0.f;
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (_Float16)(e < 4 ? xa[e] : xb[e - 4]);  // zero above the diagonal
+            for (int e = 0; e < 8; ++e) x[e] = e < 4 ? xa[e] : xb[e - 4];  // zero above the diagonal
         }
+        v = to_h8(x);
     } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (_Float16)0.f;
