@@ -967,10 +967,10 @@ struct OutPlaces {
     unsigned char* ost;
 };
 
-template <int DK, int OUT, bool BF16, int NSL>
+template <int DK, int OUT, bool BF16, int NSL, int NB = 3>
 struct ScanLayout;
 
-template <int DK, int OUT, bool BF16, int NSL, int H, int S>
+template <int DK, int OUT, bool BF16, int NSL, int NB, int H, int S>
 __device__ __forceinline__ void out_step(OutRegs<DK, NSL>& x, OutOps<DK, H>& ops, const OutSrc& nsrc,
                                          const unsigned char* blk, const OutPlaces& pl, float scale, const DmaCtx& d) {
     using OP = OutPlan<DK, H>;
@@ -1005,7 +1005,7 @@ __device__ __forceinline__ void out_step(OutRegs<DK, NSL>& x, OutOps<DK, H>& ops
         }
         ops.f[S] = load_out_op<DK, H, S>(nsrc);  // the next chunk's operand
         __builtin_amdgcn_sched_barrier(0);
-        out_step<DK, OUT, BF16, NSL, H, S + 1>(x, ops, nsrc, blk, pl, scale, d);
+        out_step<DK, OUT, BF16, NSL, NB, H, S + 1>(x, ops, nsrc, blk, pl, scale, d);
     } else {
         // O -> staging (written out at the start of the next chunk)
         const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
@@ -1016,9 +1016,9 @@ __device__ __forceinline__ void out_step(OutRegs<DK, NSL>& x, OutOps<DK, H>& ops
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     stage_o<OUT>(pl.ost + q * L::OST, pair_row(2 * H + i, 4 * lg) + r, c, scale * x.o[q][i][r]);
-        // the loads of the chunk after next into LDS, after this chunk's register loads, so
-        // that the next chunk's in-order wait for those leaves these in flight
-        dma_slots<DK, BF16, NSL, 0, NSLOT>(d);
+        // with three blocks, the loads of the chunk after next into LDS, after this chunk's
+        // register loads, so that the next chunk's in-order wait for those leaves these in flight
+        if constexpr (NB == 3) dma_slots<DK, BF16, NSL, 0, NSLOT>(d);
     }
 }
 
@@ -1040,7 +1040,7 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&st)[DK / 16], h8 (&sb)[DK / 
     chain_step<DK, BF16, NSL, 0>(x, st, blk, xc, sl);
 }
 
-template <int DK, int OUT, bool BF16, int NSL, int H>
+template <int DK, int OUT, bool BF16, int NSL, int NB, int H>
 __device__ __forceinline__ void out_chunk(OutOps<DK, H>& ops, const OutSrc& nsrc, const unsigned char* blk,
                                           const OutPlaces& pl, float scale, const DmaCtx& d) {
     using L = ScanLayout<DK, OUT, BF16, NSL>;
@@ -1052,12 +1052,16 @@ __device__ __forceinline__ void out_chunk(OutOps<DK, H>& ops, const OutSrc& nsrc
         for (int u = 0; u < DK / 32; ++u) x.sb[q][u] = get_h8(pl.xc + q * L::XC + Xchg<DK>::SB, u);
         x.o[q][0] = x.o[q][1] = z;
     }
-    out_step<DK, OUT, BF16, NSL, H, 0>(x, ops, nsrc, blk, pl, scale, d);
+    out_step<DK, OUT, BF16, NSL, NB, H, 0>(x, ops, nsrc, blk, pl, scale, d);
 }
 
-template <int DK, int OUT, bool BF16, int NSL>
+// NB LDS blocks for the chain waves' operands: with three, chunk c is in use,
+// c + 1 landed or landing and c + 2 being loaded (one workgroup per CU); with
+// two (two workgroups per CU, for launches of more workgroups than CUs), c + 1
+// is loaded during c.
+template <int DK, int OUT, bool BF16, int NSL, int NB>
 struct ScanLayout {
-    static constexpr int NBUF = 3;  // chunk c in use, c + 1 landed or landing, c + 2 being loaded
+    static constexpr int NBUF = NB;
     static constexpr int BLK = ChunkBlock<DK, BF16, NSL>::BYTES;
     static constexpr int XC = Xchg<DK>::BYTES;
     static constexpr int OST = OStage<OUT>::BYTES;
@@ -1069,28 +1073,34 @@ struct ScanLayout {
 // wait for its loads of the chunk (loads into LDS and registers count as
 // vector-memory operations, which the barrier alone does not wait for) and the
 // barrier that publishes the chunk with the chain waves' starting state.
-template <int DK, int OUT, bool BF16, int NSL, int H>
+template <int DK, int OUT, bool BF16, int NSL, int NB, int H>
 __device__ __forceinline__ void out_wave(const ScanCtx<DK>& X, unsigned char* lds_raw, float scale) {
-    using L = ScanLayout<DK, OUT, BF16, NSL>;
+    using L = ScanLayout<DK, OUT, BF16, NSL, NB>;
     static_assert(NSL == 2 && kC == 64, "two output waves, one per 32-row half of a chunk");
     constexpr int NDMA = ChunkBlock<DK, BF16, NSL>::NLOAD / NSL;  // LDS loads per chunk and output wave
     static_assert(NDMA < 64, "vmcnt field of the top wait");
     const OutPlaces pl = {lds_raw + L::NBUF * L::BLK, lds_raw + L::NBUF * L::BLK + NSL * L::XC};
     OutOps<DK, H> ops;
     load_out_ops<DK, H, 0>(ops, out_src(X, 0));
-    dma_slots<DK, BF16, NSL, 0, NDMA>(dma_ctx<DK, BF16, NSL>(X, 0, lds_raw, H));
-    dma_slots<DK, BF16, NSL, 0, NDMA>(dma_ctx<DK, BF16, NSL>(X, 1, lds_raw + L::BLK, H));
+#pragma unroll
+    for (int c0 = 0; c0 < NB - 1; ++c0)
+        dma_slots<DK, BF16, NSL, 0, NDMA>(dma_ctx<DK, BF16, NSL>(X, c0, lds_raw + c0 * L::BLK, H));
+    // the top wait: with three blocks everything but the last NDMA loads (those of chunk
+    // ck + 1, issued last) has landed; with two, everything
+    constexpr int VMC = NB == 3 ? NDMA : 0;
     for (int ck = 0; ck < X.nch; ++ck) {
-        // everything but the last NDMA loads -- those of chunk ck + 1, issued last -- has
-        // landed: this chunk's LDS block and registers, and the previous chunk's stores
+        // this chunk's LDS block and registers, and the previous chunk's stores, have landed
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt((NDMA & 15) | (NDMA >> 4) << 14 | 0x0070);  // vmcnt(NDMA) lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt((VMC & 15) | (VMC >> 4) << 14 | 0x0070);  // vmcnt(VMC) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (ck > 0) write_out<DK, OUT>(X, pl.ost + H * L::OST, ck - 1, H);
-        // the chunk after next (the last chunks load themselves again into an idle block: harmless)
-        const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + 2, lds_raw + ((ck + 2) % L::NBUF) * L::BLK, H);
-        out_chunk<DK, OUT, BF16, NSL, H>(ops, out_src(X, ck + 1), lds_raw + (ck % L::NBUF) * L::BLK, pl, scale, d);
+        // chunk ck + NB - 1 (the last chunks load themselves again into an idle block: harmless);
+        // with two blocks its loads go out here, a whole chunk ahead of their use
+        const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + NB - 1, lds_raw + ((ck + NB - 1) % NB) * L::BLK, H);
+        if constexpr (NB == 2) dma_slots<DK, BF16, NSL, 0, NDMA>(d);
+        out_chunk<DK, OUT, BF16, NSL, NB, H>(ops, out_src(X, ck + 1), lds_raw + (ck % L::NBUF) * L::BLK, pl, scale,
+                                             d);
     }
     // both output waves' staging of the last chunk is in place
     asm volatile("" ::: "memory");
@@ -1106,9 +1116,9 @@ __device__ __forceinline__ void out_wave(const ScanCtx<DK>& X, unsigned char* ld
 // columns): waves 0 .. NSL-1 are the chain waves of the NSL 16-column slices,
 // waves NSL .. 2 NSL - 1 the output waves (each one half of every slice's
 // output rows).
-template <int DK, int OUT, bool BF16, int NSL>
+template <int DK, int OUT, bool BF16, int NSL, int NB>
 __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillArgs a, const PrefillSeqs seqs) {
-    using L = ScanLayout<DK, OUT, BF16, NSL>;
+    using L = ScanLayout<DK, OUT, BF16, NSL, NB>;
     constexpr int NT = DK / 16;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int lane = threadIdx.x & 63;
@@ -1184,8 +1194,8 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
 #pragma unroll
             for (int r = 0; r < 4; ++r) stp[pair_row(t, 4 * lg) + r] = st[t][r];
     } else {
-        if (sl == 0) out_wave<DK, OUT, BF16, NSL, 0>(X, lds_raw, a.scale);
-        else out_wave<DK, OUT, BF16, NSL, 1>(X, lds_raw, a.scale);
+        if (sl == 0) out_wave<DK, OUT, BF16, NSL, NB, 0>(X, lds_raw, a.scale);
+        else out_wave<DK, OUT, BF16, NSL, NB, 1>(X, lds_raw, a.scale);
     }
 }
 template <typename K>
@@ -1194,17 +1204,42 @@ hipError_t set_lds(K kernel, size_t lds) {
                                (int)lds);
 }
 
+template <int DK, int OUT, bool BF16, int NSL, int NB>
+hipError_t launch_scan_nb(const PrefillArgs& s, const PrefillSeqs& seqs, long long grid, hipStream_t st) {
+    const size_t lds = ScanLayout<DK, OUT, BF16, NSL, NB>::BYTES;
+    hipError_t e = set_lds(&prefill_scan_kernel<DK, OUT, BF16, NSL, NB>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT, BF16, NSL, NB>), dim3((int)grid), dim3(128 * NSL), lds, st, s,
+                       seqs);
+    return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cached[64];
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    if (dev >= 0 && dev < 64) cached[dev] = n;
+    return n;
+}
+
+// Three LDS blocks when the workgroups fit the CUs one each; two (two
+// workgroups per CU, each hiding the other's waits) when there are more
+// workgroups than CUs.
 template <int DK, int OUT, bool BF16, int NSL>
 hipError_t launch_scan_nsl(const PrefillArgs& a, const PrefillSeqs& seqs, hipStream_t st) {
     PrefillArgs s = a;
     s.slices = a.d_v / (16 * NSL);
     const long long grid = (long long)a.batch * a.h_v * s.slices;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    const size_t lds = ScanLayout<DK, OUT, BF16, NSL>::BYTES;
-    hipError_t e = set_lds(&prefill_scan_kernel<DK, OUT, BF16, NSL>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT, BF16, NSL>), dim3((int)grid), dim3(128 * NSL), lds, st, s, seqs);
-    return hipGetLastError();
+    // two blocks pay only where two workgroups then fit a CU's 160 KB of LDS
+    constexpr bool TWO_FIT = 2 * ScanLayout<DK, OUT, BF16, NSL, 2>::BYTES <= 160 * 1024;
+    if constexpr (TWO_FIT) {
+        if (grid > device_cus()) return launch_scan_nb<DK, OUT, BF16, NSL, 2>(s, seqs, grid, st);
+    }
+    return launch_scan_nb<DK, OUT, BF16, NSL, 3>(s, seqs, grid, st);
 }
 
 // Two 16-column slices per workgroup: with four (one fetch of each chunk's

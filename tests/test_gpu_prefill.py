@@ -62,6 +62,7 @@ def test_prefill_full_size_sampled_heads():
     (3, 200, 1, 3, 32, 64),
     (1, 130, 2, 2, 64, 96),
     (1, 300, 1, 1, 128, 256),
+    (2, 300, 16, 48, 128, 128),  # more scan workgroups than CUs: two per CU where they fit
 ])
 @pytest.mark.parametrize("bf16", [True, False])
 def test_prefill_shapes_and_ragged_tails(B, T, Hqk, Hv, dk, dv, bf16):
