@@ -182,6 +182,7 @@ const char* gdn_status_string(int status) {
         case GDN_ERR_UNSUPPORTED: return "request not supported by this library";
         case GDN_ERR_HIP: return "HIP launch failed";
         case GDN_ERR_SLOT: return "state slot out of range";
+        case GDN_ERR_RANGE: return "a prefill value is outside the f16 range";
         default: return "unknown status";
     }
 }

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gdn.h"
 
 namespace gdn {
@@ -13,7 +15,31 @@ namespace gdn {
 constexpr int kMaxNodes = GDN_MAX_NODES;
 constexpr int kTreesPerLaunch = 16;  // tree schedules carried in one kernarg block
 constexpr int kMaxForkSlots = GDN_MAX_TREE_DEPTH - 1;
-constexpr int kMaxLdsBytes = 64 * 1024;
+constexpr int kMaxLdsBytes = 160 * 1024;  // LDS of one gfx950 compute unit, all of it usable by one workgroup
+constexpr int kDefaultLdsBytes = 64 * 1024;  // dynamic LDS a launch may use without the attribute below
+constexpr int kMaxDevices = 64;
+
+// Allows launches of kernel K (a __global__ function) to take up to
+// kMaxLdsBytes of dynamic LDS on the current device.  The attribute is set once
+// per kernel and device; concurrent first calls may both set it (the call is
+// idempotent), and the flag is an atomic, so calls from several host threads
+// are safe.
+template <auto K>
+inline hipError_t allow_max_lds() {
+    static std::atomic<uint64_t> done{0};  // bit d: set on device d
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < kMaxDevices ? uint64_t{1} << dev : 0;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(K), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kMaxLdsBytes);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
+
+// Compute units of the current device, queried once per device (an atomic cache).
+int device_cus();
 
 // One step of a tree walk (depth-first order), packed in 16 bits:
 //   bits 0-4   node index

@@ -82,8 +82,10 @@ __device__ __forceinline__ void raw_load(Raw8& r, const void* base, size_t idx) 
         r.w1 = *reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + idx + 4);
     }
 }
+// `bad` is set when an element is outside the f16 range (|x| > 65504, or not a
+// number): the matrix-core operands would not hold it.
 template <bool BF16>
-__device__ __forceinline__ h8 raw_to_h8(const Raw8& r, bool valid) {
+__device__ __forceinline__ h8 raw_to_h8(const Raw8& r, bool valid, bool& bad) {
     float x[8];
     if constexpr (BF16) {
 #pragma unroll
@@ -102,7 +104,10 @@ __device__ __forceinline__ h8 raw_to_h8(const Raw8& r, bool valid) {
         }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = valid ? x[i] : 0.f;
+    for (int i = 0; i < 8; ++i) {
+        x[i] = valid ? x[i] : 0.f;
+        bad |= !(__builtin_fabsf(x[i]) <= 65504.f);
+    }
     return to_h8(x);
 }
 
@@ -378,14 +383,16 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
             raw_load<BF16>(rk[n], a.k, src);
             raw_load<BF16>(rq[n], a.q, src);
         }
+        bool bad = false;
 #pragma unroll
         for (int n = 0; n < NK; ++n) {
             const int e = tid + 256 * n;
             const int t = e / (DK / 8), d = 8 * (e % (DK / 8));
             const bool valid = t0 + t < sq.T;
-            *reinterpret_cast<h8*>(&Kf[t * kLdK + d]) = raw_to_h8<BF16>(rk[n], valid);
-            *reinterpret_cast<h8*>(&Qf[t * kLdK + d]) = raw_to_h8<BF16>(rq[n], valid);
+            *reinterpret_cast<h8*>(&Kf[t * kLdK + d]) = raw_to_h8<BF16>(rk[n], valid, bad);
+            *reinterpret_cast<h8*>(&Qf[t * kLdK + d]) = raw_to_h8<BF16>(rq[n], valid, bad);
         }
+        if (bad && a.status != nullptr) a.status[0] = GDN_ERR_RANGE;
     }
     // every value head's gates, one head per wave at a time
     for (int j = wave; j < a.group; j += 4) {
@@ -967,7 +974,7 @@ struct OutPlaces {
     unsigned char* ost;
 };
 
-template <int DK, int OUT, bool BF16, int NSL, int NB = 3>
+template <int DK, int OUT, bool BF16, int NSL, int NB>
 struct ScanLayout;
 
 template <int DK, int OUT, bool BF16, int NSL, int NB, int H, int S>
@@ -975,7 +982,7 @@ __device__ __forceinline__ void out_step(OutRegs<DK, NSL>& x, OutOps<DK, H>& ops
                                          const unsigned char* blk, const OutPlaces& pl, float scale, const DmaCtx& d) {
     using OP = OutPlan<DK, H>;
     using CB = ChunkBlock<DK, BF16, NSL>;
-    using L = ScanLayout<DK, OUT, BF16, NSL>;
+    using L = ScanLayout<DK, OUT, BF16, NSL, NB>;
     constexpr int NSLOT = CB::NLOAD / NSL;
     if constexpr (S < OP::B_END) {
         if constexpr (S == OP::B_PU) {
@@ -1043,7 +1050,7 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&st)[DK / 16], h8 (&sb)[DK / 
 template <int DK, int OUT, bool BF16, int NSL, int NB, int H>
 __device__ __forceinline__ void out_chunk(OutOps<DK, H>& ops, const OutSrc& nsrc, const unsigned char* blk,
                                           const OutPlaces& pl, float scale, const DmaCtx& d) {
-    using L = ScanLayout<DK, OUT, BF16, NSL>;
+    using L = ScanLayout<DK, OUT, BF16, NSL, NB>;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     OutRegs<DK, NSL> x;
 #pragma unroll
@@ -1189,40 +1196,31 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
             }
         }
         __syncthreads();  // the output waves' last barrier (their last chunk's staging is complete)
+        // A value outside the f16 range on the way (an input V, a right-hand side R or the
+        // state's f16 copy) makes the state non-finite, and it stays so: report it.
+        bool finite = true;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) stp[pair_row(t, 4 * lg) + r] = st[t][r];
+            for (int r = 0; r < 4; ++r) {
+                finite &= __builtin_isfinite(st[t][r]);
+                stp[pair_row(t, 4 * lg) + r] = st[t][r];
+            }
+        if (!finite && a.status != nullptr) a.status[0] = GDN_ERR_RANGE;
     } else {
         if (sl == 0) out_wave<DK, OUT, BF16, NSL, NB, 0>(X, lds_raw, a.scale);
         else out_wave<DK, OUT, BF16, NSL, NB, 1>(X, lds_raw, a.scale);
     }
 }
-template <typename K>
-hipError_t set_lds(K kernel, size_t lds) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)lds);
-}
-
 template <int DK, int OUT, bool BF16, int NSL, int NB>
 hipError_t launch_scan_nb(const PrefillArgs& s, const PrefillSeqs& seqs, long long grid, hipStream_t st) {
-    const size_t lds = ScanLayout<DK, OUT, BF16, NSL, NB>::BYTES;
-    hipError_t e = set_lds(&prefill_scan_kernel<DK, OUT, BF16, NSL, NB>, lds);
+    constexpr size_t lds = ScanLayout<DK, OUT, BF16, NSL, NB>::BYTES;
+    static_assert(lds <= kMaxLdsBytes, "scan LDS");
+    hipError_t e = allow_max_lds<&prefill_scan_kernel<DK, OUT, BF16, NSL, NB>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_scan_kernel<DK, OUT, BF16, NSL, NB>), dim3((int)grid), dim3(128 * NSL), lds, st, s,
                        seqs);
     return hipGetLastError();
-}
-
-// Compute units of the current device (cached per device).
-int device_cus() {
-    static int cached[64];
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
-    if (dev >= 0 && dev < 64) cached[dev] = n;
-    return n;
 }
 
 // Three LDS blocks when the workgroups fit the CUs one each; two (two
@@ -1253,8 +1251,10 @@ hipError_t launch_scan(const PrefillArgs& a, const PrefillSeqs& seqs, hipStream_
 template <int DK, bool BF16>
 hipError_t launch_dk(const PrefillArgs& a, const PrefillSeqs& seqs, int out_dtype, int prep_grid, hipStream_t st) {
     const size_t lds = PrepLds<DK>::bytes(a.group);
-    hipError_t e = set_lds(&prefill_prepare_kernel<DK, BF16>, lds);
-    if (e != hipSuccess) return e;
+    if (lds > (size_t)kMaxLdsBytes) return hipErrorInvalidValue;
+    hipError_t e = hipSuccess;
+    if (lds > (size_t)kDefaultLdsBytes && (e = allow_max_lds<&prefill_prepare_kernel<DK, BF16>>()) != hipSuccess)
+        return e;
     hipLaunchKernelGGL((prefill_prepare_kernel<DK, BF16>), dim3(prep_grid), dim3(256), lds, st, a, seqs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     switch (out_dtype) {
@@ -1272,6 +1272,17 @@ hipError_t launch_dk_any(const PrefillArgs& a, const PrefillSeqs& seqs, int out_
 }
 
 }  // namespace
+
+int device_cus() {
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    const bool cache = dev >= 0 && dev < kMaxDevices;
+    if (cache && (n = cached[dev].load(std::memory_order_relaxed)) > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    if (cache) cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 size_t prefill_workspace_bytes(long long units, int h_qk, int h_v, int d_k) {
     return ws_layout((size_t)units, h_qk, h_v, d_k).total;

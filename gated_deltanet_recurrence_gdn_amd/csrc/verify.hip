@@ -499,10 +499,10 @@ __global__ __launch_bounds__(256) void commit_verify_chain_kernel(const VerifyAr
     verify_body<DK, M, EPL, kVerifyChain, PMODE, OUT, NT>(a, nullptr, nullptr);
 }
 
-template <int DK, int M, int EPL, int PMODE, int OUT>
+template <int DK, int M, int EPL, int PMODE, int OUT, bool NT>
 __global__ __launch_bounds__(256) void verify_tree_kernel(const VerifyArgs a, const TreeSched t) {
     const int bl = xcd_logical_block(blockIdx.x, gridDim.x) / (a.slices * a.h_v);
-    verify_body<DK, M, EPL, kVerifyTree, PMODE, OUT, true>(a, t.step[a.per_seq_tree ? bl : 0], nullptr);
+    verify_body<DK, M, EPL, kVerifyTree, PMODE, OUT, NT>(a, t.step[a.per_seq_tree ? bl : 0], nullptr);
 }
 
 template <int DK, int M, int EPL, bool NT>
@@ -521,20 +521,29 @@ __global__ __launch_bounds__(256) void replay_verify_chain_kernel(const VerifyAr
     verify_body<DK, M, EPL, kReplayVerifyChain, PMODE, OUT, NT>(a, nullptr, nullptr);
 }
 
+// Launch of kernel K; a launch over 64 KB of LDS first allows K all of it.
+template <auto K, typename... Args>
+hipError_t go(int grid, int waves, size_t lds, hipStream_t st, Args... args) {
+    if (lds > (size_t)kDefaultLdsBytes) {
+        const hipError_t e = allow_max_lds<K>();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(K, dim3(grid), dim3(64 * waves), lds, st, args...);
+    return hipGetLastError();
+}
+
 template <int DK, int M, int EPL, int PMODE, int OUT>
 hipError_t launch_one(const VerifyArgs& a, const TreeSched* t, int waves, size_t lds, int grid, hipStream_t st) {
-    const dim3 g(grid), blk(64 * waves);
+    if (t != nullptr && a.nt_stores)
+        return go<&verify_tree_kernel<DK, M, EPL, PMODE, OUT, true>>(grid, waves, lds, st, a, *t);
     if (t != nullptr)
-        hipLaunchKernelGGL((verify_tree_kernel<DK, M, EPL, PMODE, OUT>), g, blk, lds, st, a, *t);
-    else if (a.accepted_prev != nullptr && a.nt_stores)
-        hipLaunchKernelGGL((commit_verify_chain_kernel<DK, M, EPL, PMODE, OUT, true>), g, blk, lds, st, a);
-    else if (a.accepted_prev != nullptr)
-        hipLaunchKernelGGL((commit_verify_chain_kernel<DK, M, EPL, PMODE, OUT, false>), g, blk, lds, st, a);
-    else if (a.nt_stores)
-        hipLaunchKernelGGL((verify_chain_kernel<DK, M, EPL, PMODE, OUT, true>), g, blk, lds, st, a);
-    else
-        hipLaunchKernelGGL((verify_chain_kernel<DK, M, EPL, PMODE, OUT, false>), g, blk, lds, st, a);
-    return hipGetLastError();
+        return go<&verify_tree_kernel<DK, M, EPL, PMODE, OUT, false>>(grid, waves, lds, st, a, *t);
+    if (a.accepted_prev != nullptr && a.nt_stores)
+        return go<&commit_verify_chain_kernel<DK, M, EPL, PMODE, OUT, true>>(grid, waves, lds, st, a);
+    if (a.accepted_prev != nullptr)
+        return go<&commit_verify_chain_kernel<DK, M, EPL, PMODE, OUT, false>>(grid, waves, lds, st, a);
+    if (a.nt_stores) return go<&verify_chain_kernel<DK, M, EPL, PMODE, OUT, true>>(grid, waves, lds, st, a);
+    return go<&verify_chain_kernel<DK, M, EPL, PMODE, OUT, false>>(grid, waves, lds, st, a);
 }
 
 template <int DK, int M, int EPL, int PMODE>
@@ -558,32 +567,41 @@ hipError_t launch_dkm(const VerifyArgs& a, const TreeSched* t, int pmode, int wa
     }
 }
 
+template <int DK, int M, int EPL, int PM, int OT>
+hipError_t launch_rv(const VerifyArgs& a, int waves, size_t lds, int grid, hipStream_t st) {
+    if (a.nt_stores) return go<&replay_verify_chain_kernel<DK, M, EPL, PM, OT, true>>(grid, waves, lds, st, a);
+    return go<&replay_verify_chain_kernel<DK, M, EPL, PM, OT, false>>(grid, waves, lds, st, a);
+}
+
+template <int DK, int M, int EPL, int PM>
+hipError_t launch_rv_out(const VerifyArgs& a, int waves, size_t lds, int grid, hipStream_t st) {
+    switch (a.out_dtype) {
+        case GDN_F32: return launch_rv<DK, M, EPL, PM, 0>(a, waves, lds, grid, st);
+        case GDN_BF16: return launch_rv<DK, M, EPL, PM, 1>(a, waves, lds, grid, st);
+        case GDN_F16: return launch_rv<DK, M, EPL, PM, 2>(a, waves, lds, grid, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int DK, int M, int EPL>
 hipError_t launch_replay_dkm(const VerifyArgs& a, const TreeParents* tp, int kind, int pmode, int waves, size_t lds,
                              int grid, hipStream_t st) {
-    const dim3 g(grid), blk(64 * waves);
     if (kind == kReplayChain) {
-        if (a.nt_stores) hipLaunchKernelGGL((replay_chain_kernel<DK, M, EPL, true>), g, blk, lds, st, a);
-        else hipLaunchKernelGGL((replay_chain_kernel<DK, M, EPL, false>), g, blk, lds, st, a);
-    } else if (kind == kReplayTree) {
-        if (a.nt_stores) hipLaunchKernelGGL((replay_tree_kernel<DK, M, EPL, true>), g, blk, lds, st, a, *tp);
-        else hipLaunchKernelGGL((replay_tree_kernel<DK, M, EPL, false>), g, blk, lds, st, a, *tp);
-    } else if (kind == kReplayVerifyChain) {
-        // outputs in fp32, f16 or bf16; node states persisted or not (the replay design persists none)
-#define GDN_RV(PM, OT)                                                                                              \
-    do {                                                                                                            \
-        if (a.nt_stores) hipLaunchKernelGGL((replay_verify_chain_kernel<DK, M, EPL, PM, OT, true>), g, blk, lds, st, a); \
-        else hipLaunchKernelGGL((replay_verify_chain_kernel<DK, M, EPL, PM, OT, false>), g, blk, lds, st, a);       \
-    } while (0)
-        const int ot = a.out_dtype == GDN_F32 ? 0 : a.out_dtype == GDN_BF16 ? 1 : 2;
-        if (pmode == 0) { if (ot == 0) GDN_RV(0, 0); else if (ot == 1) GDN_RV(0, 1); else GDN_RV(0, 2); }
-        else if (pmode == 1) { if (ot == 0) GDN_RV(1, 0); else if (ot == 1) GDN_RV(1, 1); else GDN_RV(1, 2); }
-        else { if (ot == 0) GDN_RV(2, 0); else if (ot == 1) GDN_RV(2, 1); else GDN_RV(2, 2); }
-#undef GDN_RV
-    } else {
-        return hipErrorInvalidValue;
+        if (a.nt_stores) return go<&replay_chain_kernel<DK, M, EPL, true>>(grid, waves, lds, st, a);
+        return go<&replay_chain_kernel<DK, M, EPL, false>>(grid, waves, lds, st, a);
     }
-    return hipGetLastError();
+    if (kind == kReplayTree) {
+        if (a.nt_stores) return go<&replay_tree_kernel<DK, M, EPL, true>>(grid, waves, lds, st, a, *tp);
+        return go<&replay_tree_kernel<DK, M, EPL, false>>(grid, waves, lds, st, a, *tp);
+    }
+    if (kind != kReplayVerifyChain) return hipErrorInvalidValue;
+    // outputs in fp32, f16 or bf16; node states persisted or not (the replay design persists none)
+    switch (pmode) {
+        case 0: return launch_rv_out<DK, M, EPL, 0>(a, waves, lds, grid, st);
+        case 1: return launch_rv_out<DK, M, EPL, 1>(a, waves, lds, grid, st);
+        case 2: return launch_rv_out<DK, M, EPL, 2>(a, waves, lds, grid, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace

@@ -6,12 +6,12 @@
  * The recurrence, per (sequence, value head), with S the d_v x d_k state:
  *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
  *     o_t = scale * S_t q_t                     (read after the update)
- * This is the gated delta rule (Yang, Kautz, Hatamizadeh, "Gated Delta
- * Networks: Improving Mamba2 with Delta Rule", ICLR 2025).  The pages
- * describe the layer in words: page "LightSeek's TokenSpeed Hits 580 Tokens
- * per Second on Qwen3.5's 400B Model", section "Why Qwen3.5 is hard to serve
- * fast" (a fixed state of head-dimension-squared size per layer, updated per
- * token, outputs read from the current state).
+ * This is the gated delta rule of a Gated DeltaNet layer, the layer of the
+ * page "LightSeek's TokenSpeed Hits 580 Tokens per Second on Qwen3.5's 400B
+ * Model", section "Why Qwen3.5 is hard to serve fast": a fixed state of
+ * head-dimension-squared size per layer, updated per token, with the output
+ * read from the current state.  The page states it in words; the formula
+ * above is this library's definition of it.
  *
  * Conventions for every entry point
  *  - All tensors are dense, C-contiguous, in device memory, with these
@@ -28,8 +28,11 @@
  *    Value head h reads q/k head h / (h_v / h_qk).
  *  - q, k, v, state, persist and final_state must be 16-byte aligned; the
  *    other pointers 4-byte aligned.
- *  - The caller owns every buffer.  The library allocates no memory, keeps no
- *    mutable global state and is safe to call from several host threads.
+ *  - The caller owns every buffer.  The library allocates no memory and is
+ *    safe to call from several host threads.  Its only host-side state is
+ *    set once per device and never changes afterwards: the compute-unit count
+ *    it reads, and the attribute that lets a kernel use all of a compute
+ *    unit's LDS (both behind atomics).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *    enqueue work on it and return; they never synchronise the host.
  *  - Errors found on the host (null or misaligned pointers, bad shapes or
@@ -67,7 +70,8 @@ typedef enum gdn_status {
     GDN_ERR_WORKSPACE = -7,   /* workspace missing or too small */
     GDN_ERR_UNSUPPORTED = -8, /* valid request this library does not implement */
     GDN_ERR_HIP = -9,         /* the HIP runtime refused the launch */
-    GDN_ERR_SLOT = -10        /* device: state slot outside [0, n_slots) */
+    GDN_ERR_SLOT = -10,       /* device: state slot outside [0, n_slots) */
+    GDN_ERR_RANGE = -11       /* device: a prefill value left the f16 range of the matrix-core operands */
 } gdn_status;
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype;
@@ -276,7 +280,12 @@ int gdn_conv_commit(const gdn_conv_shape* shape, const int32_t* parent, int32_t 
  *
  * q, k [B][T][h_qk][d_k], v [B][T][h_v][d_v] (qkv_dtype F32 or BF16; values
  * are converted to f16 for the matrix cores, so they must lie inside the f16
- * range, and magnitudes below 2^-14 keep an absolute precision of 2^-25);
+ * range, |x| <= 65504, and magnitudes below 2^-14 keep an absolute precision
+ * of 2^-25).  A q or k element outside that range, or a value of the
+ * recurrence that leaves it on the way (from v, the state or the initial
+ * state, which then leaves the final state non-finite), sets *status to
+ * GDN_ERR_RANGE when status is not NULL; the outputs and the state of that
+ * call are then not meaningful;
  * alpha, beta [B][T][h_v] fp32; out [B][T][h_v][d_v] in out_dtype (F32, F16
  * or BF16), 16-byte aligned.  state[slot(b)] holds the initial state on entry and the state
  * after token T-1 on return (updated in place).  A zero alpha resets the state
