@@ -469,6 +469,31 @@ int check_prefill(const gdn_shape* sh) {
 }
 }  // namespace
 
+}  // extern "C"
+
+namespace gdn {
+int check_prefill_call(const gdn_shape* sh, const void* q, const void* k, const void* v, const float* alpha,
+                       const float* beta, const float* state, const int32_t* state_slot, const void* out,
+                       bool* empty) {
+    *empty = false;
+    const int rc = check_prefill(sh);
+    if (rc != GDN_OK) return rc;
+    if (state_slot != nullptr && sh->n_slots < 1) return GDN_ERR_SHAPE;
+    if (sh->batch == 0 || sh->n_nodes == 0) {
+        *empty = true;
+        return GDN_OK;
+    }
+    if ((long long)sh->batch * sh->n_nodes > 0x7fffffffLL) return GDN_ERR_SHAPE;
+    if (!q || !k || !v || !alpha || !beta || !state || !out) return GDN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return GDN_ERR_ALIGN;
+    if (!aligned(alpha, 4) || !aligned(beta, 4) || !aligned(state, 4) || !aligned(state_slot, 4))
+        return GDN_ERR_ALIGN;
+    return GDN_OK;
+}
+}  // namespace gdn
+
+extern "C" {
+
 size_t gdn_prefill_workspace_bytes(const gdn_shape* shape) {
     if (check_prefill(shape) != GDN_OK || shape->batch == 0 || shape->n_nodes == 0) return 0;
     const long long units = (long long)shape->batch * ((shape->n_nodes + GDN_PREFILL_CHUNK - 1) / GDN_PREFILL_CHUNK);
@@ -478,16 +503,10 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape* shape) {
 int gdn_prefill_chunked(const gdn_shape* shape, const void* q, const void* k, const void* v,
                         const float* alpha, const float* beta, float* state, const int32_t* state_slot,
                         void* out, void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
-    int rc = check_prefill(shape);
-    if (rc != GDN_OK) return rc;
+    bool empty = false;
+    const int rc = gdn::check_prefill_call(shape, q, k, v, alpha, beta, state, state_slot, out, &empty);
+    if (rc != GDN_OK || empty) return rc;
     const gdn_shape* sh = shape;
-    if (state_slot != nullptr && sh->n_slots < 1) return GDN_ERR_SHAPE;
-    if (sh->batch == 0 || sh->n_nodes == 0) return GDN_OK;
-    if ((long long)sh->batch * sh->n_nodes > 0x7fffffffLL) return GDN_ERR_SHAPE;
-    if (!q || !k || !v || !alpha || !beta || !state || !out) return GDN_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return GDN_ERR_ALIGN;
-    if (!aligned(alpha, 4) || !aligned(beta, 4) || !aligned(state, 4) || !aligned(state_slot, 4))
-        return GDN_ERR_ALIGN;
     const size_t need = gdn_prefill_workspace_bytes(sh);
     if (workspace == nullptr || workspace_bytes < need) return GDN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return GDN_ERR_ALIGN;
@@ -579,11 +598,12 @@ int gdn_prefill_varlen(const gdn_shape* shape, const int32_t* cu_seqlens, const 
         std::memset(&seqs, 0, sizeof(seqs));
         long long units = 0;
         for (int i = 0; i <= ns; ++i) {
-            seqs.tok0[i] = cu_seqlens[s0 + i];
             seqs.unit0[i] = (int32_t)units;
             seqs.cst0[i] = (int32_t)cst;
             if (i < ns) {
                 const int T = cu_seqlens[s0 + i + 1] - cu_seqlens[s0 + i];
+                seqs.tok0[i] = cu_seqlens[s0 + i];
+                seqs.len[i] = T;
                 units += chunks_of(T);
                 cst += T / span;
             }

@@ -161,11 +161,15 @@ struct ConvArgs {
 };
 
 // Per-sequence tables of a varlen prefill launch (up to kMaxPrefillSeqs
-// sequences): first token, first chunk unit (workspace block) and first
-// emitted boundary state of each sequence, each with one past-the-end entry.
+// sequences): first token in the packed token dimension and token count (the
+// launch covers tokens tok0 .. tok0 + len - 1 of each sequence; a launch may
+// cover a chunk-aligned middle part of a longer sequence), first chunk unit
+// (workspace block) and first emitted boundary state, the last two with one
+// past-the-end entry.
 constexpr int kMaxPrefillSeqs = 64;
 struct PrefillSeqs {
-    int32_t tok0[kMaxPrefillSeqs + 1];
+    int32_t tok0[kMaxPrefillSeqs];
+    int32_t len[kMaxPrefillSeqs];
     int32_t unit0[kMaxPrefillSeqs + 1];
     int32_t cst0[kMaxPrefillSeqs + 1];
 };
@@ -218,6 +222,11 @@ hipError_t launch_replay(const VerifyArgs& a, const TreeParents* parents, int ki
 // (sequence, value head, 32 value columns) then walks the chunks.  `units` is
 // the number of 64-token chunk units of the launch (one workspace block each).
 size_t prefill_workspace_bytes(long long units, int h_qk, int h_v, int d_k);
+// The host checks of a chunked prefill call (shape, pointers, alignment); *empty
+// is set for a call with no tokens or no sequences (nothing to launch).
+int check_prefill_call(const gdn_shape* sh, const void* q, const void* k, const void* v, const float* alpha,
+                       const float* beta, const float* state, const int32_t* state_slot, const void* out,
+                       bool* empty);
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillSeqs& seqs, int d_k, int out_dtype, hipStream_t stream);
 
 hipError_t launch_commit(const CommitArgs& a, bool persist_f16, int grid, int block,

@@ -153,7 +153,7 @@ __device__ __forceinline__ SeqInfo seq_info(const PrefillArgs& a, const PrefillS
     SeqInfo q;
     if (a.varlen) {
         q.tok0 = t.tok0[b];
-        q.T = t.tok0[b + 1] - q.tok0;
+        q.T = t.len[b];
         q.unit0 = t.unit0[b];
         q.nch = t.unit0[b + 1] - q.unit0;
         q.cst0 = t.cst0[b];
