@@ -30,6 +30,7 @@ GDN_MAX_TREE_DEPTH = 16
 GDN_PREFILL_CHUNK = 64
 GDN_MAX_CONV_WIDTH = 8
 GDN_F16_MAX = 65504.0
+GDN_PREFILL_SCRATCH_BYTES = 32 << 20
 
 STATUS = {
     0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE", -4: "GDN_ERR_ALIGN",
@@ -76,6 +77,7 @@ _SIGS = {
     "gdn_prefill_varlen_workspace_bytes": [ctypes.POINTER(GdnShape), _vp],
     "gdn_prefill_boundary_states": [_vp, _i32, _i32],
     "gdn_prefill_varlen": [ctypes.POINTER(GdnShape)] + [_vp] * 10 + [_i32, _vp, ctypes.c_size_t, _vp, _vp],
+    "gdn_prefill_chunked_noalloc": [ctypes.POINTER(GdnShape)] + [_vp] * 10,
 }
 _RESTYPES = {"gdn_status_string": ctypes.c_char_p, "gdn_prefill_workspace_bytes": ctypes.c_size_t,
              "gdn_prefill_varlen_workspace_bytes": ctypes.c_size_t, "gdn_prefill_boundary_states": ctypes.c_int64}
@@ -444,6 +446,19 @@ def gdn_prefill_chunked(q, k, v, alpha, beta, state, out, *, state_slot=None, st
             _dev_ptr(status, "status"), _stream(stream))
     return _invoke("gdn_prefill_chunked", args, (sh, q, k, v, alpha, beta, state, state_slot, out, workspace,
                                                  status), prepare)
+
+
+def gdn_prefill_chunked_noalloc(q, k, v, alpha, beta, state, out, *, state_slot=None, status=None,
+                                scale: float = 1.0, stream=None, prepare: bool = False):
+    """Chunked prefill that allocates nothing: the per-chunk operands go to the
+    library's static per-GPU scratch array (see include/gdn.h).  Calls that may
+    overlap on one GPU race."""
+    sh = _prefill_shape(q, k, v, alpha, beta, state, state_slot, out, status, scale)
+    args = (ctypes.byref(sh), _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(alpha, "alpha"),
+            _dev_ptr(beta, "beta"), _dev_ptr(state, "state"), _dev_ptr(state_slot, "state_slot"),
+            _dev_ptr(out, "out"), _dev_ptr(status, "status"), _stream(stream))
+    return _invoke("gdn_prefill_chunked_noalloc", args, (sh, q, k, v, alpha, beta, state, state_slot, out, status),
+                   prepare)
 
 
 def _host_cu(cu_seqlens) -> np.ndarray:

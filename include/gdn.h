@@ -310,6 +310,27 @@ int gdn_prefill_chunked(const gdn_shape* shape, const void* q, const void* k, co
                         size_t workspace_bytes, int32_t* status, void* stream);
 
 /*
+ * gdn_prefill_chunked for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument.  The per-chunk operands go to a static
+ * array of this library, GDN_PREFILL_SCRATCH_BYTES per GPU, which each GPU the
+ * library runs on holds until the process ends.  A prompt whose workspace
+ * (gdn_prefill_workspace_bytes) exceeds the array is processed in segments of
+ * whole 64-token chunks, each a launch pair that reuses it; the results are
+ * bit for bit those of gdn_prefill_chunked.  Heads so large that one 64-token
+ * chunk does not fit return GDN_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU uses the same array: calls that may overlap on one GPU
+ * (on different streams, or from several host threads without ordering) race
+ * and must not be issued.  The call allocates nothing: no hipMalloc, hipFree
+ * or allocating library routine.  Other arguments, limits and errors as
+ * gdn_prefill_chunked.
+ */
+#define GDN_PREFILL_SCRATCH_BYTES (32u << 20)
+int gdn_prefill_chunked_noalloc(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, float* state, const int32_t* state_slot,
+                                void* out, int32_t* status, void* stream);
+
+/*
  * Varlen batched prefill with chunk-boundary states.  The same recurrence
  * and chunked evaluation as gdn_prefill_chunked, for `batch` sequences of
  * different lengths packed one after another along the token dimension, in

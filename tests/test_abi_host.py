@@ -332,3 +332,21 @@ def test_prefill_boundary_state_count():
     assert L.gdn_prefill_boundary_states(cu.ctypes.data, 5, 0) == -1
     bad = np.array([0, 10, 5], np.int32)
     assert L.gdn_prefill_boundary_states(bad.ctypes.data, 2, 1) == -1
+
+
+def test_prefill_noalloc_rejects_heads_beyond_its_array_on_the_host():
+    """The no-allocation prefill refuses a request whose single 64-token chunk
+    needs more than its static array, before any HIP call; other checks are
+    those of gdn_prefill_chunked."""
+    L = gb.lib()
+
+    def call(sh, q=FAKE):
+        return L.gdn_prefill_chunked_noalloc(ctypes.byref(sh), q, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None)
+
+    P = dict(batch=1, n_nodes=64, h_qk=16, d_k=128, d_v=32)
+    assert call(shape(**P, h_v=2048)) == E["GDN_ERR_WORKSPACE"]
+    per_unit = L.gdn_prefill_workspace_bytes(ctypes.byref(shape(**{**P, "h_v": 2048})))
+    assert per_unit > gb.GDN_PREFILL_SCRATCH_BYTES
+    assert call(shape(**P, h_v=48), q=None) == E["GDN_ERR_NULL"]
+    assert call(shape(**P, h_v=47)) == E["GDN_ERR_SHAPE"]
+    assert call(shape(**{**P, "n_nodes": 0}, h_v=48)) == E["GDN_OK"]
