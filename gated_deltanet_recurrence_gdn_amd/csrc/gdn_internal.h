@@ -104,7 +104,8 @@ struct TreeParents {
 
 // What a verify-family launch does.
 enum VerifyKind : int {
-    kVerifyChain = 0,        // chain verify (with the fused persisted-copy commit when accepted_prev is set)
+    kVerifyChain = 0,        // chain verify
+    kCommitVerifyChain = 5,  // the persisted-copy commit of the previous block fused into a chain verify
     kVerifyTree = 1,         // tree verify, host-planned depth-first walk
     kReplayChain = 2,        // commit by replay of nodes 0 .. accepted
     kReplayTree = 3,         // commit by replay of the accepted node's root path

@@ -104,64 +104,109 @@ struct StageArea {
     }
 };
 
-// Stage every node's inputs of NB blocks.  One pass issues all of a thread's
-// global loads (k and q chunks, beta * v, the gates; of every block) before
-// any LDS store, so the common case (N * d_k / 8 <= threads) costs one memory
-// round trip.  `walk` (tree verify only) goes to block 0's walk area.
+// Staging of every node's inputs of NB blocks into LDS, one item per lane: an
+// 8-element chunk of k and of q, one beta * v entry and one node's gates (of
+// every block).  A lane's global loads are unconditional (indices clamped into
+// range, the dtype entering only through addresses) and converted only when
+// stored, so they all issue back to back and cost one memory round trip; the
+// first item of every lane is loaded before the state rows (which may wait on
+// the slot and accepted-node lookups) and stored after them, so that round
+// trip overlaps the state's.  `walk` (tree verify only) goes to block 0's walk
+// area.
+template <int NB>
+struct StageRegs {
+    u32x4 k[NB][2], q[NB][2];  // bf16: the 8 elements in [0] ([1] repeats it); fp32: 4 in each
+    uint32_t v[NB];            // the 32-bit word holding v (bf16: one of its halves)
+    float vbeta[NB], ga[NB], gb[NB];
+    bool v_hi;                 // bf16 v in the upper half of its word
+};
+
+template <int DK>
+struct StageItem {
+    int e, chunks, nvb, N;
+    __device__ bool kq() const { return e < chunks; }
+    __device__ bool v() const { return e < nvb; }
+    __device__ bool g() const { return e < N; }
+};
+
 template <int DK, int NB>
-__device__ __forceinline__ void stage_blocks(const StageArea<DK> (&sa)[2], const BlockIn (&in)[2],
-                                             const VerifyArgs& a, int b, int h, int g, int row0,
-                                             const uint16_t* walk) {
+__device__ __forceinline__ void stage_load(StageRegs<NB>& r, const StageItem<DK>& it, const BlockIn (&in)[2],
+                                           const VerifyArgs& a, int b, int h, int g, int row0) {
     constexpr int LPR = DK / 8;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = blockDim.x;
     const int N = a.n_nodes, rows = a.rows_per_wg, DV = a.d_v;
     const bool bf16 = a.qkv_bf16 != 0;
-    const int chunks = N * LPR;  // 8-element chunks of k (and of q)
-    const int nvb = N * rows;
-    const int items = chunks > nvb ? chunks : nvb;
-    for (int base = wave * 64; base < items; base += nthr) {
-        const int e = base + lane;
-        const bool has_kq = e < chunks, has_v = e < nvb, has_g = e < N;
-        float kf[NB][8], qf[NB][8], vv[NB], vbeta[NB], ga[NB], gb[NB];
+    const size_t esz = bf16 ? 2 : 4;
+    const int ekq = it.e < it.chunks ? it.e : it.chunks - 1;
+    const int ev = it.e < it.nvb ? it.e : it.nvb - 1;
+    const int eg = it.e < it.N ? it.e : it.N - 1;
+    const size_t kqi = (((size_t)b * N + ekq / LPR) * a.h_qk + g) * DK + 8 * (ekq % LPR);
+    const int n = ev / rows;
+    const size_t vi = (((size_t)b * N + n) * a.h_v + h) * DV + row0 + ev % rows;
+    const size_t vb = bf16 ? (vi * 2) & ~(size_t)3 : vi * 4;
+    r.v_hi = bf16 && (vi & 1);
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            vv[i] = vbeta[i] = ga[i] = gb[i] = 0.f;
-            if (has_kq) {
-                const size_t src = (((size_t)b * N + e / LPR) * a.h_qk + g) * DK + 8 * (e % LPR);
-                load8_as_f32(in[i].k, src, bf16, kf[i]);
-                load8_as_f32(in[i].q, src, bf16, qf[i]);
-            }
-            if (has_v) {
-                const int n = e / rows, j = e % rows;
-                vv[i] = load1_as_f32(in[i].v, (((size_t)b * N + n) * a.h_v + h) * DV + row0 + j, bf16);
-                vbeta[i] = in[i].beta[((size_t)b * N + n) * a.h_v + h];
-            }
-            if (has_g) {
-                ga[i] = in[i].alpha[((size_t)b * N + e) * a.h_v + h];
-                gb[i] = in[i].beta[((size_t)b * N + e) * a.h_v + h];
-            }
+    for (int i = 0; i < NB; ++i) {
+        const unsigned char* kp = static_cast<const unsigned char*>(in[i].k) + kqi * esz;
+        const unsigned char* qp = static_cast<const unsigned char*>(in[i].q) + kqi * esz;
+        r.k[i][0] = *reinterpret_cast<const u32x4*>(kp);
+        r.k[i][1] = *reinterpret_cast<const u32x4*>(kp + (bf16 ? 0 : 16));
+        r.q[i][0] = *reinterpret_cast<const u32x4*>(qp);
+        r.q[i][1] = *reinterpret_cast<const u32x4*>(qp + (bf16 ? 0 : 16));
+        r.v[i] = *reinterpret_cast<const uint32_t*>(static_cast<const unsigned char*>(in[i].v) + vb);
+        r.vbeta[i] = in[i].beta[((size_t)b * N + n) * a.h_v + h];
+        r.ga[i] = in[i].alpha[((size_t)b * N + eg) * a.h_v + h];
+        r.gb[i] = in[i].beta[((size_t)b * N + eg) * a.h_v + h];
+    }
+}
+
+__device__ __forceinline__ void raw8_to_f32(const u32x4 (&w)[2], bool bf16, float (&x)[8]) {
+    if (bf16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(w[0][i]);
+            x[2 * i + 1] = bf16_hi(w[0][i]);
         }
+    } else {
+        const f32x4 lo = __builtin_bit_cast(f32x4, w[0]), hi = __builtin_bit_cast(f32x4, w[1]);
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            float part = 0.f;
-            if (has_kq) {
-                float* kd = sa[i].kL + (e / LPR) * DK + 8 * (e % LPR);
-                float* qd = sa[i].qL + (e / LPR) * DK + 8 * (e % LPR);
-                *reinterpret_cast<f32x4*>(kd) = f32x4{kf[i][0], kf[i][1], kf[i][2], kf[i][3]};
-                *reinterpret_cast<f32x4*>(kd + 4) = f32x4{kf[i][4], kf[i][5], kf[i][6], kf[i][7]};
-                *reinterpret_cast<f32x4*>(qd) = f32x4{qf[i][0], qf[i][1], qf[i][2], qf[i][3]};
-                *reinterpret_cast<f32x4*>(qd + 4) = f32x4{qf[i][4], qf[i][5], qf[i][6], qf[i][7]};
+        for (int i = 0; i < 4; ++i) {
+            x[i] = lo[i];
+            x[4 + i] = hi[i];
+        }
+    }
+}
+
+template <int DK, int NB>
+__device__ __forceinline__ void stage_store(const StageRegs<NB>& r, const StageItem<DK>& it, bool bf16,
+                                            const StageArea<DK> (&sa)[2], const uint16_t* walk) {
+    constexpr int LPR = DK / 8;
+    const int e = it.e;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) part = fmaf(kf[i][j], qf[i][j], part);
-            }
-            part = group_sum<LPR>(part);
-            if (has_kq && (e % LPR) == 0) reinterpret_cast<float*>(sa[i].cL + e / LPR)[2] = part;
-            if (has_v) sa[i].vbL[e] = vbeta[i] * vv[i];
-            if (has_g) {
-                reinterpret_cast<float*>(sa[i].cL + e)[0] = ga[i];
-                reinterpret_cast<float*>(sa[i].cL + e)[1] = gb[i];
-                if (i == 0 && walk != nullptr) sa[0].walkL[e] = walk[e];
-            }
+    for (int i = 0; i < NB; ++i) {
+        float kf[8], qf[8];
+        raw8_to_f32(r.k[i], bf16, kf);
+        raw8_to_f32(r.q[i], bf16, qf);
+        float part = 0.f;
+        if (it.kq()) {
+            float* kd = sa[i].kL + (e / LPR) * DK + 8 * (e % LPR);
+            float* qd = sa[i].qL + (e / LPR) * DK + 8 * (e % LPR);
+            *reinterpret_cast<f32x4*>(kd) = f32x4{kf[0], kf[1], kf[2], kf[3]};
+            *reinterpret_cast<f32x4*>(kd + 4) = f32x4{kf[4], kf[5], kf[6], kf[7]};
+            *reinterpret_cast<f32x4*>(qd) = f32x4{qf[0], qf[1], qf[2], qf[3]};
+            *reinterpret_cast<f32x4*>(qd + 4) = f32x4{qf[4], qf[5], qf[6], qf[7]};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) part = fmaf(kf[j], qf[j], part);
+        }
+        part = group_sum<LPR>(part);
+        if (it.kq() && (e % LPR) == 0) reinterpret_cast<float*>(sa[i].cL + e / LPR)[2] = part;
+        if (it.v()) {
+            const float vv = !bf16 ? __builtin_bit_cast(float, r.v[i]) : r.v_hi ? bf16_hi(r.v[i]) : bf16_lo(r.v[i]);
+            sa[i].vbL[e] = r.vbeta[i] * vv;
+        }
+        if (it.g()) {
+            reinterpret_cast<float*>(sa[i].cL + e)[0] = r.ga[i];
+            reinterpret_cast<float*>(sa[i].cL + e)[1] = r.gb[i];
+            if (i == 0 && walk != nullptr) sa[0].walkL[e] = walk[e];
         }
     }
 }
@@ -360,10 +405,12 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
     constexpr bool TREE = KIND == kVerifyTree;
     constexpr bool REPLAY = KIND == kReplayChain || KIND == kReplayTree || KIND == kReplayVerifyChain;
     constexpr int NB = KIND == kReplayVerifyChain ? 2 : 1;  // staged blocks
+    constexpr bool FUSED = KIND == kCommitVerifyChain;       // the commit is part of the state load
+    constexpr bool HAS_ACC = FUSED || REPLAY;                // an accepted node is read per sequence
     extern __shared__ __align__(16) float lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nwaves = blockDim.x >> 6;
+    const int nwaves = a.rows_per_wg / R;  // the launch's block is 64 nwaves threads
 
     int blk = xcd_logical_block(blockIdx.x, gridDim.x);
     const int slice = blk % a.slices;
@@ -377,6 +424,23 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
     const int rows = a.rows_per_wg;
     const int row0 = slice * rows;
 
+    // 2a. the first staging item of this lane: global loads issued before the state's
+    // (and before the slot and accepted-node lookups the state load waits on)
+    const BlockIn in[2] = {{KIND == kReplayVerifyChain ? a.rq : a.q, KIND == kReplayVerifyChain ? a.rk : a.k,
+                            KIND == kReplayVerifyChain ? a.rv : a.v, KIND == kReplayVerifyChain ? a.ralpha : a.alpha,
+                            KIND == kReplayVerifyChain ? a.rbeta : a.beta},
+                           {a.q, a.k, a.v, a.alpha, a.beta}};
+    const uint16_t* stage_walk = TREE ? walk : nullptr;
+    StageItem<DK> item;
+    item.chunks = N * (DK / 8);
+    item.nvb = N * rows;
+    item.N = N;
+    item.e = wave * 64 + lane;
+    const int items = item.chunks > item.nvb ? item.chunks : item.nvb;
+    StageRegs<NB> sr;
+    stage_load<DK, NB>(sr, item, in, a, b, h, g, row0);
+
+
     int s = b;
     if (a.state_slot != nullptr) {
         s = a.state_slot[b];
@@ -387,7 +451,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
     }
     // the accepted node of the committed block (fused commit or replay) must be in range
     int acc = 0;
-    if (a.accepted_prev != nullptr) {
+    if constexpr (HAS_ACC) {
         acc = a.accepted_prev[b];
         if (acc < 0 || acc >= N) {
             if (tid == 0 && a.status != nullptr) a.status[0] = GDN_ERR_NODE;
@@ -400,7 +464,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
     const StageArea<DK> sa[2] = {StageArea<DK>(lds, N, rows), StageArea<DK>(lds + stage_floats, N, rows)};
     float* forkL = lds + NB * stage_floats;
 
-    // 1. this wave's state rows -> VGPRs (issued first; the loads overlap staging)
+    // 1. this wave's state rows -> VGPRs
     LaneRows L;
     L.b = b;
     L.h = h;
@@ -412,7 +476,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
     float S[M][EPL];
     float* cache_head = (a.state_w != nullptr ? a.state_w : const_cast<float*>(a.state)) +
                         ((size_t)s * a.h_v + h) * head_elems;
-    if (KIND != kVerifyChain || a.accepted_prev == nullptr) {
+    if constexpr (!FUSED) {
         load_rows<DK, M, EPL>(S, a.state + ((size_t)s * a.h_v + h) * head_elems, L);
     } else {
         // Commit while loading: the initial state is the previous step's accepted node
@@ -439,13 +503,14 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
         store_state_rows<DK, M, EPL, NT>(cache_head, L, S);
     }
 
-    // 2. stage every node's inputs (both blocks of a replay + verify)
-    if constexpr (KIND == kReplayVerifyChain) {
-        const BlockIn in[2] = {{a.rq, a.rk, a.rv, a.ralpha, a.rbeta}, {a.q, a.k, a.v, a.alpha, a.beta}};
-        stage_blocks<DK, 2>(sa, in, a, b, h, g, row0, nullptr);
-    } else {
-        const BlockIn in[2] = {{a.q, a.k, a.v, a.alpha, a.beta}, {a.q, a.k, a.v, a.alpha, a.beta}};
-        stage_blocks<DK, 1>(sa, in, a, b, h, g, row0, TREE ? walk : nullptr);
+    // 2b. stage every node's inputs (both blocks of a replay + verify): the first item
+    // loaded above, then any further ones (when N * d_k / 8 exceeds the threads)
+    stage_store<DK, NB>(sr, item, a.qkv_bf16 != 0, sa, stage_walk);
+    for (int base = wave * 64 + 64 * nwaves; base < items; base += 64 * nwaves) {  // wave-uniform bound
+        StageItem<DK> it = item;
+        it.e = base + lane;
+        stage_load<DK, NB>(sr, it, in, a, b, h, g, row0);
+        stage_store<DK, NB>(sr, it, a.qkv_bf16 != 0, sa, stage_walk);
     }
     // a tree replay runs the accepted node's root path, root first
     int n_steps = N;
@@ -492,11 +557,11 @@ __global__ __launch_bounds__(256) void verify_chain_kernel(const VerifyArgs a) {
     verify_body<DK, M, EPL, kVerifyChain, PMODE, OUT, NT>(a, nullptr, nullptr);
 }
 
-// The fused commit + verify launch: the same body, under its own symbol so kernel
-// traces and counters tell it apart from a plain verify.
+// The fused commit + verify launch: the same body with the commit in its state
+// load (a compile-time kind, so the plain verify waits on no commit store).
 template <int DK, int M, int EPL, int PMODE, int OUT, bool NT>
 __global__ __launch_bounds__(256) void commit_verify_chain_kernel(const VerifyArgs a) {
-    verify_body<DK, M, EPL, kVerifyChain, PMODE, OUT, NT>(a, nullptr, nullptr);
+    verify_body<DK, M, EPL, kCommitVerifyChain, PMODE, OUT, NT>(a, nullptr, nullptr);
 }
 
 template <int DK, int M, int EPL, int PMODE, int OUT, bool NT>
