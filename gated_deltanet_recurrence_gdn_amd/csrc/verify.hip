@@ -253,6 +253,53 @@ __device__ __forceinline__ void store_state_rows(float* head_base, const LaneRow
         }
 }
 
+// The state rows a lane holds, loaded raw (16-byte words, unconditionally, the
+// element type entering only through addresses) and widened to fp32 later, so
+// the loads are in flight while the wave does other work.  F16: the eight
+// elements of a chunk in w[..][0] (w[..][1] repeats it); fp32: four in each.
+template <int M, int EPL>
+struct RowsRaw {
+    u32x4 w[M][EPL / 8][2];
+};
+
+template <int DK, int M, int EPL>
+__device__ __forceinline__ void load_rows_raw(RowsRaw<M, EPL>& r, const void* head_base, bool f16,
+                                              const LaneRows& L) {
+    constexpr int LPR = DK / EPL, RPG = 64 / LPR;
+    const size_t esz = f16 ? 2 : 4;
+    const unsigned char* src = static_cast<const unsigned char*>(head_base) +
+                               ((size_t)(L.row0 + L.wrow + L.r) * DK + 8 * L.c) * esz;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int j = 0; j < EPL / 8; ++j) {
+            const unsigned char* p = src + ((size_t)m * RPG * DK + 8 * LPR * j) * esz;
+            r.w[m][j][0] = *reinterpret_cast<const u32x4*>(p);
+            r.w[m][j][1] = *reinterpret_cast<const u32x4*>(p + (f16 ? 0 : 16));
+        }
+}
+
+template <int M, int EPL>
+__device__ __forceinline__ void widen_rows(float (&S)[M][EPL], const RowsRaw<M, EPL>& r, bool f16) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int j = 0; j < EPL / 8; ++j) {
+            if (f16) {
+                const f16x8 hv = __builtin_bit_cast(f16x8, r.w[m][j][0]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) S[m][8 * j + e] = (float)hv[e];
+            } else {
+                const f32x4 lo = __builtin_bit_cast(f32x4, r.w[m][j][0]), hi = __builtin_bit_cast(f32x4, r.w[m][j][1]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    S[m][8 * j + e] = lo[e];
+                    S[m][8 * j + 4 + e] = hi[e];
+                }
+            }
+        }
+}
+
 // The node loop over n_steps steps of one staged block: per step the optional
 // fork restore, the two row reductions, the update, the persisted copy, the
 // output, the optional fork save.  CODES: step st runs node walk[st] with its
@@ -473,35 +520,26 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
     L.r = lane / LPR;
     L.wrow = wave * R;  // first row of this wave inside the slice
     const size_t head_elems = (size_t)DV * DK;
-    float S[M][EPL];
     float* cache_head = (a.state_w != nullptr ? a.state_w : const_cast<float*>(a.state)) +
                         ((size_t)s * a.h_v + h) * head_elems;
-    if constexpr (!FUSED) {
-        load_rows<DK, M, EPL>(S, a.state + ((size_t)s * a.h_v + h) * head_elems, L);
-    } else {
-        // Commit while loading: the initial state is the previous step's accepted node
-        // (its exact fp32 final state when the whole block was accepted, else its persisted
-        // copy widened to fp32); it is also written back to the state cache.
+    // The starting state: the cached state, or (fused commit) the previous step's accepted
+    // node -- its exact fp32 final state when the whole block was accepted, else its
+    // persisted copy, widened to fp32 -- which is also written back to the state cache.
+    // Its loads are issued first; the staging's LDS work runs while they are in flight.
+    const void* src_head = a.state + ((size_t)s * a.h_v + h) * head_elems;
+    bool src_f16 = false;
+    if constexpr (FUSED) {
         if (a.final_prev != nullptr && acc == N - 1) {
-            load_rows<DK, M, EPL>(S, a.final_prev + ((size_t)b * a.h_v + h) * head_elems, L);
-        } else if (a.persist_prev_f16) {
-            const _Float16* src = static_cast<const _Float16*>(a.persist_prev) +
-                                  (((size_t)b * N + acc) * a.h_v + h) * head_elems +
-                                  (size_t)(row0 + L.wrow + L.r) * DK + 8 * L.c;
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int j = 0; j < EPL / 8; ++j) {
-                    const f16x8 hv = *reinterpret_cast<const f16x8*>(src + (size_t)m * RPG * DK + 8 * LPR * j);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) S[m][8 * j + e] = (float)hv[e];
-                }
+            src_head = a.final_prev + ((size_t)b * a.h_v + h) * head_elems;
         } else {
-            load_rows<DK, M, EPL>(S, static_cast<const float*>(a.persist_prev) +
-                                         (((size_t)b * N + acc) * a.h_v + h) * head_elems, L);
+            src_f16 = a.persist_prev_f16 != 0;
+            const size_t off = (((size_t)b * N + acc) * a.h_v + h) * head_elems;
+            src_head = src_f16 ? static_cast<const void*>(static_cast<const _Float16*>(a.persist_prev) + off)
+                               : static_cast<const void*>(static_cast<const float*>(a.persist_prev) + off);
         }
-        store_state_rows<DK, M, EPL, NT>(cache_head, L, S);
     }
+    RowsRaw<M, EPL> raw;
+    load_rows_raw<DK, M, EPL>(raw, src_head, src_f16, L);
 
     // 2b. stage every node's inputs (both blocks of a replay + verify): the first item
     // loaded above, then any further ones (when N * d_k / 8 exceeds the threads)
@@ -512,6 +550,12 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
         stage_load<DK, NB>(sr, it, in, a, b, h, g, row0);
         stage_store<DK, NB>(sr, it, a.qkv_bf16 != 0, sa, stage_walk);
     }
+
+    // 1b. the state rows in fp32 (and, fused, the commit)
+    float S[M][EPL];
+    widen_rows<M, EPL>(S, raw, src_f16);
+    if constexpr (FUSED) store_state_rows<DK, M, EPL, NT>(cache_head, L, S);
+
     // a tree replay runs the accepted node's root path, root first
     int n_steps = N;
     if constexpr (KIND == kReplayChain || KIND == kReplayVerifyChain) n_steps = acc + 1;
