@@ -12,13 +12,13 @@
  *       S_t = alpha_t * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
  *       o_t = scale * S_t q_t
  *   S is d_v x d_k, stored row-major (row j = value channel j, d_k contiguous
- *   key channels).  The rule is the gated delta rule of Yang, Kautz and
- *   Hatamizadeh, "Gated Delta Networks: Improving Mamba2 with Delta Rule"
- *   (ICLR 2025).  The pages describe the same layer only in words: page
- *   "LightSeek's TokenSpeed Hits 580 Tokens per Second on Qwen3.5's 400B
- *   Model", section "Why Qwen3.5 is hard to serve fast": a fixed state whose
- *   size is the head dimension squared, updated incrementally per token, and
- *   each output is read by querying the current (already updated) state.
+ *   key channels).  This is the gated delta rule of a Gated DeltaNet layer,
+ *   which the pages describe in words only: page "LightSeek's TokenSpeed Hits
+ *   580 Tokens per Second on Qwen3.5's 400B Model", section "Why Qwen3.5 is
+ *   hard to serve fast": a fixed state whose size is the head dimension
+ *   squared, updated incrementally per token, and each output is read by
+ *   querying the current (already updated) state.  The formula above is the
+ *   statement of that rule this oracle follows.
  *
  *   Chain: nodes 0..N-1, node t starts from node t-1 (node 0 from the cached
  *   state).  Tree: node t starts from node parent[t] (parent[0] = -1 = the
