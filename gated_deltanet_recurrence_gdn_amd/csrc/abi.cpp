@@ -64,7 +64,9 @@ size_t stage_bytes(int n, int d_k, int rows) {
 // verify 11.3 us against 10.0 us, the tree 19.8 us against 15.0 us.  Eight
 // waves per workgroup at batch 1 -- half the workgroups, half the staging --
 // measured the same: fused step 10.7-11.8 us against 10.7 us.)
-int plan_verify(const gdn_shape* sh, int fork_slots, VerifyPlan* p, int blocks = 1) {
+// A tree walk reads a fork slot every step (slot 0 when the step restores
+// nothing), so a tree launch reserves at least one slot.
+int plan_verify(const gdn_shape* sh, int fork_slots, VerifyPlan* p, int blocks = 1, bool tree = false) {
     const int rpg = 512 / sh->d_k;
     int m = 1;
     const long long waves_m1 = (long long)sh->batch * sh->h_v * (sh->d_v / rpg);
@@ -75,7 +77,7 @@ int plan_verify(const gdn_shape* sh, int fork_slots, VerifyPlan* p, int blocks =
         if (sh->d_v % (w * R) != 0) continue;
         const int rows = w * R;
         const size_t lds = (size_t)blocks * stage_bytes(sh->n_nodes, sh->d_k, rows) +
-                           (size_t)fork_slots * rows * sh->d_k * 4;
+                           (size_t)(tree && fork_slots < 1 ? 1 : fork_slots) * rows * sh->d_k * 4;
         if (lds > (size_t)kMaxLdsBytes) continue;
         p->m_groups = m;
         p->epl = 8;
@@ -118,7 +120,9 @@ int persist_mode(const gdn_shape* sh, const void* persist) {
 // visited in index order; a node with two or more children is saved to the
 // next free fork slot after it is computed and released when its last child
 // starts, so live slots form a stack along the current root path (at most
-// depth - 1 of them).
+// depth - 1 of them).  A restored slot is live from its save to the restore,
+// so no step in between writes it; in particular a step never restores the
+// slot the step before it saved (the kernel reads a step's slot one step early).
 int plan_tree(const int32_t* par, int n, uint16_t* walk, int* max_slots) {
     int depth[GDN_MAX_NODES], nchild[GDN_MAX_NODES], started[GDN_MAX_NODES], slot_of[GDN_MAX_NODES];
     int first_child[GDN_MAX_NODES], next_sib[GDN_MAX_NODES], last_child[GDN_MAX_NODES];
@@ -136,7 +140,7 @@ int plan_tree(const int32_t* par, int n, uint16_t* walk, int* max_slots) {
         if (first_child[p] < 0) first_child[p] = i; else next_sib[last_child[p]] = i;
         last_child[p] = i;
     }
-    int stack[GDN_MAX_NODES], sp = 0, top = 0, prev = -1, steps = 0;
+    int stack[GDN_MAX_NODES], sp = 0, top = 0, prev = -1, steps = 0, prev_save = -1;
     stack[sp++] = 0;
     while (sp > 0) {
         const int x = stack[--sp];
@@ -144,13 +148,16 @@ int plan_tree(const int32_t* par, int n, uint16_t* walk, int* max_slots) {
         if (x != 0) {
             const int p = par[x];
             if (p != prev) {
-                if (slot_of[p] < 0 || slot_of[p] != top - 1) return GDN_ERR_PARENT;  // cannot happen
+                if (slot_of[p] < 0 || slot_of[p] != top - 1 || slot_of[p] == prev_save)
+                    return GDN_ERR_PARENT;  // cannot happen
                 code |= kSchedRestore | (uint16_t)(slot_of[p] << 6);
             }
             if (++started[p] == nchild[p] && nchild[p] >= 2) { --top; slot_of[p] = -1; }
         }
+        prev_save = -1;
         if (nchild[x] >= 2) {
             if (top >= kMaxForkSlots) return GDN_ERR_PARENT;
+            prev_save = top;
             slot_of[x] = top++;
             code |= kSchedSave | (uint16_t)(slot_of[x] << 11);
             if (top > *max_slots) *max_slots = top;
@@ -254,7 +261,7 @@ int gdn_verify_tree(const gdn_shape* shape, const int32_t* parent, int32_t n_tre
         if ((rc = plan_tree(parent + (size_t)t * N, N, walk, &max_slots)) != GDN_OK) return rc;
     if (B == 0) return GDN_OK;
     VerifyPlan p;
-    if ((rc = plan_verify(shape, max_slots, &p)) != GDN_OK) return rc;
+    if ((rc = plan_verify(shape, max_slots, &p, 1, true)) != GDN_OK) return rc;
     VerifyArgs a = make_args(shape, p, q, k, v, alpha, beta, state, state_slot, out, persist, nullptr, status);
     a.fork_slots = max_slots;
     const int pm = persist_mode(shape, persist);

@@ -47,7 +47,7 @@ __device__ __forceinline__ void put_out(void* out, size_t idx, float o) {
 template <int M, int EPL>
 struct NodeOps {
     float k[EPL], q[EPL];
-    f32x4 coef;  // alpha, beta, q.k, unused
+    f32x4 coef;  // alpha, beta alpha, scale alpha, scale (q.k)
     float vb[M]; // beta * v for this lane's rows
 };
 
@@ -85,8 +85,10 @@ struct BlockIn {
 };
 
 // One block's staging area in LDS: k[N][DK] and q[N][DK] as fp32, the node
-// coefficients (alpha, beta, q.k) as f32x4 [N], beta * v [N][rows] for the
-// workgroup's rows, and walk[N] (tree walk codes or a replay path).
+// coefficients (alpha, beta alpha, scale alpha, scale (q.k)) as f32x4 [N] --
+// the products formed once here, in fp32 as the node step would form them --
+// beta * v [N][rows] for the workgroup's rows, and walk[N] (tree walk codes or
+// a replay path).
 template <int DK>
 struct StageArea {
     float* kL;
@@ -178,7 +180,7 @@ __device__ __forceinline__ void raw8_to_f32(const u32x4 (&w)[2], bool bf16, floa
 
 template <int DK, int NB>
 __device__ __forceinline__ void stage_store(const StageRegs<NB>& r, const StageItem<DK>& it, bool bf16,
-                                            const StageArea<DK> (&sa)[2], const uint16_t* walk) {
+                                            float scale, const StageArea<DK> (&sa)[2], const uint16_t* walk) {
     constexpr int LPR = DK / 8;
     const int e = it.e;
 #pragma unroll
@@ -198,14 +200,15 @@ __device__ __forceinline__ void stage_store(const StageRegs<NB>& r, const StageI
             for (int j = 0; j < 8; ++j) part = fmaf(kf[j], qf[j], part);
         }
         part = group_sum<LPR>(part);
-        if (it.kq() && (e % LPR) == 0) reinterpret_cast<float*>(sa[i].cL + e / LPR)[2] = part;
+        if (it.kq() && (e % LPR) == 0) reinterpret_cast<float*>(sa[i].cL + e / LPR)[3] = scale * part;
         if (it.v()) {
             const float vv = !bf16 ? __builtin_bit_cast(float, r.v[i]) : r.v_hi ? bf16_hi(r.v[i]) : bf16_lo(r.v[i]);
             sa[i].vbL[e] = r.vbeta[i] * vv;
         }
         if (it.g()) {
             reinterpret_cast<float*>(sa[i].cL + e)[0] = r.ga[i];
-            reinterpret_cast<float*>(sa[i].cL + e)[1] = r.gb[i];
+            reinterpret_cast<float*>(sa[i].cL + e)[1] = r.gb[i] * r.ga[i];
+            reinterpret_cast<float*>(sa[i].cL + e)[2] = scale * r.ga[i];
             if (i == 0 && walk != nullptr) sa[0].walkL[e] = walk[e];
         }
     }
@@ -302,15 +305,22 @@ __device__ __forceinline__ void widen_rows(float (&S)[M][EPL], const RowsRaw<M, 
 
 // The node loop over n_steps steps of one staged block: per step the optional
 // fork restore, the two row reductions, the update, the persisted copy, the
-// output, the optional fork save.  CODES: step st runs node walk[st] with its
-// fork bits (a tree walk, or a replay path whose codes carry no fork bits);
-// otherwise step st runs node st.  The next step's operands are read from LDS
-// while the current step computes.
+// output, the optional fork save.  CODES: step st runs node walk[st] (a tree
+// walk, or a replay path); otherwise step st runs node st.  FORKS (tree walks):
+// the codes carry fork bits.  The walk codes sit in one register (lane i holds
+// code i, read with a lane-select), so no step waits on LDS for its code; the
+// next step's operands -- and, FORKS, its fork slot, read whether or not it
+// restores -- are read from LDS while the current step computes.  Reading the
+// slot one step early is safe because a slot being restored is live: no save
+// between the parent's and the child's steps writes it (the walk's fork slots
+// form a stack).
 // OUTS = false (a replay): no outputs, so neither S q nor o is formed.
-template <int DK, int M, int EPL, bool CODES, int PMODE, int OUT, bool NT, bool OUTS = true>
+template <int DK, int M, int EPL, bool CODES, bool FORKS, int PMODE, int OUT, bool NT, bool OUTS = true>
 __device__ __forceinline__ void node_loop(float (&S)[M][EPL], const StageArea<DK>& sa, int n_steps,
                                           const VerifyArgs& a, void* out, const LaneRows& L, float* myfork,
                                           int fork_stride) {
+    static_assert(!FORKS || CODES, "fork bits come with walk codes");
+    static_assert(kMaxNodes <= 64, "one walk code per lane");
     constexpr int LPR = DK / EPL, RPG = 64 / LPR, NJ = EPL / 8;
     const int lane = threadIdx.x & 63, c = L.c, b = L.b, h = L.h;
     const int N = a.n_nodes, DV = a.d_v, rows = a.rows_per_wg;
@@ -323,27 +333,22 @@ __device__ __forceinline__ void node_loop(float (&S)[M][EPL], const StageArea<DK
     const size_t seq0 = (size_t)b * N;
     const size_t pbase = seq0 * pstride + (size_t)h * head_elems + (size_t)(L.row0 + vr0) * DK + 8 * c;
     const size_t obase = seq0 * ostride + (size_t)h * DV + L.row0 + vr0;
-    const float scale = a.scale;
+    using Slot = float[M][EPL];
 
-    auto step = [&](const NodeOps<M, EPL>& x, int code) {
+    auto step = [&](const NodeOps<M, EPL>& x, const Slot& fork_in, int code) {
         const int node = sched_node((uint16_t)code);
-        if constexpr (CODES) {
+        if constexpr (FORKS) {
             if (code & kSchedRestore) {
-                const float* src = myfork + sched_restore_slot((uint16_t)code) * fork_stride;
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
-                    for (int j = 0; j < 2 * NJ; ++j) {
-                        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (m * 64 + lane) * EPL + 4 * j);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) S[m][4 * j + e] = x0[e];
-                    }
+                    for (int e = 0; e < EPL; ++e) S[m][e] = fork_in[m][e];
             }
         }
         const float al = x.coef[0];
-        const float bal = x.coef[1] * al;     // beta * alpha
-        const float sal = scale * al;         // scale * alpha
-        const float sqk = scale * x.coef[2];  // scale * (q . k)
+        const float bal = x.coef[1];  // beta * alpha
+        const float sal = x.coef[2];  // scale * alpha
+        const float sqk = x.coef[3];  // scale * (q . k)
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             // Row sums in one fixed order for every layout: each 8-element chunk
@@ -408,7 +413,7 @@ __device__ __forceinline__ void node_loop(float (&S)[M][EPL], const StageArea<DK
             if (OUTS && out != nullptr && c == 0)
                 put_out<OUT>(out, obase + (uint32_t)node * ostride + (uint32_t)(m * RPG), o);
         }
-        if constexpr (CODES) {
+        if constexpr (FORKS) {
             if (code & kSchedSave) {
                 float* dst = myfork + sched_save_slot((uint16_t)code) * fork_stride;
 #pragma unroll
@@ -420,24 +425,43 @@ __device__ __forceinline__ void node_loop(float (&S)[M][EPL], const StageArea<DK
             }
         }
     };
+    // this lane's fork-slot entry of a step's restore slot (slot 0 without the bit)
+    auto read_fork = [&](Slot& r, int code) {
+        if constexpr (FORKS) {
+            const float* src = myfork + sched_restore_slot((uint16_t)code) * fork_stride;
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int j = 0; j < 2 * NJ; ++j) {
+                    const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (m * 64 + lane) * EPL + 4 * j);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r[m][4 * j + e] = x0[e];
+                }
+        }
+    };
+    const int wcode = CODES && lane < n_steps ? sa.walkL[lane] : 0;
     auto code_at = [&](int st) {
         const int x = st < n_steps ? st : n_steps - 1;
-        return CODES ? sa.walkL[x] : x;
+        return CODES ? __builtin_amdgcn_readlane(wcode, x) : x;
     };
 
     // Two operand buffers in ping-pong: while one node computes, the next
     // node's operands are already on their way from LDS.
     NodeOps<M, EPL> opA, opB;
+    Slot fkA, fkB;
     int codeA = code_at(0), codeB;
     read_node<DK, M, EPL>(opA, sa.kL, sa.qL, sa.cL, sa.vbL, sched_node((uint16_t)codeA), c, vr0, rows);
+    read_fork(fkA, codeA);
     for (int st = 0; st < n_steps; st += 2) {
         codeB = code_at(st + 1);
         read_node<DK, M, EPL>(opB, sa.kL, sa.qL, sa.cL, sa.vbL, sched_node((uint16_t)codeB), c, vr0, rows);
-        step(opA, codeA);
+        read_fork(fkB, codeB);
+        step(opA, fkA, codeA);
         if (st + 1 >= n_steps) break;
         codeA = code_at(st + 2);
         read_node<DK, M, EPL>(opA, sa.kL, sa.qL, sa.cL, sa.vbL, sched_node((uint16_t)codeA), c, vr0, rows);
-        step(opB, codeB);
+        read_fork(fkA, codeA);
+        step(opB, fkB, codeB);
     }
 }
 
@@ -543,12 +567,12 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
 
     // 2b. stage every node's inputs (both blocks of a replay + verify): the first item
     // loaded above, then any further ones (when N * d_k / 8 exceeds the threads)
-    stage_store<DK, NB>(sr, item, a.qkv_bf16 != 0, sa, stage_walk);
+    stage_store<DK, NB>(sr, item, a.qkv_bf16 != 0, a.scale, sa, stage_walk);
     for (int base = wave * 64 + 64 * nwaves; base < items; base += 64 * nwaves) {  // wave-uniform bound
         StageItem<DK> it = item;
         it.e = base + lane;
         stage_load<DK, NB>(sr, it, in, a, b, h, g, row0);
-        stage_store<DK, NB>(sr, it, a.qkv_bf16 != 0, sa, stage_walk);
+        stage_store<DK, NB>(sr, it, a.qkv_bf16 != 0, a.scale, sa, stage_walk);
     }
 
     // 1b. the state rows in fp32 (and, fused, the commit)
@@ -579,12 +603,12 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
     if constexpr (REPLAY) {
         // replay of the committed block: no outputs, no persisted copies; the result
         // is the committed state
-        node_loop<DK, M, EPL, KIND == kReplayTree, 0, OUT, NT, false>(S, sa[0], n_steps, a, nullptr, L, myfork,
+        node_loop<DK, M, EPL, KIND == kReplayTree, false, 0, OUT, NT, false>(S, sa[0], n_steps, a, nullptr, L, myfork,
                                                                       fork_stride);
         store_state_rows<DK, M, EPL, NT>(cache_head, L, S);
     }
     if constexpr (KIND == kReplayVerifyChain || !REPLAY) {
-        node_loop<DK, M, EPL, TREE, PMODE, OUT, NT>(S, sa[NB - 1], N, a, a.out, L, myfork, fork_stride);
+        node_loop<DK, M, EPL, TREE, TREE, PMODE, OUT, NT>(S, sa[NB - 1], N, a, a.out, L, myfork, fork_stride);
         // 4. final state (chains): the exact fp32 state after node N-1
         if constexpr (!TREE) {
             if (a.final_state != nullptr)

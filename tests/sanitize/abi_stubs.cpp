@@ -34,6 +34,7 @@ static void check_walk(const uint16_t* step, int n, const int32_t* parent, int f
     for (int i = 0; i < kMaxForkSlots; ++i) slot_node[i] = -2;
     int seen[kMaxNodes] = {0};
     int cur = -1;  // the node whose state the registers hold (-1: the cached state)
+    int prev_save = -1;  // the slot the previous step saved (the kernel reads a slot one step early)
     for (int i = 0; i < n; ++i) {
         const uint16_t c = step[i];
         const int node = sched_node(c);
@@ -43,16 +44,19 @@ static void check_walk(const uint16_t* step, int n, const int32_t* parent, int f
         if (c & kSchedRestore) {
             const int sl = sched_restore_slot(c);
             CHECK(sl < fork_slots);
+            CHECK(sl != prev_save);
             from = slot_node[sl];
         }
         CHECK(from == parent[node]);
         CHECK(seen[node] == 0);
         seen[node] = 1;
         cur = node;
+        prev_save = -1;
         if (c & kSchedSave) {
             const int sl = sched_save_slot(c);
             CHECK(sl < fork_slots);
             slot_node[sl] = node;
+            prev_save = sl;
         }
     }
     for (int i = 0; i < n; ++i) CHECK(seen[i] == 1);
@@ -71,6 +75,11 @@ hipError_t launch_verify(const VerifyArgs& a, const TreeSched* t, int d_k, int m
     CHECK(lds <= (size_t)kMaxLdsBytes);
     CHECK(pm >= 0 && pm <= 2);
     CHECK(a.group * a.h_qk == a.h_v);
+    if (t != nullptr) {
+        // every step reads a fork slot (slot 0 when it restores nothing)
+        const int slots = a.fork_slots < 1 ? 1 : a.fork_slots;
+        CHECK(lds >= (size_t)slots * a.rows_per_wg * d_k * 4);
+    }
     if (t != nullptr && sanitize::expected_parent != nullptr) {
         const int trees = a.per_seq_tree ? a.n_seq : 1;
         for (int i = 0; i < trees; ++i)
