@@ -113,7 +113,8 @@ struct StageArea {
 // stored, so they all issue back to back and cost one memory round trip; the
 // first item of every lane is loaded before the state rows (which may wait on
 // the slot and accepted-node lookups) and stored after them, so that round
-// trip overlaps the state's.  `walk` (tree verify only) goes to block 0's walk
+// trip overlaps the state's.  An item past the last one loads clamped
+// duplicates and stores nothing.  `walk` (tree verify only) goes to block 0's walk
 // area.
 template <int NB>
 struct StageRegs {
@@ -501,15 +502,21 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
                             KIND == kReplayVerifyChain ? a.rv : a.v, KIND == kReplayVerifyChain ? a.ralpha : a.alpha,
                             KIND == kReplayVerifyChain ? a.rbeta : a.beta},
                            {a.q, a.k, a.v, a.alpha, a.beta}};
+    // A tree (up to 32 nodes) has more staging items than threads; its first two
+    // items per lane are loaded up front, so their loads share one round trip.
+    constexpr int NI = TREE ? 2 : 1;
     const uint16_t* stage_walk = TREE ? walk : nullptr;
-    StageItem<DK> item;
-    item.chunks = N * (DK / 8);
-    item.nvb = N * rows;
-    item.N = N;
-    item.e = wave * 64 + lane;
-    const int items = item.chunks > item.nvb ? item.chunks : item.nvb;
-    StageRegs<NB> sr;
-    stage_load<DK, NB>(sr, item, in, a, b, h, g, row0);
+    StageItem<DK> item[NI];
+    StageRegs<NB> sr[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        item[i].chunks = N * (DK / 8);
+        item[i].nvb = N * rows;
+        item[i].N = N;
+        item[i].e = wave * 64 + lane + i * 64 * nwaves;
+        stage_load<DK, NB>(sr[i], item[i], in, a, b, h, g, row0);
+    }
+    const int items = item[0].chunks > item[0].nvb ? item[0].chunks : item[0].nvb;
 
 
     int s = b;
@@ -565,14 +572,15 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
     RowsRaw<M, EPL> raw;
     load_rows_raw<DK, M, EPL>(raw, src_head, src_f16, L);
 
-    // 2b. stage every node's inputs (both blocks of a replay + verify): the first item
-    // loaded above, then any further ones (when N * d_k / 8 exceeds the threads)
-    stage_store<DK, NB>(sr, item, a.qkv_bf16 != 0, a.scale, sa, stage_walk);
-    for (int base = wave * 64 + 64 * nwaves; base < items; base += 64 * nwaves) {  // wave-uniform bound
-        StageItem<DK> it = item;
+    // 2b. stage every node's inputs (both blocks of a replay + verify): the items
+    // loaded above, then any further ones (when N * d_k / 8 exceeds them)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) stage_store<DK, NB>(sr[i], item[i], a.qkv_bf16 != 0, a.scale, sa, stage_walk);
+    for (int base = wave * 64 + NI * 64 * nwaves; base < items; base += 64 * nwaves) {  // wave-uniform bound
+        StageItem<DK> it = item[0];
         it.e = base + lane;
-        stage_load<DK, NB>(sr, it, in, a, b, h, g, row0);
-        stage_store<DK, NB>(sr, it, a.qkv_bf16 != 0, a.scale, sa, stage_walk);
+        stage_load<DK, NB>(sr[0], it, in, a, b, h, g, row0);
+        stage_store<DK, NB>(sr[0], it, a.qkv_bf16 != 0, a.scale, sa, stage_walk);
     }
 
     // 1b. the state rows in fp32 (and, fused, the commit)
