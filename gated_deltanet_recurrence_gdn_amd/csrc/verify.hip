@@ -340,6 +340,9 @@ __device__ __forceinline__ void node_loop(float (&S)[M][EPL], const StageArea<DK
         const int node = sched_node((uint16_t)code);
         if constexpr (FORKS) {
             if (code & kSchedRestore) {
+                // a branch on the wave-uniform code, not eight selects on every step
+                // (an empty volatile asm keeps the compiler from flattening it)
+                asm volatile("");
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
