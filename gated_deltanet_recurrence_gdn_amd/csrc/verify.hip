@@ -522,22 +522,21 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
     const int items = item[0].chunks > item[0].nvb ? item[0].chunks : item[0].nvb;
 
 
+    // The slot and the accepted node of the committed block (fused commit or replay)
+    // are both read before anything is stored, so they are scalar loads, whose wait
+    // does not also wait for the staging loads in flight.
     int s = b;
-    if (a.state_slot != nullptr) {
-        s = a.state_slot[b];
-        if (s < 0 || s >= a.n_slots) {
-            if (tid == 0 && a.status != nullptr) a.status[0] = GDN_ERR_SLOT;
-            return;
-        }
-    }
-    // the accepted node of the committed block (fused commit or replay) must be in range
+    if (a.state_slot != nullptr) s = a.state_slot[b];
     int acc = 0;
-    if constexpr (HAS_ACC) {
-        acc = a.accepted_prev[b];
-        if (acc < 0 || acc >= N) {
-            if (tid == 0 && a.status != nullptr) a.status[0] = GDN_ERR_NODE;
-            return;
-        }
+    if constexpr (HAS_ACC) acc = a.accepted_prev[b];
+    if (a.state_slot != nullptr && (s < 0 || s >= a.n_slots)) {
+        if (tid == 0 && a.status != nullptr) a.status[0] = GDN_ERR_SLOT;
+        return;
+    }
+    // the accepted node must be in range
+    if (HAS_ACC && (acc < 0 || acc >= N)) {
+        if (tid == 0 && a.status != nullptr) a.status[0] = GDN_ERR_NODE;
+        return;
     }
 
     const int stage_floats = StageArea<DK>::floats(N, rows);
