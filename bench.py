@@ -233,7 +233,7 @@ def main() -> int:
         del src, dst
     timer = Timer(torch, dev)
     if args.only_prefill:
-        print(json.dumps({"prefill": bench_prefill(torch, gb, wl, dev, timer, max(5, args.steps // 25))}),
+        print(json.dumps({"prefill": bench_prefill(torch, gb, wl, dev, timer, max(10, args.steps // 5))}),
               flush=True)
         return 0
     w = wl.WORKLOADS["chain"]
@@ -405,7 +405,7 @@ def secondary(torch, gb, wl, dev, timer, args):
     log("replay_batched_chain", out["replay_batched_chain"])
     out["index_chain"] = bench_index(torch, gb, wl, dev, timer, args)
     log("index_chain", out["index_chain"])
-    out["prefill"] = bench_prefill(torch, gb, wl, dev, timer, max(5, args.steps // 25))
+    out["prefill"] = bench_prefill(torch, gb, wl, dev, timer, max(10, args.steps // 5))
     log("prefill", out["prefill"])
     out["prefill_varlen"] = bench_prefill_varlen(torch, gb, wl, dev, timer, max(3, args.steps // 100))
     log("prefill_varlen", out["prefill_varlen"])
@@ -496,7 +496,7 @@ def bench_prefill(torch, gb, wl, dev, timer, reps):
     t = dev_set(torch, wl.make_inputs(w), dev)
     out = torch.empty(w.batch, w.n_nodes, w.h_v, w.d_v, device=dev, dtype=torch.float16)
     call = gb.gdn_prefill_chunked(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["state0"], out, prepare=True)
-    ms, med, _ = measure(timer, [call], reps, 3)
+    ms, med, _ = measure(timer, [call], reps, 3, settle=SETTLE_S)
     fl = prefill_flops(w)
     return {"ms": ms, "median_ms": med, "tokens_per_s": w.batch * w.n_nodes / (ms * 1e-3),
             "algorithmic_gflop": fl / 1e9, "tflops": fl / (ms * 1e-3) / 1e12,
@@ -520,7 +520,7 @@ def bench_prefill_varlen(torch, gb, wl, dev, timer, reps, n_seq=8):
     ws = torch.empty(gb.gdn_prefill_varlen_workspace_bytes(cu, q, v, st, out), dtype=torch.uint8, device=dev)
     call = gb.gdn_prefill_varlen(cu, q, k, v, alpha, beta, st, out, chunk_states=cs, state_interval=26,
                                  workspace=ws, prepare=True)
-    ms, med, _ = measure(timer, [call], reps, 2)
+    ms, med, _ = measure(timer, [call], reps, 2, settle=SETTLE_S)
     fl = prefill_flops(w) * n_seq
     return {"sequences": n_seq, "tokens": n_seq * T, "ms": ms, "median_ms": med,
             "tokens_per_s": n_seq * T / (ms * 1e-3), "tflops": fl / (ms * 1e-3) / 1e12,

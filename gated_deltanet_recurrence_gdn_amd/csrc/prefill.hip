@@ -336,6 +336,26 @@ __device__ __forceinline__ void offdiag_column(PrepHead& W) {
         for (int r = 0; r < 4; ++r) W.T(JB + 1 + n, JB)[(4 * lg + r) * kTS + c] = tcol[n][r];
 }
 
+// Forward substitution of (I + A) x = e_jc for a strictly lower 16 x 16 block A,
+// in column order: once x[m] is final, A[t][m] x[m] leaves every later x[t].
+// Lane (bb, jc) holds column jc of its block's A (a[t] = A[t][jc]), so A[t][m] is
+// lane m's a[t], broadcast to the 16 lanes of the block's DPP row (row_newbcast:m):
+// two instructions per product, no LDS reads.
+template <int M>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + M, 0xF, 0xF, true));
+}
+template <int M>
+__device__ __forceinline__ void fwd_column(const float (&a)[16], float (&x)[16]) {
+    if constexpr (M < 15) {
+        float nx = -x[M];
+        asm("" : "+v"(nx));  // a plain operand: two-operand multiply-adds, not negated three-operand ones
+#pragma unroll
+        for (int t = M + 1; t < 16; ++t) x[t] = fmaf(row_bcast<M>(a[t]), nx, x[t]);
+        fwd_column<M + 1>(a, x);
+    }
+}
+
 template <int DK, bool BF16>
 __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs a, const PrefillSeqs seqs) {
     constexpr int kLdK = DK + 8;
@@ -458,27 +478,18 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         }
         __syncthreads();
         if (wave == 0) {
-            // diagonal 16 x 16 blocks of T by forward substitution: lane = (block, column)
+            // diagonal 16 x 16 blocks of T by forward substitution, one column of one block
+            // per lane: lane (bb, jc) reads column jc of A_bb once, then solves for column jc
+            // of T_bb (see fwd_column)
             const int bb = lane >> 4, jc = lane & 15;
             const float* Ab = W.A[tix(bb, bb)];
-            float x[16];
-            // row t's first t entries, read one row ahead of their use
-            f32x4 row[2][4];
+            float a[16], x[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                if (t + 1 < 16) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (4 * q < t + 1) row[(t + 1) & 1][q] = *reinterpret_cast<const f32x4*>(Ab + (t + 1) * kTS + 4 * q);
-                }
-                // four independent partial sums: x[t] waits on x[t - 1] through one product and
-                // two additions instead of a chain of t products
-                float ps[4] = {(t == jc) ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int m = 0; m < t; ++m) ps[m & 3] = fmaf(-row[t & 1][m / 4][m % 4], x[m], ps[m & 3]);
-                x[t] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-                __builtin_amdgcn_sched_barrier(0);
+                a[t] = Ab[t * kTS + jc];
+                x[t] = t == jc ? 1.f : 0.f;
             }
+            fwd_column<0>(a, x);
 #pragma unroll
             for (int t = 0; t < 16; ++t) W.T(bb, bb)[t * kTS + jc] = x[t];  // after all reads of A_bb
         } else {
