@@ -259,6 +259,21 @@ def test_tree_node_equals_gpu_chain_over_its_path():
         assert torch.equal(out[:, n], cout[:, -1]), n
 
 
+def test_tree_without_forks_in_two_row_groups_equals_chain():
+    """A tree whose parents form a chain has no fork slot to restore, yet the tree
+    kernel reads a slot every step: the launch reserves one.  At a batch large
+    enough for two row groups per wave, its outputs and node states equal the chain
+    kernel's bit for bit."""
+    B, N = 12, 8
+    w, d = small_inputs(91, B, N, 16, 48, 128, 128)
+    t = dev_inputs(d)
+    parent = np.arange(-1, N - 1, dtype=np.int32)
+    out, persist = run_tree(t, parent, N)
+    cout, cpersist, _ = run_chain(t, N, final=False)
+    assert torch.equal(out, cout)
+    assert torch.equal(persist, cpersist)
+
+
 def test_non_ancestor_inputs_do_not_reach_a_node():
     w = wl.WORKLOADS["tree"]
     d = wl.make_inputs(w)
