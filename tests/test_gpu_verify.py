@@ -419,6 +419,36 @@ def test_fused_commit_verify_equals_commit_then_verify(persist_dtype, same_buffe
     assert torch.equal(out, out_r) and torch.equal(per, per_r) and torch.equal(fin, fin_r)
 
 
+@pytest.mark.parametrize("persist_dtype", [torch.float16, torch.float32])
+def test_fused_commit_verify_through_state_slots(persist_dtype):
+    """The fused step on a state pool addressed through slots equals commit then verify on the same pool;
+    slots no sequence names keep their contents."""
+    B, N, n_slots = 5, 16, 11
+    w, d1 = small_inputs(41, B, N, 2, 6, 128, 128)
+    _, d2 = small_inputs(42, B, N, 2, 6, 128, 128)
+    t1, t2 = dev_inputs(d1), dev_inputs(d2)
+    slots = torch.tensor([9, 0, 4, 10, 2], dtype=torch.int32, device=DEV)
+    pool0 = torch.randn(n_slots, 6, 128, 128, device=DEV)
+    pool0[slots.long()] = t1["state0"]
+    out1, per1, fin1 = run_chain(t1, N, persist_dtype=persist_dtype, state=pool0, state_slot=slots)
+    acc = torch.tensor([15, 0, 7, 3, 15], dtype=torch.int32, device=DEV)
+    pool_ref = pool0.clone()
+    assert _commit(acc, per1, pool_ref, final=fin1, slot=slots) == 0
+    out_r, per_r, fin_r = run_chain(t2, N, persist_dtype=persist_dtype, state=pool_ref, state_slot=slots)
+    pool = pool0.clone()
+    out, per, fin = alloc_outputs(t2, N, persist_dtype)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gb.gdn_commit_verify_chain(acc, per1, t2["q"], t2["k"], t2["v"], t2["alpha"], t2["beta"], pool,
+                               final_prev=fin1, out=out, persist=per, final_state=fin, state_slot=slots,
+                               status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(pool, pool_ref)
+    untouched = [s for s in range(n_slots) if s not in set(slots.tolist())]
+    assert torch.equal(pool[untouched], pool0[untouched])
+    assert torch.equal(out, out_r) and torch.equal(per, per_r) and torch.equal(fin, fin_r)
+
+
 def test_fused_decode_loop_matches_oracle():
     """Three fused steps (accepted lengths 5, 16, 1) against the oracle applied step by step."""
     B, N = 2, 16
