@@ -65,6 +65,7 @@ _SIGS = {
     "gdn_verify_chain": [ctypes.POINTER(GdnShape)] + [_vp] * 12,
     "gdn_verify_tree": [ctypes.POINTER(GdnShape), _vp, _i32] + [_vp] * 11,
     "gdn_commit_verify_chain": [ctypes.POINTER(GdnShape)] + [_vp] * 15,
+    "gdn_commit_verify_tree": [ctypes.POINTER(GdnShape), _vp, _vp, _vp, _i32] + [_vp] * 11,
     "gdn_commit": [ctypes.POINTER(GdnShape)] + [_vp] * 7,
     "gdn_commit_replay": [ctypes.POINTER(GdnShape), _vp, _i32] + [_vp] * 10,
     "gdn_replay_verify_chain": [ctypes.POINTER(GdnShape)] + [_vp] * 18,
@@ -296,6 +297,28 @@ def gdn_verify_tree(parent, q, k, v, alpha, beta, state, *, out=None, persist=No
             _dev_ptr(status, "status"), _stream(stream))
     return _invoke("gdn_verify_tree", args, (sh, par, q, k, v, alpha, beta, state, state_slot, out, persist, status),
                    prepare)
+
+
+def gdn_commit_verify_tree(accepted_prev, persist_prev, parent, q, k, v, alpha, beta, state, *, out=None,
+                           persist=None, state_slot=None, status=None, scale: float = 1.0, stream=None,
+                           prepare: bool = False):
+    """Commit the previous step's accepted node and verify the next tree, in one launch."""
+    sh = _verify_shape(q, k, v, alpha, beta, state, state_slot, out,
+                       persist if persist is not None else persist_prev, None, status, scale)
+    B, N, Hv, dv, dk = sh.batch, sh.n_nodes, sh.h_v, sh.d_v, sh.d_k
+    _expect(accepted_prev, "accepted_prev", (B,), torch.int32)
+    _expect(persist_prev, "persist_prev", (B, N, Hv, dv, dk), (torch.float16, torch.float32))
+    if persist is not None and persist_prev is not None and persist.dtype != persist_prev.dtype:
+        raise TypeError("persist and persist_prev must have one dtype")
+    par = _host_parent(parent, N, B)
+    n_trees = 1 if par.ndim == 1 else par.shape[0]
+    args = (ctypes.byref(sh), _dev_ptr(accepted_prev, "accepted_prev"), _dev_ptr(persist_prev, "persist_prev"),
+            _vp(par.ctypes.data), _i32(n_trees), _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+            _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"), _dev_ptr(state, "state"),
+            _dev_ptr(state_slot, "state_slot"), _dev_ptr(out, "out"), _dev_ptr(persist, "persist"),
+            _dev_ptr(status, "status"), _stream(stream))
+    return _invoke("gdn_commit_verify_tree", args, (sh, accepted_prev, persist_prev, par, q, k, v, alpha, beta,
+                                                    state, state_slot, out, persist, status), prepare)
 
 
 def gdn_tree_walk(parent):

@@ -245,17 +245,26 @@ int gdn_commit_verify_chain(const gdn_shape* shape, const int32_t* accepted_prev
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
-int gdn_verify_tree(const gdn_shape* shape, const int32_t* parent, int32_t n_trees, const void* q,
-                    const void* k, const void* v, const float* alpha, const float* beta,
-                    const float* state, const int32_t* state_slot, void* out, void* persist,
-                    int32_t* status, void* stream) {
-    int rc = check_verify(shape, q, k, v, alpha, beta, state, state_slot, out, persist, nullptr);
-    if (rc != GDN_OK) return rc;
+namespace {
+
+// The previous step's accepted node, committed inside a tree verify's state load.
+struct TreeCommit {
+    const int32_t* accepted_prev;
+    const void* persist_prev;
+    float* state;
+};
+
+// Walk planning and launches of a tree verify (fused with the commit of the
+// previous step when `commit` is set).  Every tree is validated before anything
+// is launched; one tree per sequence goes kTreesPerLaunch sequences per launch.
+int tree_verify(const gdn_shape* shape, const int32_t* parent, int32_t n_trees, const void* q, const void* k,
+                const void* v, const float* alpha, const float* beta, const float* state,
+                const int32_t* state_slot, void* out, void* persist, int32_t* status, const TreeCommit* commit,
+                void* stream) {
     if (parent == nullptr) return GDN_ERR_NULL;
     const int B = shape->batch, N = shape->n_nodes;
     if (!(n_trees == 1 || (n_trees == B && B > 0))) return GDN_ERR_SHAPE;
-    // validate every tree before anything is launched
-    int max_slots = 0;
+    int rc, max_slots = 0;
     uint16_t walk[GDN_MAX_NODES];
     for (int t = 0; t < n_trees; ++t)
         if ((rc = plan_tree(parent + (size_t)t * N, N, walk, &max_slots)) != GDN_OK) return rc;
@@ -264,6 +273,12 @@ int gdn_verify_tree(const gdn_shape* shape, const int32_t* parent, int32_t n_tre
     if ((rc = plan_verify(shape, max_slots, &p, 1, true)) != GDN_OK) return rc;
     VerifyArgs a = make_args(shape, p, q, k, v, alpha, beta, state, state_slot, out, persist, nullptr, status);
     a.fork_slots = max_slots;
+    if (commit != nullptr) {
+        a.accepted_prev = commit->accepted_prev;
+        a.persist_prev = commit->persist_prev;
+        a.state_w = commit->state;
+        a.persist_prev_f16 = shape->persist_dtype == GDN_F16;
+    }
     const int pm = persist_mode(shape, persist);
     TreeSched ts;
     std::memset(&ts, 0, sizeof(ts));
@@ -276,7 +291,6 @@ int gdn_verify_tree(const gdn_shape* shape, const int32_t* parent, int32_t n_tre
                                      static_cast<hipStream_t>(stream));
         return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
     }
-    // one tree per sequence: kTreesPerLaunch sequences per launch
     a.per_seq_tree = 1;
     for (int s0 = 0; s0 < B; s0 += kTreesPerLaunch) {
         const int ns = (B - s0 < kTreesPerLaunch) ? (B - s0) : kTreesPerLaunch;
@@ -289,6 +303,32 @@ int gdn_verify_tree(const gdn_shape* shape, const int32_t* parent, int32_t n_tre
         if (e != hipSuccess) return GDN_ERR_HIP;
     }
     return GDN_OK;
+}
+
+}  // namespace
+
+int gdn_verify_tree(const gdn_shape* shape, const int32_t* parent, int32_t n_trees, const void* q,
+                    const void* k, const void* v, const float* alpha, const float* beta,
+                    const float* state, const int32_t* state_slot, void* out, void* persist,
+                    int32_t* status, void* stream) {
+    const int rc = check_verify(shape, q, k, v, alpha, beta, state, state_slot, out, persist, nullptr);
+    if (rc != GDN_OK) return rc;
+    return tree_verify(shape, parent, n_trees, q, k, v, alpha, beta, state, state_slot, out, persist, status,
+                       nullptr, stream);
+}
+
+int gdn_commit_verify_tree(const gdn_shape* shape, const int32_t* accepted_prev, const void* persist_prev,
+                           const int32_t* parent, int32_t n_trees, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, float* state, const int32_t* state_slot,
+                           void* out, void* persist, int32_t* status, void* stream) {
+    const int rc = check_verify(shape, q, k, v, alpha, beta, state, state_slot, out, persist, nullptr);
+    if (rc != GDN_OK) return rc;
+    if (shape->batch > 0 && (accepted_prev == nullptr || persist_prev == nullptr)) return GDN_ERR_NULL;
+    if (shape->persist_dtype != GDN_F16 && shape->persist_dtype != GDN_F32) return GDN_ERR_DTYPE;
+    if (!aligned(accepted_prev, 4) || !aligned(persist_prev, 16)) return GDN_ERR_ALIGN;
+    const TreeCommit c{accepted_prev, persist_prev, state};
+    return tree_verify(shape, parent, n_trees, q, k, v, alpha, beta, state, state_slot, out, persist, status, &c,
+                       stream);
 }
 
 int gdn_commit_replay(const gdn_shape* shape, const int32_t* parent, int32_t n_trees,

@@ -80,7 +80,7 @@ struct VerifyArgs {
     int32_t fork_slots;  // fork slots reserved in LDS (tree walks)
     int32_t per_seq_tree;// 0: tree 0 for every sequence; 1: tree b - seq0
     float scale;
-    // fused commit of the previous step (chain launches only; accepted_prev == nullptr: off)
+    // fused commit of the previous step (accepted_prev == nullptr: off; final_prev: chains only)
     const int32_t* accepted_prev;
     const void* persist_prev;
     const float* final_prev;
@@ -110,6 +110,7 @@ enum VerifyKind : int {
     kReplayChain = 2,        // commit by replay of nodes 0 .. accepted
     kReplayTree = 3,         // commit by replay of the accepted node's root path
     kReplayVerifyChain = 4,  // replay commit of the previous chain block, then verify the next
+    kCommitVerifyTree = 6,   // the persisted-copy commit of the previous block fused into a tree verify
 };
 
 // Depth-first walk of up to kTreesPerLaunch trees (tree launches only).
@@ -207,10 +208,16 @@ struct PrefillArgs {
 // Verify kernel launch.  d_k selects the instantiation; m_groups is the number
 // of row groups each wave keeps and epl the state elements per lane (8; see
 // verify.hip); persist_mode 0 = none,
-// 1 = f16, 2 = fp32; tree == nullptr launches the chain kernel.
+// 1 = f16, 2 = fp32; tree == nullptr launches the chain kernel.  A set
+// a.accepted_prev launches the fused commit + verify of the same shape.
 hipError_t launch_verify(const VerifyArgs& a, const TreeSched* tree, int d_k, int m_groups, int epl,
                          int persist_mode, int waves_per_wg, size_t lds_bytes, int grid,
                          hipStream_t stream);
+// The fused commit + tree verify instances (their own translation unit);
+// launch_verify forwards to it.
+hipError_t launch_commit_verify_tree(const VerifyArgs& a, const TreeSched& tree, int d_k, int m_groups, int epl,
+                                     int persist_mode, int waves_per_wg, size_t lds_bytes, int grid,
+                                     hipStream_t stream);
 
 // Replay launches (kind kReplayChain, kReplayTree or kReplayVerifyChain); parents is
 // used by kReplayTree only.

@@ -155,6 +155,32 @@ int gdn_verify_tree(const gdn_shape* shape, const int32_t* parent, int32_t n_tre
                     int32_t* status, void* stream);
 
 /*
+ * One launch for a tree decode step: commit the previous step's accepted node,
+ * then verify the next tree from the committed state.  Equivalent to
+ *     gdn_commit(shape, accepted_prev, persist_prev, NULL, state, state_slot, status)
+ *     gdn_verify_tree(shape, parent, n_trees, q, k, v, alpha, beta, state, state_slot,
+ *                     out, persist, status)
+ * with the commit fused into the verify's state load: the accepted node's
+ * persisted copy is read once, widened to fp32, written to state[slot(b)] and
+ * used directly as the root's starting state.  Page "400 tok/s with Qwen3.5",
+ * section "Handling recurrent state" (state set to the accepted boundary before
+ * the next verification); page "Qwen3.6 27B: From 20 t/s to 184 t/s", section
+ * "Diffusion applied to text" (the tree verified in one pass).
+ *
+ * persist_prev is the previous step's persist: same layout, n_nodes and
+ * persist_dtype as this call's; it may be the very buffer this call writes
+ * (each value is read before it is overwritten).  accepted_prev is a device
+ * array [B] of node indices of the previous step (the last node of its accepted
+ * path); a node outside [0, N) skips the sequence entirely (state and outputs
+ * untouched) and sets *status to GDN_ERR_NODE.  parent, n_trees and the other
+ * arguments and errors as gdn_verify_tree.
+ */
+int gdn_commit_verify_tree(const gdn_shape* shape, const int32_t* accepted_prev, const void* persist_prev,
+                           const int32_t* parent, int32_t n_trees, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, float* state, const int32_t* state_slot,
+                           void* out, void* persist, int32_t* status, void* stream);
+
+/*
  * Commit the accepted node of every sequence into the state cache.
  * Page "400 tok/s with Qwen3.5", section "Handling recurrent state": after a
  * rejection the state is set to the accepted boundary; a fully accepted

@@ -73,8 +73,12 @@ int main() {
         const int rc = gdn_verify_tree(&s, par.data(), per_seq ? B : 1, F, F, F, FF, FF, FF, nullptr, F, F,
                                        nullptr, nullptr);
         EXPECT(rc == GDN_OK || rc == GDN_ERR_UNSUPPORTED);
-        sanitize::expected_parent = nullptr;
         const int32_t* acc = reinterpret_cast<const int32_t*>(F);
+        // the fused commit + tree verify plans the same walks
+        const int rcf = gdn_commit_verify_tree(&s, acc, F, par.data(), per_seq ? B : 1, F, F, F, FF, FF, FF,
+                                               nullptr, F, F, nullptr, nullptr);
+        EXPECT(rcf == rc);
+        sanitize::expected_parent = nullptr;
         EXPECT(gdn_commit_replay(&s, par.data(), per_seq ? B : 1, acc, F, F, F, FF, FF, FF, nullptr, nullptr,
                                  nullptr) == GDN_OK);
         gdn_conv_shape cs = {B, n, 8 * (1 + (int)(rng() % 64)), 2 + (int)(rng() % 7), B, GDN_BF16};
@@ -101,6 +105,10 @@ int main() {
         EXPECT(rc <= 0 && rc >= GDN_ERR_SLOT);
         rc = gdn_commit_verify_chain(&s, acc, F, FF, F, F, F, FF, FF, FF, nullptr, F, F, FF + 4096, nullptr,
                                      nullptr);
+        EXPECT(rc <= 0 && rc >= GDN_ERR_SLOT);
+        const int32_t chain_par[GDN_MAX_NODES + 1] = {-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15,
+                                                      16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31};
+        rc = gdn_commit_verify_tree(&s, acc, F, chain_par, 1, F, F, F, FF, FF, FF, nullptr, F, F, nullptr, nullptr);
         EXPECT(rc <= 0 && rc >= GDN_ERR_SLOT);
         rc = gdn_replay_verify_chain(&s, acc, F, F, F, FF, FF, F, F, F, FF, FF, FF, nullptr, F, nullptr, nullptr,
                                      nullptr, nullptr);

@@ -75,6 +75,11 @@ hipError_t launch_verify(const VerifyArgs& a, const TreeSched* t, int d_k, int m
     CHECK(lds <= (size_t)kMaxLdsBytes);
     CHECK(pm >= 0 && pm <= 2);
     CHECK(a.group * a.h_qk == a.h_v);
+    if (a.accepted_prev != nullptr) {
+        // a fused commit reads the previous step's node and writes the state cache
+        CHECK(a.persist_prev != nullptr && a.state_w != nullptr);
+        if (t != nullptr) CHECK(a.final_prev == nullptr);
+    }
     if (t != nullptr) {
         // every step reads a fork slot (slot 0 when it restores nothing)
         const int slots = a.fork_slots < 1 ? 1 : a.fork_slots;

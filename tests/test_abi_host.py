@@ -220,6 +220,34 @@ def test_fused_commit_verify_rejects_bad_requests():
     assert f(shape(d_k=96)) == E["GDN_ERR_SHAPE"]
 
 
+def test_fused_commit_verify_tree_rejects_bad_requests():
+    L = gb.lib()
+
+    def f(sh, parent=(-1, 0, 0), n_trees=1, acc=FAKE, per_prev=FAKE, st=FAKE):
+        par = np.ascontiguousarray(parent, dtype=np.int32) if parent is not None else None
+        return L.gdn_commit_verify_tree(ctypes.byref(sh), acc, per_prev,
+                                        par.ctypes.data if par is not None else None, n_trees, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, st, None, FAKE, FAKE, None, None)
+    sh3 = dict(n_nodes=3)
+    assert f(shape(**sh3), acc=None) == E["GDN_ERR_NULL"]
+    assert f(shape(**sh3), per_prev=None) == E["GDN_ERR_NULL"]
+    assert f(shape(**sh3), per_prev=FAKE + 8) == E["GDN_ERR_ALIGN"]
+    assert f(shape(**sh3), acc=FAKE + 2) == E["GDN_ERR_ALIGN"]
+    assert f(shape(**sh3), st=FAKE + 4) == E["GDN_ERR_ALIGN"]
+    assert f(shape(n_nodes=3, d_k=96)) == E["GDN_ERR_SHAPE"]
+    assert f(shape(**sh3, persist_dtype=gb.GDN_BF16)) == E["GDN_ERR_DTYPE"]
+    # the parent rules of gdn_verify_tree, checked before anything is launched
+    assert f(shape(**sh3), parent=None) == E["GDN_ERR_NULL"]
+    assert f(shape(**sh3), parent=[0, 0, 1]) == E["GDN_ERR_PARENT"]
+    assert f(shape(**sh3), parent=[-1, 0, 2]) == E["GDN_ERR_PARENT"]
+    assert f(shape(n_nodes=3, batch=2), parent=[-1, 0, 1] * 3, n_trees=3) == E["GDN_ERR_SHAPE"]
+    deep = [-1] + list(range(16))  # 17 nodes on one path
+    assert f(shape(n_nodes=17), parent=deep) == E["GDN_ERR_PARENT"]
+    # an empty batch validates the tree and launches nothing
+    assert f(shape(n_nodes=3, batch=0), acc=None, per_prev=None) == 0
+    assert f(shape(n_nodes=3, batch=0), parent=[-1, 0, 2]) == E["GDN_ERR_PARENT"]
+
+
 def test_commit_replay_rejects_bad_requests():
     L = gb.lib()
 

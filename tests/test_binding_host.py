@@ -90,6 +90,23 @@ def test_fused_commit_verify_checks_the_previous_block():
                                    final_prev=torch.zeros(B, HV, DV, DK + 32), persist=a["persist"])
 
 
+def test_fused_commit_verify_tree_checks_the_previous_block_and_the_tree():
+    a = verify_args()
+    acc = torch.zeros(B, dtype=torch.int32)
+    par = np.array([-1] + list(range(N - 1)), np.int32)
+    args = (a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["state"])
+    with pytest.raises(ValueError):
+        gb.gdn_commit_verify_tree(torch.zeros(B + 1, dtype=torch.int32), a["persist"], par, *args, out=a["out"],
+                                  persist=a["persist"])
+    with pytest.raises(ValueError):
+        gb.gdn_commit_verify_tree(acc, torch.zeros(B, N + 1, HV, DV, DK, dtype=torch.float16), par, *args,
+                                  out=a["out"], persist=a["persist"])
+    with pytest.raises(TypeError):
+        gb.gdn_commit_verify_tree(acc, a["persist"].float(), par, *args, out=a["out"], persist=a["persist"])
+    with pytest.raises(ValueError, match="parent"):
+        gb.gdn_commit_verify_tree(acc, a["persist"], par[:-1], *args, out=a["out"], persist=a["persist"])
+
+
 def test_commit_checks_index_state_and_final_shapes():
     per = torch.zeros(B, N, HV, DV, DK, dtype=torch.float16)
     st = torch.zeros(B, HV, DV, DK)

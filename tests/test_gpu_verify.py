@@ -478,6 +478,120 @@ def test_fused_decode_loop_matches_oracle():
     assert max_rel(to_host(st), ref_state) <= STATE_TOL
 
 
+# --------------------------------------------------------------------------
+# fused commit + tree verify (one launch per tree decode step)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("persist_dtype", [torch.float16, torch.float32])
+@pytest.mark.parametrize("same_buffers", [False, True])
+def test_fused_commit_verify_tree_equals_commit_then_verify(persist_dtype, same_buffers):
+    """The fused tree step equals gdn_commit followed by gdn_verify_tree, bit for bit, also when it
+    writes over the node states it commits from."""
+    rng = np.random.default_rng(61)
+    B, N = 3, 22
+    _, d1 = small_inputs(61, B, N, 2, 6, 128, 128, tree=True)
+    _, d2 = small_inputs(62, B, N, 2, 6, 128, 128, tree=True)
+    p1, p2 = wl.random_tree(N, 16, rng), wl.random_tree(N, 16, rng)
+    t1, t2 = dev_inputs(d1), dev_inputs(d2)
+    out1, per1 = run_tree(t1, p1, N, persist_dtype=persist_dtype)
+    acc = torch.tensor([21, 0, 9], dtype=torch.int32, device=DEV)
+    st_ref = t1["state0"].clone()
+    assert _commit(acc, per1, st_ref) == 0
+    out_r, per_r = run_tree({**t2, "state0": st_ref}, p2, N, persist_dtype=persist_dtype)
+    st = t1["state0"].clone()
+    if same_buffers:
+        out, per = out1.clone(), per1.clone()
+        per_prev = per
+    else:
+        out, per, _ = alloc_outputs(t2, N, persist_dtype, final=False)
+        per_prev = per1
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gb.gdn_commit_verify_tree(acc, per_prev, p2, t2["q"], t2["k"], t2["v"], t2["alpha"], t2["beta"], st,
+                              out=out, persist=per, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(st, st_ref)
+    assert torch.equal(out, out_r) and torch.equal(per, per_r)
+
+
+def test_fused_commit_verify_per_sequence_trees_through_slots():
+    """One tree per sequence, more sequences than one launch carries, states in a slot pool."""
+    rng = np.random.default_rng(63)
+    B, N, n_slots = 21, 12, 25
+    _, d1 = small_inputs(63, B, N, 1, 2, 64, 64, tree=True)
+    _, d2 = small_inputs(64, B, N, 1, 2, 64, 64, tree=True)
+    t1, t2 = dev_inputs(d1), dev_inputs(d2)
+    par1 = np.stack([wl.random_tree(N, 8, rng) for _ in range(B)])
+    par2 = np.stack([wl.random_tree(N, 8, rng) for _ in range(B)])
+    slots = torch.from_numpy(rng.permutation(n_slots)[:B].astype(np.int32)).to(DEV)
+    pool0 = torch.randn(n_slots, 2, 64, 64, device=DEV)
+    pool0[slots.long()] = t1["state0"]
+    _, per1 = run_tree({**t1, "state0": pool0}, par1, N, state_slot=slots)
+    acc = torch.from_numpy(rng.integers(0, N, B).astype(np.int32)).to(DEV)
+    pool_ref = pool0.clone()
+    assert _commit(acc, per1, pool_ref, slot=slots) == 0
+    out_r, per_r = run_tree({**t2, "state0": pool_ref}, par2, N, state_slot=slots)
+    pool = pool0.clone()
+    out, per, _ = alloc_outputs(t2, N, final=False)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gb.gdn_commit_verify_tree(acc, per1, par2, t2["q"], t2["k"], t2["v"], t2["alpha"], t2["beta"], pool,
+                              out=out, persist=per, state_slot=slots, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(pool, pool_ref)
+    assert torch.equal(out, out_r) and torch.equal(per, per_r)
+
+
+def test_fused_tree_decode_loop_matches_oracle():
+    """Three tree steps, the second and third fused with the commit of the step before, against the
+    oracle applied step by step (commit of the accepted node's exact state)."""
+    rng = np.random.default_rng(65)
+    B, N = 2, 22
+    steps = [small_inputs(65 + i, B, N, 2, 4, 128, 128, tree=True)[1] for i in range(3)]
+    pars = [wl.random_tree(N, 16, rng) for _ in range(3)]
+    accs = [np.array([5, 21], np.int32), np.array([0, 13], np.int32), np.array([17, 2], np.int32)]
+    st = dev_inputs(steps[0])["state0"].clone()
+    ref_state = steps[0]["state0"].astype(np.float64)
+    per_prev = acc_prev = None
+    for i, d in enumerate(steps):
+        t = dev_inputs(d)
+        out, per, _ = alloc_outputs(t, N, final=False)
+        if i == 0:
+            gb.gdn_verify_tree(pars[0], t["q"], t["k"], t["v"], t["alpha"], t["beta"], st, out=out, persist=per)
+        else:
+            gb.gdn_commit_verify_tree(acc_prev, per_prev, pars[i], t["q"], t["k"], t["v"], t["alpha"],
+                                      t["beta"], st, out=out, persist=per)
+        torch.cuda.synchronize()
+        ref = oracle.tree(d["q"], d["k"], d["v"], d["alpha"], d["beta"], ref_state, pars[i])
+        e = (max_rel(to_host(out), ref["out"]), max_rel(to_host(per), ref["nodes"]))
+        say(f"tree step {i}: out {e[0]:.2e} node states {e[1]:.2e}")
+        assert e[0] <= OUT_TOL and e[1] <= PERSIST_TOL
+        ref_state, _ = oracle.commit(ref_state, ref["nodes"], accs[i])
+        acc_prev = torch.from_numpy(accs[i]).to(DEV)
+        per_prev = per
+    assert _commit(acc_prev, per_prev, st) == 0
+    assert max_rel(to_host(st), ref_state) <= STATE_TOL
+
+
+def test_fused_tree_bad_accepted_node_skips_sequence():
+    rng = np.random.default_rng(67)
+    w, d = small_inputs(67, 3, 8, 1, 2, 64, 64, tree=True)
+    t = dev_inputs(d)
+    par = wl.random_tree(8, 4, rng)
+    _, per1 = run_tree(t, par, 8)
+    st = t["state0"].clone()
+    out, per, _ = alloc_outputs(t, 8, final=False)
+    out.zero_(); per.zero_()
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    acc = torch.tensor([2, -1, 7], dtype=torch.int32, device=DEV)
+    gb.gdn_commit_verify_tree(acc, per1, par, t["q"], t["k"], t["v"], t["alpha"], t["beta"], st, out=out,
+                              persist=per, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == gb.CODES["GDN_ERR_NODE"]
+    assert torch.equal(st[1], t["state0"][1]) and torch.count_nonzero(per[1]) == 0
+    assert torch.count_nonzero(out[1]) == 0
+    assert torch.equal(st[0], per1[0, 2].float()) and torch.equal(st[2], per1[2, 7].float())
+
+
 def test_fused_bad_accepted_node_skips_sequence():
     w, d = small_inputs(41, 3, 8, 1, 2, 64, 64)
     t = dev_inputs(d)
