@@ -836,12 +836,20 @@ __device__ __forceinline__ void load_out_ops(OutOps<DK, H>& ops, const OutSrc& r
 }
 
 // The state (f16, as the products' B operand) and U (f16) handed from the
-// chain wave to the output wave of a slice, in operand order: 16 bytes per
-// lane per operand.
-template <int DK>
+// chain wave to the output waves of a slice, in operand order: 16 bytes per
+// lane per operand.  LAG (output waves one chunk behind the chain): three
+// copies of the state (the copy a chunk starts from is written at the end of
+// the chunk before and read during the chunk after) and two of U (written
+// during its chunk, read during the next), so no copy is written while it may
+// be read; without LAG one of each, ordered by the middle barrier.
+template <int DK, bool LAG>
 struct Xchg {
     static constexpr int KB = DK / 32, VB = kC / 32;
-    static constexpr int SB = 0, UB = KB * 1024, BYTES = UB + VB * 1024;
+    static constexpr int NSB = LAG ? 3 : 1, NUB = LAG ? 2 : 1;
+    static constexpr int SBB = KB * 1024, UBB = VB * 1024;  // bytes of one copy
+    static constexpr int UB0 = NSB * SBB, BYTES = UB0 + NUB * UBB;
+    __device__ static int sb(int ck) { return (LAG ? ck % 3 : 0) * SBB; }  // the state chunk ck starts from
+    __device__ static int ub(int ck) { return UB0 + (LAG ? ck % 2 : 0) * UBB; }  // chunk ck's U
 };
 __device__ __forceinline__ void put_h8(unsigned char* base, int i, const h8& v) {
     *reinterpret_cast<h8*>(base + i * 1024 + 16 * (threadIdx.x & 63)) = v;
@@ -905,9 +913,9 @@ __device__ __forceinline__ void extra_reads(ChainRegs<DK>& x, const unsigned cha
     }
 }
 
-template <int DK, bool BF16, int NSL, int S>
+template <int DK, bool BF16, int NSL, bool LAG, int S>
 __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16], const unsigned char* blk,
-                                           unsigned char* xc, int sl) {
+                                           unsigned char* xu, unsigned char* xs, int sl) {
     using PL = Plan<DK>;
     constexpr int NP = PL::NP, NT = PL::NT, VB = PL::VB, KB = PL::KB;
     if constexpr (S < PL::A_END) {
@@ -940,13 +948,14 @@ __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16
                     }
         }
         if constexpr (S == PL::A_ST) {
-            // U in f16 to the output wave; U scaled by Gamma_{C,t} here
+            // U in f16 to the output waves; U scaled by Gamma_{C,t} here
 #pragma unroll
             for (int v = 0; v < VB; ++v) {
-                put_h8(xc + Xchg<DK>::UB, v, pack_h8(x.uu[2 * v], x.uu[2 * v + 1]));
+                put_h8(xu, v, pack_h8(x.uu[2 * v], x.uu[2 * v + 1]));
                 x.ug[v] = pack_h8(x.gq[2 * v] * x.uu[2 * v], x.gq[2 * v + 1] * x.uu[2 * v + 1]);
             }
-            lds_barrier();  // U published (the output waves wait here for it)
+            // U published (the output waves wait here for it); LAG: they read it a chunk later
+            if constexpr (!LAG) lds_barrier();
         }
         if constexpr (S < PL::A_U) {
             constexpr int p = S % NP, u = S / NP;
@@ -959,14 +968,14 @@ __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16
             st[t] = mfma16(x.fa[S], x.ug[v], st[t]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        chain_step<DK, BF16, NSL, S + 1>(x, st, blk, xc, sl);
+        chain_step<DK, BF16, NSL, LAG, S + 1>(x, st, blk, xu, xs, sl);
     } else {
         // the next chunk's starting state as the products' B operand, kept for this wave's
-        // next K H and handed to the output wave
+        // next K H and handed to the output waves
 #pragma unroll
         for (int u = 0; u < KB; ++u) {
             x.sb[u] = pack_h8(st[2 * u], st[2 * u + 1]);
-            put_h8(xc + Xchg<DK>::SB, u, x.sb[u]);
+            put_h8(xs, u, x.sb[u]);
         }
     }
 }
@@ -978,10 +987,11 @@ struct OutRegs {
     f32x4 gp[2];
 };
 
-// The output wave's view of the hand-off areas and output staging: slice s's
-// at xc + s * XC and ost + s * OST.
+// The output wave's view of the chunk it computes: slice s's starting state at
+// sb + s * XC, its U at ub + s * XC and its output staging at ost + s * OST.
 struct OutPlaces {
-    const unsigned char* xc;
+    const unsigned char* sb;
+    const unsigned char* ub;
     unsigned char* ost;
 };
 
@@ -1001,15 +1011,18 @@ __device__ __forceinline__ void out_step(OutRegs<DK, NSL>& x, OutOps<DK, H>& ops
             const float* gam = reinterpret_cast<const float*>(blk + CB::G0);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                x.gp[i] = *reinterpret_cast<const f32x4*>(gam + pair_row(2 * H + i, 4 * lg));
+                // LAG: the gate rows came with the chunk, a chunk ago (x.gp)
+                if constexpr (!L::LAG) x.gp[i] = *reinterpret_cast<const f32x4*>(gam + pair_row(2 * H + i, 4 * lg));
 #pragma unroll
                 for (int q = 0; q < NSL; ++q) x.o[q][i] = x.gp[i] * x.o[q][i];  // gamma Q H
             }
-            lds_barrier();  // U from the chain waves (the next chunk's loads stay in flight)
+            // U from the chain waves (the next chunk's loads stay in flight); LAG: published
+            // by the chunk's barrier
+            if constexpr (!L::LAG) lds_barrier();
 #pragma unroll
             for (int q = 0; q < NSL; ++q)
 #pragma unroll
-                for (int v = 0; v < OP::NUB; ++v) x.ub[q][v] = get_h8(pl.xc + q * L::XC + Xchg<DK>::UB, v);
+                for (int v = 0; v < OP::NUB; ++v) x.ub[q][v] = get_h8(pl.ub + q * L::XC, v);
         }
         // one operand, the products of every slice
         if constexpr (S < OP::B_PU) {
@@ -1025,7 +1038,7 @@ __device__ __forceinline__ void out_step(OutRegs<DK, NSL>& x, OutOps<DK, H>& ops
         __builtin_amdgcn_sched_barrier(0);
         out_step<DK, OUT, BF16, NSL, NB, H, S + 1>(x, ops, nsrc, blk, pl, scale, d);
     } else {
-        // O -> staging (written out at the start of the next chunk)
+        // O -> staging (written out at the start of the next pass)
         const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
 #pragma unroll
         for (int q = 0; q < NSL; ++q)
@@ -1040,9 +1053,10 @@ __device__ __forceinline__ void out_step(OutRegs<DK, NSL>& x, OutOps<DK, H>& ops
     }
 }
 
-template <int DK, bool BF16, int NSL>
+// One chunk of a chain wave: U goes to xu, the next chunk's starting state to xs.
+template <int DK, bool BF16, int NSL, bool LAG>
 __device__ __forceinline__ void chain_chunk(f32x4 (&st)[DK / 16], h8 (&sb)[DK / 32], const unsigned char* blk,
-                                            unsigned char* xc, int sl) {
+                                            unsigned char* xu, unsigned char* xs, int sl) {
     using PL = Plan<DK>;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     ChainRegs<DK> x{sb};
@@ -1055,19 +1069,23 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&st)[DK / 16], h8 (&sb)[DK / 
     x.fa[4] = chain_operand<DK, 4>(blk);
     x.fa[5] = chain_operand<DK, 5>(blk);
     static_assert(Plan<DK>::D == 6, "prologue reads D operands");
-    chain_step<DK, BF16, NSL, 0>(x, st, blk, xc, sl);
+    chain_step<DK, BF16, NSL, LAG, 0>(x, st, blk, xu, xs, sl);
 }
 
+// One chunk of an output wave: blk is the chunk's LDS block (its gate rows;
+// LAG: gp holds them instead).
 template <int DK, int OUT, bool BF16, int NSL, int NB, int H>
 __device__ __forceinline__ void out_chunk(OutOps<DK, H>& ops, const OutSrc& nsrc, const unsigned char* blk,
-                                          const OutPlaces& pl, float scale, const DmaCtx& d) {
+                                          const OutPlaces& pl, float scale, const DmaCtx& d, const f32x4 (&gp)[2]) {
     using L = ScanLayout<DK, OUT, BF16, NSL, NB>;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     OutRegs<DK, NSL> x;
+    x.gp[0] = gp[0];
+    x.gp[1] = gp[1];
 #pragma unroll
     for (int q = 0; q < NSL; ++q) {
 #pragma unroll
-        for (int u = 0; u < DK / 32; ++u) x.sb[q][u] = get_h8(pl.xc + q * L::XC + Xchg<DK>::SB, u);
+        for (int u = 0; u < DK / 32; ++u) x.sb[q][u] = get_h8(pl.sb + q * L::XC, u);
         x.o[q][0] = x.o[q][1] = z;
     }
     out_step<DK, OUT, BF16, NSL, NB, H, 0>(x, ops, nsrc, blk, pl, scale, d);
@@ -1077,27 +1095,43 @@ __device__ __forceinline__ void out_chunk(OutOps<DK, H>& ops, const OutSrc& nsrc
 // c + 1 landed or landing and c + 2 being loaded (one workgroup per CU); with
 // two (two workgroups per CU, for launches of more workgroups than CUs), c + 1
 // is loaded during c.
+// LAG (three blocks): the output waves compute each chunk during the next one,
+// from double-buffered hand-offs and staging, so the chunk has one barrier.
 template <int DK, int OUT, bool BF16, int NSL, int NB>
 struct ScanLayout {
     static constexpr int NBUF = NB;
+    static constexpr bool LAG = NB == 3;
+    using XG = Xchg<DK, LAG>;
     static constexpr int BLK = ChunkBlock<DK, BF16, NSL>::BYTES;
-    static constexpr int XC = Xchg<DK>::BYTES;
+    static constexpr int XC = XG::BYTES;
     static constexpr int OST = OStage<OUT>::BYTES;
-    static constexpr int BYTES = NBUF * BLK + NSL * (XC + OST);
+    static constexpr int NOST = LAG ? 2 : 1;  // staging copies (slice s of copy j at j NSL OST + s OST)
+    static constexpr int BYTES = NBUF * BLK + NSL * (XC + NOST * OST);
+    __device__ static int ost(int ck) { return (LAG ? ck % 2 : 0) * NSL * OST; }
 };
 
 // Output wave H (rows 32 H .. 32 H + 31 of both slices; it writes out slice H's
-// staged outputs, which both output waves stage).  Every chunk starts with its
-// wait for its loads of the chunk (loads into LDS and registers count as
-// vector-memory operations, which the barrier alone does not wait for) and the
-// barrier that publishes the chunk with the chain waves' starting state.
+// staged outputs, which both output waves stage).  Every pass starts with its
+// wait for its loads (loads into LDS and registers count as vector-memory
+// operations, which the barrier alone does not wait for) and the barrier that
+// publishes the chunk with the chain waves' starting state.  Without LAG, pass
+// ck computes chunk ck alongside the chain waves (U handed over at the middle
+// barrier); with LAG, pass ck computes chunk ck - 1 from what the chain waves
+// published during it (one more pass at the end), and keeps chunk ck's gate
+// rows in registers for the next pass, so no wave reads a block after the
+// loads of a later chunk into it may have been issued.
 template <int DK, int OUT, bool BF16, int NSL, int NB, int H>
 __device__ __forceinline__ void out_wave(const ScanCtx<DK>& X, unsigned char* lds_raw, float scale) {
     using L = ScanLayout<DK, OUT, BF16, NSL, NB>;
+    using XG = typename L::XG;
+    using CB = ChunkBlock<DK, BF16, NSL>;
     static_assert(NSL == 2 && kC == 64, "two output waves, one per 32-row half of a chunk");
-    constexpr int NDMA = ChunkBlock<DK, BF16, NSL>::NLOAD / NSL;  // LDS loads per chunk and output wave
+    constexpr int NDMA = CB::NLOAD / NSL;  // LDS loads per chunk and output wave
     static_assert(NDMA < 64, "vmcnt field of the top wait");
-    const OutPlaces pl = {lds_raw + L::NBUF * L::BLK, lds_raw + L::NBUF * L::BLK + NSL * L::XC};
+    constexpr int LAGC = L::LAG ? 1 : 0;  // chunks the output waves run behind the chain waves
+    const unsigned char* xcb = lds_raw + L::NBUF * L::BLK;
+    unsigned char* ostb = lds_raw + L::NBUF * L::BLK + NSL * L::XC;
+    const int lg = (threadIdx.x & 63) >> 4;
     OutOps<DK, H> ops;
     load_out_ops<DK, H, 0>(ops, out_src(X, 0));
 #pragma unroll
@@ -1106,26 +1140,47 @@ __device__ __forceinline__ void out_wave(const ScanCtx<DK>& X, unsigned char* ld
     // the top wait: with three blocks everything but the last NDMA loads (those of chunk
     // ck + 1, issued last) has landed; with two, everything
     constexpr int VMC = NB == 3 ? NDMA : 0;
-    for (int ck = 0; ck < X.nch; ++ck) {
-        // this chunk's LDS block and registers, and the previous chunk's stores, have landed
+    f32x4 gp[2] = {};  // LAG: gate rows (gamma at this wave's rows) of the chunk computed next
+    for (int ck = 0; ck < X.nch + LAGC; ++ck) {
+        // this chunk's LDS block and registers, and the stores of two passes ago, have landed
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt((VMC & 15) | (VMC >> 4) << 14 | 0x0070);  // vmcnt(VMC) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (ck > 0) write_out<DK, OUT>(X, pl.ost + H * L::OST, ck - 1, H);
+        const int cw = ck - 1 - LAGC;  // the chunk staged in the previous pass
+        const int cc = ck - LAGC;      // the chunk this pass computes
+        // this pass's LDS offsets as opaque scalars (no per-access address registers)
+        int ow = L::ost(cw), od = ((ck + NB - 1) % NB) * L::BLK, og = (ck % L::NBUF) * L::BLK + CB::G0;
+        int ob = (cc % L::NBUF) * L::BLK, os = XG::sb(cc), ou = XG::ub(cc), oo = L::ost(cc);
+        asm volatile("" : "+s"(ow), "+s"(od), "+s"(og), "+s"(ob), "+s"(os), "+s"(ou), "+s"(oo));
+        if (cw >= 0) write_out<DK, OUT>(X, ostb + ow + H * L::OST, cw, H);
         // chunk ck + NB - 1 (the last chunks load themselves again into an idle block: harmless);
         // with two blocks its loads go out here, a whole chunk ahead of their use
-        const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + NB - 1, lds_raw + ((ck + NB - 1) % NB) * L::BLK, H);
+        const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + NB - 1, lds_raw + od, H);
         if constexpr (NB == 2) dma_slots<DK, BF16, NSL, 0, NDMA>(d);
-        out_chunk<DK, OUT, BF16, NSL, NB, H>(ops, out_src(X, ck + 1), lds_raw + (ck % L::NBUF) * L::BLK, pl, scale,
-                                             d);
+        f32x4 gn[2] = {gp[0], gp[1]};
+        if constexpr (L::LAG) {
+            if (ck < X.nch) {
+                const float* gam = reinterpret_cast<const float*>(lds_raw + og);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) gn[i] = *reinterpret_cast<const f32x4*>(gam + pair_row(2 * H + i, 4 * lg));
+            }
+        }
+        if (cc >= 0) {
+            const OutPlaces pl = {xcb + os, xcb + ou, ostb + oo};
+            out_chunk<DK, OUT, BF16, NSL, NB, H>(ops, out_src(X, cc + 1), lds_raw + ob, pl, scale, d, gp);
+        } else if constexpr (NB == 3) {
+            dma_slots<DK, BF16, NSL, 0, NDMA>(d);  // the first pass computes nothing; its loads still go out
+        }
+        gp[0] = gn[0];
+        gp[1] = gn[1];
     }
     // both output waves' staging of the last chunk is in place
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    write_out<DK, OUT>(X, pl.ost + H * L::OST, X.nch - 1, H);
+    write_out<DK, OUT>(X, ostb + L::ost(X.nch - 1) + H * L::OST, X.nch - 1, H);
     // the last chunks' repeated loads into LDS land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(0);
 }
@@ -1171,6 +1226,7 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
             return;  // uniform over the workgroup: every wave leaves before any barrier
         }
     }
+    using XG = typename L::XG;
     unsigned char* xc = lds_raw + L::NBUF * L::BLK + sl * L::XC;
     float* stp = a.state + (((size_t)s * a.h_v + X.h) * a.d_v + X.col0 + 16 * sl + c) * DK;
     // Each role runs its own loop (the same barriers per chunk), so the registers of one role's
@@ -1190,12 +1246,16 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
 #pragma unroll
         for (int u = 0; u < DK / 32; ++u) {
             sb[u] = pack_h8(st[2 * u], st[2 * u + 1]);
-            put_h8(xc + Xchg<DK>::SB, u, sb[u]);
+            put_h8(xc + XG::sb(0), u, sb[u]);
         }
         for (int ck = 0; ck < X.nch; ++ck) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            chain_chunk<DK, BF16, NSL>(st, sb, lds_raw + (ck % L::NBUF) * L::BLK, xc, sl);
+            // the chunk's LDS offsets as opaque scalars: otherwise loop strength reduction keeps
+            // one address register per operand read, rebuilt every chunk with a vector add
+            int ob = (ck % L::NBUF) * L::BLK, ou = XG::ub(ck), os = XG::sb(ck + 1);
+            asm volatile("" : "+s"(ob), "+s"(ou), "+s"(os));
+            chain_chunk<DK, BF16, NSL, L::LAG>(st, sb, lds_raw + ob, xc + ou, xc + os, sl);
             // the state after every state_interval-th full chunk, for prefix caching
             if (a.chunk_states != nullptr && (ck + 1) % a.state_interval == 0 && (ck + 1) * kC <= X.T) {
                 const size_t m = (size_t)sq.cst0 + (ck + 1) / a.state_interval - 1;
@@ -1206,7 +1266,13 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
                     for (int r = 0; r < 4; ++r) csp[pair_row(t, 4 * lg) + r] = st[t][r];
             }
         }
-        __syncthreads();  // the output waves' last barrier (their last chunk's staging is complete)
+        // the output waves' remaining barriers: LAG, the pass that computes the last chunk (after
+        // this wave's hand-offs of it have landed); then the one after their last staging
+        if constexpr (L::LAG) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        __syncthreads();
         // A value outside the f16 range on the way (an input V, a right-hand side R or the
         // state's f16 copy) makes the state non-finite, and it stays so: report it.
         bool finite = true;
