@@ -1072,14 +1072,12 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&st)[DK / 16], h8 (&sb)[DK / 
     chain_step<DK, BF16, NSL, LAG, 0>(x, st, blk, xu, xs, sl);
 }
 
-// One chunk of an output wave: blk is the chunk's LDS block (its gate rows;
-// LAG: gp holds them instead).
-template <int DK, int OUT, bool BF16, int NSL, int NB, int H>
-__device__ __forceinline__ void out_chunk(OutOps<DK, H>& ops, const OutSrc& nsrc, const unsigned char* blk,
-                                          const OutPlaces& pl, float scale, const DmaCtx& d, const f32x4 (&gp)[2]) {
+// The start of an output wave's chunk: the state it starts from (every slice's),
+// zero outputs, and the gate rows (LAG; otherwise read from the block later).
+template <int DK, int OUT, bool BF16, int NSL, int NB>
+__device__ __forceinline__ void out_begin(OutRegs<DK, NSL>& x, const OutPlaces& pl, const f32x4 (&gp)[2]) {
     using L = ScanLayout<DK, OUT, BF16, NSL, NB>;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    OutRegs<DK, NSL> x;
     x.gp[0] = gp[0];
     x.gp[1] = gp[1];
 #pragma unroll
@@ -1088,6 +1086,14 @@ __device__ __forceinline__ void out_chunk(OutOps<DK, H>& ops, const OutSrc& nsrc
         for (int u = 0; u < DK / 32; ++u) x.sb[q][u] = get_h8(pl.sb + q * L::XC, u);
         x.o[q][0] = x.o[q][1] = z;
     }
+}
+
+// One chunk of an output wave (after out_begin): blk is the chunk's LDS block
+// (its gate rows, unless LAG).
+template <int DK, int OUT, bool BF16, int NSL, int NB, int H>
+__device__ __forceinline__ void out_chunk(OutRegs<DK, NSL>& x, OutOps<DK, H>& ops, const OutSrc& nsrc,
+                                          const unsigned char* blk, const OutPlaces& pl, float scale,
+                                          const DmaCtx& d) {
     out_step<DK, OUT, BF16, NSL, NB, H, 0>(x, ops, nsrc, blk, pl, scale, d);
 }
 
@@ -1128,7 +1134,6 @@ __device__ __forceinline__ void out_wave(const ScanCtx<DK>& X, unsigned char* ld
     static_assert(NSL == 2 && kC == 64, "two output waves, one per 32-row half of a chunk");
     constexpr int NDMA = CB::NLOAD / NSL;  // LDS loads per chunk and output wave
     static_assert(NDMA < 64, "vmcnt field of the top wait");
-    constexpr int LAGC = L::LAG ? 1 : 0;  // chunks the output waves run behind the chain waves
     const unsigned char* xcb = lds_raw + L::NBUF * L::BLK;
     unsigned char* ostb = lds_raw + L::NBUF * L::BLK + NSL * L::XC;
     const int lg = (threadIdx.x & 63) >> 4;
@@ -1140,40 +1145,63 @@ __device__ __forceinline__ void out_wave(const ScanCtx<DK>& X, unsigned char* ld
     // the top wait: with three blocks everything but the last NDMA loads (those of chunk
     // ck + 1, issued last) has landed; with two, everything
     constexpr int VMC = NB == 3 ? NDMA : 0;
-    f32x4 gp[2] = {};  // LAG: gate rows (gamma at this wave's rows) of the chunk computed next
-    for (int ck = 0; ck < X.nch + LAGC; ++ck) {
-        // this chunk's LDS block and registers, and the stores of two passes ago, have landed
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt((VMC & 15) | (VMC >> 4) << 14 | 0x0070);  // vmcnt(VMC) lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        const int cw = ck - 1 - LAGC;  // the chunk staged in the previous pass
-        const int cc = ck - LAGC;      // the chunk this pass computes
-        // this pass's LDS offsets as opaque scalars (no per-access address registers)
-        int ow = L::ost(cw), od = ((ck + NB - 1) % NB) * L::BLK, og = (ck % L::NBUF) * L::BLK + CB::G0;
-        int ob = (cc % L::NBUF) * L::BLK, os = XG::sb(cc), ou = XG::ub(cc), oo = L::ost(cc);
-        asm volatile("" : "+s"(ow), "+s"(od), "+s"(og), "+s"(ob), "+s"(os), "+s"(ou), "+s"(oo));
-        if (cw >= 0) write_out<DK, OUT>(X, ostb + ow + H * L::OST, cw, H);
-        // chunk ck + NB - 1 (the last chunks load themselves again into an idle block: harmless);
-        // with two blocks its loads go out here, a whole chunk ahead of their use
-        const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + NB - 1, lds_raw + od, H);
-        if constexpr (NB == 2) dma_slots<DK, BF16, NSL, 0, NDMA>(d);
-        f32x4 gn[2] = {gp[0], gp[1]};
-        if constexpr (L::LAG) {
+    if constexpr (!L::LAG) {
+        // pass ck computes chunk ck (the gate rows come from its block at the middle barrier)
+        const OutPlaces pl = {xcb + XG::sb(0), xcb + XG::ub(0), ostb};
+        const f32x4 gz[2] = {};
+        for (int ck = 0; ck < X.nch; ++ck) {
+            // this chunk's LDS block and registers, and the previous chunk's stores, have landed
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt((VMC & 15) | (VMC >> 4) << 14 | 0x0070);  // vmcnt(VMC) lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            // the chunk's starting states first: the products wait on them, the stores below do not
+            OutRegs<DK, NSL> x;
+            out_begin<DK, OUT, BF16, NSL, NB>(x, pl, gz);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ck > 0) write_out<DK, OUT>(X, ostb + H * L::OST, ck - 1, H);
+            // chunk ck + NB - 1 (the last chunks load themselves again into an idle block: harmless);
+            // with two blocks its loads go out here, a whole chunk ahead of their use
+            const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + NB - 1, lds_raw + ((ck + NB - 1) % NB) * L::BLK, H);
+            if constexpr (NB == 2) dma_slots<DK, BF16, NSL, 0, NDMA>(d);
+            out_chunk<DK, OUT, BF16, NSL, NB, H>(x, ops, out_src(X, ck + 1), lds_raw + (ck % L::NBUF) * L::BLK, pl,
+                                                 scale, d);
+        }
+    } else {
+        f32x4 gp[2] = {};  // gate rows (gamma at this wave's rows) of the chunk computed next
+        for (int ck = 0; ck <= X.nch; ++ck) {
+            // this chunk's LDS block and registers, and the stores of two passes ago, have landed
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt((VMC & 15) | (VMC >> 4) << 14 | 0x0070);  // vmcnt(VMC) lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            const int cw = ck - 2;  // the chunk staged in the previous pass
+            const int cc = ck - 1;  // the chunk this pass computes
+            // this pass's LDS offsets as opaque scalars (otherwise loop strength reduction keeps one
+            // address register per access, rebuilt every pass)
+            int ow = L::ost(cw), od = ((ck + NB - 1) % NB) * L::BLK, og = (ck % L::NBUF) * L::BLK + CB::G0;
+            int ob = (cc % L::NBUF) * L::BLK, os = XG::sb(cc), ou = XG::ub(cc), oo = L::ost(cc);
+            asm volatile("" : "+s"(ow), "+s"(od), "+s"(og), "+s"(ob), "+s"(os), "+s"(ou), "+s"(oo));
+            if (cw >= 0) write_out<DK, OUT>(X, ostb + ow + H * L::OST, cw, H);
+            // chunk ck + 2 (the last chunks load themselves again into an idle block: harmless)
+            const DmaCtx d = dma_ctx<DK, BF16, NSL>(X, ck + NB - 1, lds_raw + od, H);
+            f32x4 gn[2] = {gp[0], gp[1]};
             if (ck < X.nch) {
                 const float* gam = reinterpret_cast<const float*>(lds_raw + og);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) gn[i] = *reinterpret_cast<const f32x4*>(gam + pair_row(2 * H + i, 4 * lg));
             }
+            if (cc >= 0) {
+                const OutPlaces pl = {xcb + os, xcb + ou, ostb + oo};
+                OutRegs<DK, NSL> x;
+                out_begin<DK, OUT, BF16, NSL, NB>(x, pl, gp);
+                out_chunk<DK, OUT, BF16, NSL, NB, H>(x, ops, out_src(X, cc + 1), lds_raw + ob, pl, scale, d);
+            } else {
+                dma_slots<DK, BF16, NSL, 0, NDMA>(d);  // the first pass computes nothing; its loads still go out
+            }
+            gp[0] = gn[0];
+            gp[1] = gn[1];
         }
-        if (cc >= 0) {
-            const OutPlaces pl = {xcb + os, xcb + ou, ostb + oo};
-            out_chunk<DK, OUT, BF16, NSL, NB, H>(ops, out_src(X, cc + 1), lds_raw + ob, pl, scale, d, gp);
-        } else if constexpr (NB == 3) {
-            dma_slots<DK, BF16, NSL, 0, NDMA>(d);  // the first pass computes nothing; its loads still go out
-        }
-        gp[0] = gn[0];
-        gp[1] = gn[1];
     }
     // both output waves' staging of the last chunk is in place
     asm volatile("" ::: "memory");
@@ -1251,10 +1279,10 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
         for (int ck = 0; ck < X.nch; ++ck) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            // the chunk's LDS offsets as opaque scalars: otherwise loop strength reduction keeps
+            // LAG: the chunk's LDS offsets as opaque scalars; otherwise loop strength reduction keeps
             // one address register per operand read, rebuilt every chunk with a vector add
             int ob = (ck % L::NBUF) * L::BLK, ou = XG::ub(ck), os = XG::sb(ck + 1);
-            asm volatile("" : "+s"(ob), "+s"(ou), "+s"(os));
+            if constexpr (L::LAG) asm volatile("" : "+s"(ob), "+s"(ou), "+s"(os));
             chain_chunk<DK, BF16, NSL, L::LAG>(st, sb, lds_raw + ob, xc + ou, xc + os, sl);
             // the state after every state_interval-th full chunk, for prefix caching
             if (a.chunk_states != nullptr && (ck + 1) % a.state_interval == 0 && (ck + 1) * kC <= X.T) {

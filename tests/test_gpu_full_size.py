@@ -6,6 +6,8 @@ configuration, against the fp64 oracle through the C ABI.
   writes (the benchmark's aliasing);
 - the same launch at 384 units (8 sequences x 48 layers), the instance with two
   row groups per wave and plain stores, on every unit;
+- the 22-node tree step in one launch (fused commit + tree verify) at batch 1,
+  with the same aliasing;
 - two launches on two streams back to back.
 Bars: max relative error <= 2e-3 on outputs and fp32 states, <= 1e-2 on the f16
 persisted states; the committed state bit-exact with its source."""
@@ -16,8 +18,8 @@ import torch
 import oracle
 from gated_deltanet_recurrence_gdn_amd import binding as gb
 from gated_deltanet_recurrence_gdn_amd import workloads as wl
-from helpers import (DEV, OUT_TOL, PERSIST_TOL, STATE_TOL, alloc_outputs, dev_inputs, max_rel, run_chain, say,
-                     small_inputs, to_host)
+from helpers import (DEV, OUT_TOL, PERSIST_TOL, STATE_TOL, alloc_outputs, dev_inputs, max_rel, run_chain, run_tree,
+                     say, small_inputs, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +76,40 @@ def test_fused_step_at_batch_one_full_size():
     # and bit for bit the two-launch step (commit, then verify)
     o2, p2, f2 = run_chain(t2, w.n_nodes, state=source.clone())
     assert torch.equal(out, o2) and torch.equal(per, p2) and torch.equal(fin, f2)
+
+
+def test_fused_tree_step_at_batch_one_full_size():
+    """The 22-node tree step in one launch, in the benchmark's configuration and aliasing: block 2's tree
+    verified over the out/persist buffers block 1's accepted node is committed from."""
+    w = wl.WORKLOADS["tree"]
+    seed = wl.WORKLOAD_SEEDS["tree"]
+    d1 = wl.make_inputs(w, seed=seed)
+    d2 = wl.make_inputs(w, seed=seed + 7919)
+    t1, t2 = dev_inputs(d1), dev_inputs(d2)
+    out, per = run_tree(t1, d1["parent"], w.n_nodes)
+    acc = torch.from_numpy(d1["accepted"]).to(DEV)
+    source = per[torch.arange(w.batch, device=DEV), acc.long()].float()
+    state = t1["state0"].clone()
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gb.gdn_commit_verify_tree(acc, per, d2["parent"], t2["q"], t2["k"], t2["v"], t2["alpha"], t2["beta"], state,
+                              out=out, persist=per, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    say("fused tree step, batch 1: accepted", d1["accepted"])
+    assert torch.equal(state, source)
+    ref = oracle.tree(d2["q"], d2["k"], d2["v"], d2["alpha"], d2["beta"], to_host(state), d2["parent"])
+    e = (max_rel(to_host(out), ref["out"]), max_rel(to_host(per), ref["nodes"]))
+    say(f"fused tree step vs oracle from the committed state: out {e[0]:.2e} persist {e[1]:.2e}")
+    assert e[0] <= OUT_TOL and e[1] <= PERSIST_TOL
+    # end to end in fp64: block 1's tree, the commit of its accepted node, block 2's tree
+    ref1 = oracle.tree(d1["q"], d1["k"], d1["v"], d1["alpha"], d1["beta"], d1["state0"], d1["parent"])
+    st64, _ = oracle.commit(d1["state0"].astype(np.float64), ref1["nodes"], d1["accepted"])
+    assert max_rel(to_host(state), st64) <= PERSIST_TOL  # the commit source is the f16 copy
+    ref2 = oracle.tree(d2["q"], d2["k"], d2["v"], d2["alpha"], d2["beta"], st64, d2["parent"])
+    assert max_rel(to_host(out), ref2["out"]) <= OUT_TOL
+    # and bit for bit the two-launch step (commit, then tree verify)
+    o2, p2 = run_tree({**t2, "state0": source.clone()}, d2["parent"], w.n_nodes)
+    assert torch.equal(out, o2) and torch.equal(per, p2)
 
 
 def test_fused_step_at_384_units_every_unit():
