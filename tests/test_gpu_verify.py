@@ -541,6 +541,55 @@ def test_fused_commit_verify_per_sequence_trees_through_slots():
     assert torch.equal(out, out_r) and torch.equal(per, per_r)
 
 
+def test_fused_fork_free_tree_in_two_row_groups_equals_fused_chain():
+    """A tree with no forks at a batch large enough for two row groups per wave: the fused tree step equals
+    the fused chain step bit for bit (node states, outputs and the committed state)."""
+    B, N = 12, 8
+    _, d1 = small_inputs(71, B, N, 16, 48, 128, 128)
+    _, d2 = small_inputs(72, B, N, 16, 48, 128, 128)
+    t1, t2 = dev_inputs(d1), dev_inputs(d2)
+    chain_par = np.arange(-1, N - 1, dtype=np.int32)
+    _, per1, fin1 = run_chain(t1, N)
+    acc = torch.tensor([0, 3, 6, 2, 5, 1, 4, 6, 0, 2, 3, 5], dtype=torch.int32, device=DEV)  # never N - 1
+    st_c, st_t = t1["state0"].clone(), t1["state0"].clone()
+    out_c, per_c, fin_c = alloc_outputs(t2, N)
+    out_t, per_t, _ = alloc_outputs(t2, N, final=False)
+    gb.gdn_commit_verify_chain(acc, per1, t2["q"], t2["k"], t2["v"], t2["alpha"], t2["beta"], st_c,
+                               final_prev=fin1, out=out_c, persist=per_c, final_state=fin_c)
+    gb.gdn_commit_verify_tree(acc, per1, chain_par, t2["q"], t2["k"], t2["v"], t2["alpha"], t2["beta"], st_t,
+                              out=out_t, persist=per_t)
+    torch.cuda.synchronize()
+    assert torch.equal(st_t, st_c)
+    assert torch.equal(out_t, out_c) and torch.equal(per_t, per_c)
+
+
+def test_fused_tree_plain_store_launches_equal_commit_then_verify():
+    """Per-sequence trees writing more than 256 MB of node states (plain stores, several launches of
+    sixteen trees): the fused step equals commit then tree verify bit for bit."""
+    rng = np.random.default_rng(73)
+    B, N = 40, 12
+    _, d1 = small_inputs(73, B, N, 16, 48, 128, 128, tree=True)
+    _, d2 = small_inputs(74, B, N, 16, 48, 128, 128, tree=True)
+    t1, t2 = dev_inputs(d1), dev_inputs(d2)
+    par1 = np.stack([wl.random_tree(N, 6, rng) for _ in range(B)])
+    par2 = np.stack([wl.random_tree(N, 6, rng) for _ in range(B)])
+    _, per1 = run_tree(t1, par1, N)
+    assert per1.numel() * 2 >= 256 << 20
+    acc = torch.from_numpy(rng.integers(0, N, B).astype(np.int32)).to(DEV)
+    st_ref = t1["state0"].clone()
+    assert _commit(acc, per1, st_ref) == 0
+    out_r, per_r = run_tree({**t2, "state0": st_ref}, par2, N)
+    st = t1["state0"].clone()
+    out, per, _ = alloc_outputs(t2, N, final=False)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gb.gdn_commit_verify_tree(acc, per1, par2, t2["q"], t2["k"], t2["v"], t2["alpha"], t2["beta"], st,
+                              out=out, persist=per, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(st, st_ref)
+    assert torch.equal(out, out_r) and torch.equal(per, per_r)
+
+
 def test_fused_tree_decode_loop_matches_oracle():
     """Three tree steps, the second and third fused with the commit of the step before, against the
     oracle applied step by step (commit of the accepted node's exact state)."""
