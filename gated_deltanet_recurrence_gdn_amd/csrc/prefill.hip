@@ -340,18 +340,25 @@ __device__ __forceinline__ void offdiag_column(PrepHead& W) {
 // in column order: once x[m] is final, A[t][m] x[m] leaves every later x[t].
 // Lane (bb, jc) holds column jc of its block's A (a[t] = A[t][jc]), so A[t][m] is
 // lane m's a[t], broadcast to the 16 lanes of the block's DPP row (row_newbcast:m):
-// two instructions per product, no LDS reads.
+// one instruction per product, no LDS reads.
+// x += bcast_M(a) n in one fused multiply-add (one rounding, as fmaf): the
+// two-operand v_fmac_f32 takes a DPP source, the three-operand v_fma_f32 the
+// compiler otherwise selects does not on gfx950 (it emitted a separate DPP move
+// per product).  a is never written by a vector instruction here (LDS loads
+// only), so the DPP read needs no wait states after its producer.
 template <int M>
-__device__ __forceinline__ float row_bcast(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + M, 0xF, 0xF, true));
+__device__ __forceinline__ float fmac_row_bcast(float x, float a, float n) {
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                 : "+v"(x)
+                 : "v"(a), "v"(n), "n"(M));
+    return x;
 }
 template <int M>
 __device__ __forceinline__ void fwd_column(const float (&a)[16], float (&x)[16]) {
     if constexpr (M < 15) {
-        float nx = -x[M];
-        asm("" : "+v"(nx));  // a plain operand: two-operand multiply-adds, not negated three-operand ones
+        const float nx = -x[M];
 #pragma unroll
-        for (int t = M + 1; t < 16; ++t) x[t] = fmaf(row_bcast<M>(a[t]), nx, x[t]);
+        for (int t = M + 1; t < 16; ++t) x[t] = fmac_row_bcast<M>(x[t], a[t], nx);
         fwd_column<M + 1>(a, x);
     }
 }
