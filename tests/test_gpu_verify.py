@@ -541,6 +541,32 @@ def test_fused_commit_verify_per_sequence_trees_through_slots():
     assert torch.equal(out, out_r) and torch.equal(per, per_r)
 
 
+@pytest.mark.parametrize("out_dtype,persist", [(torch.bfloat16, True), (torch.float16, True), (torch.float32, False)])
+def test_fused_tree_output_dtypes_and_no_persist(out_dtype, persist):
+    """The fused tree step with bf16 / f16 outputs, or persisting nothing, equals commit then tree verify
+    with the same options bit for bit."""
+    rng = np.random.default_rng(69)
+    B, N = 2, 16
+    _, d1 = small_inputs(69, B, N, 2, 4, 64, 64, tree=True)
+    _, d2 = small_inputs(70, B, N, 2, 4, 64, 64, tree=True)
+    t1, t2 = dev_inputs(d1), dev_inputs(d2)
+    p1, p2 = wl.random_tree(N, 8, rng), wl.random_tree(N, 8, rng)
+    _, per1 = run_tree(t1, p1, N)
+    acc = torch.tensor([11, 4], dtype=torch.int32, device=DEV)
+    st_ref = t1["state0"].clone()
+    assert _commit(acc, per1, st_ref) == 0
+    pdt = torch.float16 if persist else None
+    out_r, per_r = run_tree({**t2, "state0": st_ref}, p2, N, persist_dtype=pdt, out_dtype=out_dtype)
+    st = t1["state0"].clone()
+    out, per, _ = alloc_outputs(t2, N, pdt, out_dtype, final=False)
+    gb.gdn_commit_verify_tree(acc, per1, p2, t2["q"], t2["k"], t2["v"], t2["alpha"], t2["beta"], st, out=out,
+                              persist=per)
+    torch.cuda.synchronize()
+    assert torch.equal(st, st_ref) and torch.equal(out, out_r)
+    if persist:
+        assert torch.equal(per, per_r)
+
+
 def test_fused_fork_free_tree_in_two_row_groups_equals_fused_chain():
     """A tree with no forks at a batch large enough for two row groups per wave: the fused tree step equals
     the fused chain step bit for bit (node states, outputs and the committed state)."""
