@@ -1284,8 +1284,18 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
             put_h8(xc + XG::sb(0), u, sb[u]);
         }
         for (int ck = 0; ck < X.nch; ++ck) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+            if constexpr (L::LAG) {
+                // No wait for this wave's LDS writes: the output waves read the state copy written at
+                // the end of the chunk before only a pass later, and U of the chunk before in the pass
+                // after this barrier -- those writes precede this wave's operand reads of the chunk
+                // before, whose results it has used, so they are done.
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            } else {
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
             // LAG: the chunk's LDS offsets as opaque scalars; otherwise loop strength reduction keeps
             // one address register per operand read, rebuilt every chunk with a vector add
             int ob = (ck % L::NBUF) * L::BLK, ou = XG::ub(ck), os = XG::sb(ck + 1);
