@@ -977,6 +977,14 @@ __device__ __forceinline__ void chain_step(ChainRegs<DK>& x, f32x4 (&st)[DK / 16
         __builtin_amdgcn_sched_barrier(0);
         chain_step<DK, BF16, NSL, LAG, S + 1>(x, st, blk, xu, xs, sl);
     } else {
+        if constexpr (LAG) {
+            // U of this chunk has landed before the state copy goes out: the output waves read U
+            // after the next barrier, which this wave passes without waiting for its LDS writes
+            // (with few update products no operand read of this chunk follows the U writes)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            asm volatile("" ::: "memory");
+        }
         // the next chunk's starting state as the products' B operand, kept for this wave's
         // next K H and handed to the output waves
 #pragma unroll
@@ -1285,10 +1293,10 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
         }
         for (int ck = 0; ck < X.nch; ++ck) {
             if constexpr (L::LAG) {
-                // No wait for this wave's LDS writes: the output waves read the state copy written at
-                // the end of the chunk before only a pass later, and U of the chunk before in the pass
-                // after this barrier -- those writes precede this wave's operand reads of the chunk
-                // before, whose results it has used, so they are done.
+                // No wait for this wave's LDS writes: U of the chunk before, which the output waves
+                // read after this barrier, landed before that chunk's state copy went out (chain_step);
+                // the state copy is read a pass later and lands before this wave's first operand wait
+                // of this chunk (LDS operations complete in order).
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
