@@ -59,3 +59,40 @@ def test_noalloc_rejects_heads_beyond_the_array():
     assert ei.value.code == gb.CODES["GDN_ERR_WORKSPACE"]
     torch.cuda.synchronize()
     assert bool((st == 3.0).all())
+
+
+@pytest.mark.parametrize("w", [wl.Workload("custom", 2, 300, 2, 6, 64, 64),       # one prepare + scan pair
+                               wl.Workload("custom", 3, 1000, 16, 48, 128, 128)],  # segments of the array
+                         ids=["one-launch-pair", "segments"])
+def test_noalloc_prefill_replays_from_a_hip_graph(w):
+    """What the entry point is for: a call that allocates nothing can be
+    captured in a HIP graph.  Captured once (after an eager call), then
+    replayed three times with eager work and synchronizations between the
+    replays; every replay equals the eager call bit for bit (the state and the
+    outputs are reset before each replay, outside the graph)."""
+    d = wl.make_inputs(w, seed=950)
+    t = dev_inputs(d)
+    B, T, _, _ = t["q"].shape
+    Hv, dv = t["v"].shape[2], t["v"].shape[3]
+    st = t["state0"].clone()
+    out = torch.zeros(B, T, Hv, dv, device=DEV)
+    args = (t["q"], t["k"], t["v"], t["alpha"], t["beta"], st, out)
+    gb.gdn_prefill_chunked_noalloc(*args)
+    torch.cuda.synchronize()
+    ref_out, ref_st = out.clone(), st.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        gb.gdn_prefill_chunked_noalloc(*args)
+    torch.cuda.synchronize()
+    for i in range(3):
+        st.copy_(t["state0"])
+        out.zero_()
+        busy = torch.randn(1 << 20, device=DEV)
+        busy.mul_(2.0).sum().item()  # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("graph replay", i)
+        assert torch.equal(out, ref_out) and torch.equal(st, ref_st), i
