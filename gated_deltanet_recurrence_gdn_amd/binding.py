@@ -20,7 +20,8 @@ import os
 import numpy as np
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+# GDN_LIBRARY selects another build of the library (the debug build, libgdn_debug.so)
+_LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 _lib = None
 _raw_fns: dict = {}
 
@@ -35,7 +36,7 @@ GDN_PREFILL_SCRATCH_BYTES = 32 << 20
 STATUS = {
     0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE", -4: "GDN_ERR_ALIGN",
     -5: "GDN_ERR_PARENT", -6: "GDN_ERR_NODE", -7: "GDN_ERR_WORKSPACE", -8: "GDN_ERR_UNSUPPORTED",
-    -9: "GDN_ERR_HIP", -10: "GDN_ERR_SLOT", -11: "GDN_ERR_RANGE",
+    -9: "GDN_ERR_HIP", -10: "GDN_ERR_SLOT", -11: "GDN_ERR_RANGE", -12: "GDN_ERR_INTERNAL",
 }
 CODES = {v: k for k, v in STATUS.items()}
 

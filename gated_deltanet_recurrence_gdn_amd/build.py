@@ -4,6 +4,14 @@ Every source in csrc/ is compiled with hipcc for gfx950 only, in parallel,
 into _build/, then linked into libgdn.so inside the package directory, so the
 built library travels with the source tree.  Packed-fp32 instruction
 selection is turned off for all device code.
+
+build(debug=True) builds the same sources with -DGDN_DEBUG into
+libgdn_debug.so: the kernels' indices into the caller's arrays and the
+workspace (staging loads, state rows, node states, outputs, commits, the
+prefill's raw loads and workspace blocks) are checked, and one past its
+array's end is reported as GDN_ERR_INTERNAL through the call's status word and
+clamped into the array (the release build compiles the checks away).  Load it
+by setting GDN_LIBRARY to its path.
 """
 from __future__ import annotations
 
@@ -18,6 +26,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
+DEBUG_LIB = os.path.join(PKG, "libgdn_debug.so")
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -36,8 +45,8 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra: list[str], build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = [HIPCC, *COMMON, *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -45,21 +54,23 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra: list[str] | None = None, jobs: int = 8) -> str:
-    extra = list(extra or [])
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra: list[str] | None = None, jobs: int = 8, debug: bool = False) -> str:
+    extra = list(extra or []) + (["-DGDN_DEBUG"] if debug else [])
+    build_dir = BUILD + ("_debug" if debug else "")
+    lib = DEBUG_LIB if debug else LIB
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", flush=True)
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources", flush=True)
+    return lib
 
 
 if __name__ == "__main__":

@@ -97,7 +97,7 @@ VerifyArgs make_args(const gdn_shape* sh, const VerifyPlan& p, const void* q, co
     std::memset(&a, 0, sizeof(a));
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state = state; a.state_slot = state_slot;
     a.out = out; a.persist = persist; a.final_state = final_state; a.status = status;
-    a.seq0 = 0; a.n_seq = sh->batch; a.n_nodes = sh->n_nodes; a.h_qk = sh->h_qk; a.h_v = sh->h_v;
+    a.seq0 = 0; a.n_seq = sh->batch; a.batch = sh->batch; a.n_nodes = sh->n_nodes; a.h_qk = sh->h_qk; a.h_v = sh->h_v;
     a.d_v = sh->d_v; a.n_slots = sh->n_slots; a.group = sh->h_v / sh->h_qk;
     a.rows_per_wg = p.rows_per_wg; a.slices = p.slices;
     a.qkv_bf16 = sh->qkv_dtype == GDN_BF16; a.out_dtype = sh->out_dtype;
@@ -190,6 +190,7 @@ const char* gdn_status_string(int status) {
         case GDN_ERR_HIP: return "HIP launch failed";
         case GDN_ERR_SLOT: return "state slot out of range";
         case GDN_ERR_RANGE: return "a prefill value is outside the f16 range";
+        case GDN_ERR_INTERNAL: return "an index check of the debug build failed";
         default: return "unknown status";
     }
 }
@@ -480,6 +481,7 @@ int gdn_conv_commit(const gdn_conv_shape* shape, const int32_t* parent, int32_t 
     a.hist = static_cast<unsigned char*>(conv_state);
     a.accepted = accepted_node; a.state_slot = state_slot; a.status = status;
     a.n_nodes = N; a.keep = sh->width - 1; a.pieces = (int32_t)(row / 16); a.n_slots = sh->n_slots;
+    a.batch = B;
     a.wg_per_seq = (a.pieces + 255) / 256;
     a.chain = parent == nullptr;
     a.per_seq_tree = n_trees > 1;
@@ -566,6 +568,8 @@ int gdn_prefill_chunked(const gdn_shape* shape, const void* q, const void* k, co
     a.qkv_bf16 = sh->qkv_dtype == GDN_BF16; a.scale = sh->scale;
     a.varlen = 0;
     a.units = sh->batch * ((sh->n_nodes + GDN_PREFILL_CHUNK - 1) / GDN_PREFILL_CHUNK);
+    a.batch_total = sh->batch;
+    a.tokens_total = (int64_t)sh->batch * sh->n_nodes;
     PrefillSeqs seqs;
     std::memset(&seqs, 0, sizeof(seqs));
     hipError_t e = launch_prefill(a, seqs, sh->d_k, sh->out_dtype, static_cast<hipStream_t>(stream));
@@ -637,6 +641,9 @@ int gdn_prefill_varlen(const gdn_shape* shape, const int32_t* cu_seqlens, const 
     a.varlen = 1;
     a.chunk_states = chunk_states;
     a.state_interval = chunk_states != nullptr ? state_interval : 1;
+    a.batch_total = sh->batch;
+    a.tokens_total = sh->n_nodes;
+    a.n_chunk_states = chunk_states != nullptr ? gdn_prefill_boundary_states(cu_seqlens, sh->batch, state_interval) : 0;
     const long long span = (long long)GDN_PREFILL_CHUNK * a.state_interval;
     long long cst = 0;
     for (int s0 = 0; s0 < sh->batch; s0 += kMaxPrefillSeqs) {

@@ -39,14 +39,19 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a) {
     }
     const size_t e = ((size_t)tile * blockDim.x + threadIdx.x) * 8;
     if (e >= (size_t)a.head_elems) return;
-    float* dst = a.state + ((size_t)s * a.h_v + h) * a.head_elems + e;
+    [[maybe_unused]] const size_t heads = (size_t)a.batch * a.h_v;
+    float* dst = a.state + GDN_AT(((size_t)s * a.h_v + h) * a.head_elems + e, 8,
+                                  (size_t)(a.state_slot != nullptr ? a.n_slots : a.batch) * a.h_v * a.head_elems,
+                                  a.status);
     f32x4 x0, x1;
     if (a.final_state != nullptr && acc == a.n_nodes - 1) {
-        const float* src = a.final_state + ((size_t)b * a.h_v + h) * a.head_elems + e;
+        const float* src = a.final_state + GDN_AT(((size_t)b * a.h_v + h) * a.head_elems + e, 8,
+                                                  heads * a.head_elems, a.status);
         x0 = *reinterpret_cast<const f32x4*>(src);
         x1 = *reinterpret_cast<const f32x4*>(src + 4);
     } else {
-        const size_t off = (((size_t)b * a.n_nodes + acc) * a.h_v + h) * a.head_elems + e;
+        const size_t off = GDN_AT((((size_t)b * a.n_nodes + acc) * a.h_v + h) * a.head_elems + e, 8,
+                                  heads * a.n_nodes * a.head_elems, a.status);
         if constexpr (F16) {
             const f16x8 hv = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(a.persist) + off);
             x0 = f32x4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};

@@ -50,6 +50,9 @@ __global__ __launch_bounds__(256) void conv_commit_kernel(const ConvArgs a, cons
     const size_t row = (size_t)a.pieces * 16;
     unsigned char* hist = a.hist + (size_t)s * a.keep * row + (size_t)piece * 16;
     const unsigned char* xb = a.x + (size_t)b * a.n_nodes * row + (size_t)piece * 16;
+    // (debug build: every row read or written stays inside its array)
+    [[maybe_unused]] const size_t hist_end = (size_t)(a.state_slot != nullptr ? a.n_slots : a.batch) * a.keep * row;
+    [[maybe_unused]] const size_t x_end = (size_t)a.batch * a.n_nodes * row;
     // history row keep-1-k takes the ancestor at distance k when the path is that
     // long, else the old history row keep-1-k+depth; all sources are read first
     u32x4 v[kMaxConvKeep];
@@ -57,14 +60,18 @@ __global__ __launch_bounds__(256) void conv_commit_kernel(const ConvArgs a, cons
 #pragma unroll
     for (int k = 0; k < kMaxConvKeep; ++k) {
         if (k < a.keep) {
-            const unsigned char* src = k < depth ? xb + (size_t)n * row : hist + (size_t)(a.keep - 1 - k + depth) * row;
+            const unsigned char* src =
+                k < depth ? a.x + GDN_AT(xb - a.x + (size_t)n * row, 16, x_end, a.status)
+                          : a.hist + GDN_AT(hist - a.hist + (size_t)(a.keep - 1 - k + depth) * row, 16, hist_end, a.status);
             v[k] = *reinterpret_cast<const u32x4*>(src);
             if (k < depth) n = a.chain ? n - 1 : par[n];
         }
     }
 #pragma unroll
     for (int k = 0; k < kMaxConvKeep; ++k)
-        if (k < a.keep) *reinterpret_cast<u32x4*>(hist + (size_t)(a.keep - 1 - k) * row) = v[k];
+        if (k < a.keep)
+            *reinterpret_cast<u32x4*>(a.hist + GDN_AT(hist - a.hist + (size_t)(a.keep - 1 - k) * row, 16, hist_end,
+                                                      a.status)) = v[k];
 }
 
 }  // namespace

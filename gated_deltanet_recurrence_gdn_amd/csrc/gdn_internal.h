@@ -53,6 +53,22 @@ __host__ __device__ constexpr int sched_node(uint16_t c) { return c & 31; }
 __host__ __device__ constexpr int sched_restore_slot(uint16_t c) { return (c >> 6) & 15; }
 __host__ __device__ constexpr int sched_save_slot(uint16_t c) { return (c >> 11) & 15; }
 
+// Index checks of the debug build (-DGDN_DEBUG, the same source): an access
+// of `span` elements at index i of an array of n elements that would pass its
+// end is reported through the launch's status word (GDN_ERR_INTERNAL) and
+// clamped into the array, so it still touches valid memory.  The release
+// build compiles the checks away (GDN_AT(i, ...) is i).
+#ifdef GDN_DEBUG
+__device__ __forceinline__ size_t gdn_checked(size_t i, size_t span, size_t n, int32_t* status) {
+    if (i + span <= n) return i;
+    if (status != nullptr) status[0] = GDN_ERR_INTERNAL;
+    return n >= span ? n - span : 0;
+}
+#define GDN_AT(i, span, n, status) ::gdn::gdn_checked((size_t)(i), (size_t)(span), (size_t)(n), (status))
+#else
+#define GDN_AT(i, span, n, status) (i)
+#endif
+
 struct VerifyArgs {
     const void* q;
     const void* k;
@@ -67,6 +83,7 @@ struct VerifyArgs {
     int32_t* status;
     int32_t seq0;        // first sequence handled by this launch
     int32_t n_seq;       // sequences handled by this launch
+    int32_t batch;       // sequences of the call (the arrays' leading dimension)
     int32_t n_nodes;
     int32_t h_qk;
     int32_t h_v;
@@ -158,6 +175,7 @@ struct ConvArgs {
     int32_t wg_per_seq;   // workgroups per sequence
     int32_t n_slots;
     int32_t seq0;         // first sequence of this launch
+    int32_t batch;        // sequences of the call (the arrays' leading dimension)
     int32_t chain;        // 1: parents are n - 1
     int32_t per_seq_tree; // 0: tree 0 for every sequence; 1: tree b - seq0
 };
@@ -203,6 +221,10 @@ struct PrefillArgs {
     int32_t state_interval; // chunks between emitted states (>= 1 when chunk_states is set)
     int32_t seq_states;     // boundary states emitted per sequence (equal-length launches)
     int32_t seq0;           // first sequence of this launch (index of state_slot and of state rows)
+    // array extents, for the debug build's index checks
+    int32_t batch_total;    // sequences of the call (state rows without slots)
+    int64_t tokens_total;   // tokens of the q, k, v, alpha, beta and out arrays
+    int64_t n_chunk_states; // boundary states chunk_states holds
 };
 
 // Verify kernel launch.  d_k selects the instantiation; m_groups is the number

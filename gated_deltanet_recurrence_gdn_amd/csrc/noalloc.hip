@@ -72,6 +72,8 @@ extern "C" int gdn_prefill_chunked_noalloc(const gdn_shape* shape, const void* q
     a.qkv_bf16 = sh->qkv_dtype == GDN_BF16; a.scale = sh->scale;
     a.varlen = 1;
     a.state_interval = 1;
+    a.batch_total = sh->batch;
+    a.tokens_total = (int64_t)sh->batch * sh->n_nodes;
     const int T = sh->n_nodes;
     const long long nch = ceil_chunks(T);
     const int group = (int)(max_units < kMaxPrefillSeqs ? max_units : kMaxPrefillSeqs);

@@ -233,7 +233,8 @@ struct Gate {
 __device__ __forceinline__ Gate load_gate(const PrefillArgs& a, const SeqInfo& sq, int t0, int hv) {
     const int lane = threadIdx.x & 63;
     const bool in = t0 + lane < sq.T;
-    const size_t gi = ((size_t)sq.tok0 + (in ? t0 + lane : sq.T - 1)) * a.h_v + hv;
+    const size_t gi = GDN_AT(((size_t)sq.tok0 + (in ? t0 + lane : sq.T - 1)) * a.h_v + hv, 1,
+                             (size_t)a.tokens_total * a.h_v, a.status);
     Gate gt;
     gt.al = a.alpha[gi];
     gt.bt = a.beta[gi];
@@ -406,7 +407,8 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
             const int e = tid + 256 * n;
             const int t = e / (DK / 8), d = 8 * (e % (DK / 8));
             const int tc = t0 + t < sq.T ? t0 + t : sq.T - 1;
-            const size_t src = (((size_t)sq.tok0 + tc) * a.h_qk + g) * DK + d;
+            const size_t src = GDN_AT((((size_t)sq.tok0 + tc) * a.h_qk + g) * DK + d, 8,
+                                      (size_t)a.tokens_total * a.h_qk * DK, a.status);
             raw_load<BF16>(rk[n], a.k, src);
             raw_load<BF16>(rq[n], a.q, src);
         }
@@ -423,7 +425,8 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
     }
     // every value head's gates, one head per wave at a time
     for (int j = wave; j < a.group; j += 4) {
-        float* gw = reinterpret_cast<float*>(wsb + ws.G) + (unit_v0 + j) * 3 * kC;
+        float* gw = reinterpret_cast<float*>(wsb + ws.G) +
+                    GDN_AT((unit_v0 + j) * 3 * kC, 3 * kC, (size_t)a.units * a.h_v * 3 * kC, a.status);
         head_gates(j == wave ? gate0 : load_gate(a, sq, t0, g * a.group + j), gates + j * 2 * kC, gw);
     }
     __syncthreads();
@@ -444,8 +447,9 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         gram[jj] = acc;
     }
     {
-        _Float16* kw = reinterpret_cast<_Float16*>(wsb + ws.K) + unit_q * kC * DK;
-        _Float16* qw = reinterpret_cast<_Float16*>(wsb + ws.Q) + unit_q * kC * DK;
+        const size_t kq0 = GDN_AT(unit_q * kC * DK, kC * DK, (size_t)a.units * a.h_qk * kC * DK, a.status);
+        _Float16* kw = reinterpret_cast<_Float16*>(wsb + ws.K) + kq0;
+        _Float16* qw = reinterpret_cast<_Float16*>(wsb + ws.Q) + kq0;
         constexpr int PIECES = DK * kC / 8;
         for (int e = tid; e < 2 * PIECES; e += 256) {
             const int m = e / PIECES, i = e % PIECES;
@@ -501,7 +505,8 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
             for (int t = 0; t < 16; ++t) W.T(bb, bb)[t * kTS + jc] = x[t];  // after all reads of A_bb
         } else {
             // meanwhile the P fragments (two per wave)
-            _Float16* Pw = reinterpret_cast<_Float16*>(wsb + ws.P) + unit_v * kC * kC;
+            _Float16* Pw = reinterpret_cast<_Float16*>(wsb + ws.P) +
+                           GDN_AT(unit_v * kC * kC, kC * kC, (size_t)a.units * a.h_v * kC * kC, a.status);
             write_frag<false>(W, gl, Pw, 2 * (wave - 1));
             write_frag<false>(W, gl, Pw, 2 * (wave - 1) + 1);
         }
@@ -512,7 +517,8 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
         else if (wave == 2) offdiag_column<2>(W);
         __syncthreads();
         // T' = T diag(beta) fragments
-        _Float16* Tw = reinterpret_cast<_Float16*>(wsb + ws.T) + unit_v * kC * kC;
+        _Float16* Tw = reinterpret_cast<_Float16*>(wsb + ws.T) +
+                       GDN_AT(unit_v * kC * kC, kC * kC, (size_t)a.units * a.h_v * kC * kC, a.status);
         write_frag<true>(W, gl, Tw, wave);
         if (wave < 2) write_frag<true>(W, gl, Tw, wave + 4);
         __syncthreads();  // the next value head overwrites A and P
@@ -1271,7 +1277,9 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
     }
     using XG = typename L::XG;
     unsigned char* xc = lds_raw + L::NBUF * L::BLK + sl * L::XC;
-    float* stp = a.state + (((size_t)s * a.h_v + X.h) * a.d_v + X.col0 + 16 * sl + c) * DK;
+    float* stp = a.state + GDN_AT((((size_t)s * a.h_v + X.h) * a.d_v + X.col0 + 16 * sl + c) * DK, DK,
+                                  (size_t)(a.state_slot != nullptr ? a.n_slots : a.batch_total) * a.h_v * a.d_v * DK,
+                                  a.status);
     // Each role runs its own loop (the same barriers per chunk), so the registers of one role's
     // loop-carried values are not held by the other.  Every chunk starts with the output waves'
     // wait for their loads of the chunk (loads into LDS and registers count as vector-memory
@@ -1312,7 +1320,8 @@ __global__ __launch_bounds__(128 * NSL) void prefill_scan_kernel(const PrefillAr
             // the state after every state_interval-th full chunk, for prefix caching
             if (a.chunk_states != nullptr && (ck + 1) % a.state_interval == 0 && (ck + 1) * kC <= X.T) {
                 const size_t m = (size_t)sq.cst0 + (ck + 1) / a.state_interval - 1;
-                float* csp = a.chunk_states + ((m * a.h_v + X.h) * a.d_v + X.col0 + 16 * sl + c) * DK;
+                float* csp = a.chunk_states + GDN_AT(((m * a.h_v + X.h) * a.d_v + X.col0 + 16 * sl + c) * DK, DK,
+                                                     (size_t)a.n_chunk_states * a.h_v * a.d_v * DK, a.status);
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
 #pragma unroll

@@ -146,9 +146,12 @@ __device__ __forceinline__ void stage_load(StageRegs<NB>& r, const StageItem<DK>
     const int ekq = it.e < it.chunks ? it.e : it.chunks - 1;
     const int ev = it.e < it.nvb ? it.e : it.nvb - 1;
     const int eg = it.e < it.N ? it.e : it.N - 1;
-    const size_t kqi = (((size_t)b * N + ekq / LPR) * a.h_qk + g) * DK + 8 * (ekq % LPR);
+    const size_t kqi = GDN_AT((((size_t)b * N + ekq / LPR) * a.h_qk + g) * DK + 8 * (ekq % LPR), 8,
+                              (size_t)a.batch * N * a.h_qk * DK, a.status);
     const int n = ev / rows;
-    const size_t vi = (((size_t)b * N + n) * a.h_v + h) * DV + row0 + ev % rows;
+    const size_t vi = GDN_AT((((size_t)b * N + n) * a.h_v + h) * DV + row0 + ev % rows, 1,
+                             (size_t)a.batch * N * a.h_v * DV, a.status);
+    [[maybe_unused]] const size_t ng = (size_t)a.batch * N * a.h_v;  // gate entries
     const size_t vb = bf16 ? (vi * 2) & ~(size_t)3 : vi * 4;
     r.v_hi = bf16 && (vi & 1);
 #pragma unroll
@@ -160,9 +163,9 @@ __device__ __forceinline__ void stage_load(StageRegs<NB>& r, const StageItem<DK>
         r.q[i][0] = *reinterpret_cast<const u32x4*>(qp);
         r.q[i][1] = *reinterpret_cast<const u32x4*>(qp + (bf16 ? 0 : 16));
         r.v[i] = *reinterpret_cast<const uint32_t*>(static_cast<const unsigned char*>(in[i].v) + vb);
-        r.vbeta[i] = in[i].beta[((size_t)b * N + n) * a.h_v + h];
-        r.ga[i] = in[i].alpha[((size_t)b * N + eg) * a.h_v + h];
-        r.gb[i] = in[i].beta[((size_t)b * N + eg) * a.h_v + h];
+        r.vbeta[i] = in[i].beta[GDN_AT(((size_t)b * N + n) * a.h_v + h, 1, ng, a.status)];
+        r.ga[i] = in[i].alpha[GDN_AT(((size_t)b * N + eg) * a.h_v + h, 1, ng, a.status)];
+        r.gb[i] = in[i].beta[GDN_AT(((size_t)b * N + eg) * a.h_v + h, 1, ng, a.status)];
     }
 }
 
@@ -405,7 +408,8 @@ __device__ __forceinline__ void node_loop(float (&S)[M][EPL], const StageArea<DK
             // persisted states are written once and read later by commit, never by this kernel
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const size_t at = pbase + (uint32_t)node * pstride + (uint32_t)(m * RPG * DK + 8 * LPR * j);
+                const size_t at = GDN_AT(pbase + (uint32_t)node * pstride + (uint32_t)(m * RPG * DK + 8 * LPR * j), 8,
+                                         (size_t)a.batch * N * pstride, a.status);
                 if constexpr (PMODE == 1) {
                     const float* x = &S[m][8 * j];
                     const f16x8 hv = to_f16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
@@ -421,7 +425,8 @@ __device__ __forceinline__ void node_loop(float (&S)[M][EPL], const StageArea<DK
                 }
             }
             if (OUTS && out != nullptr && c == 0)
-                put_out<OUT>(out, obase + (uint32_t)node * ostride + (uint32_t)(m * RPG), o);
+                put_out<OUT>(out, GDN_AT(obase + (uint32_t)node * ostride + (uint32_t)(m * RPG), 1,
+                                         (size_t)a.batch * N * ostride, a.status), o);
         }
         if constexpr (FORKS) {
             if (code & kSchedSave) {
@@ -558,22 +563,31 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
     L.c = lane % LPR;
     L.r = lane / LPR;
     L.wrow = wave * R;  // first row of this wave inside the slice
+#ifdef GDN_DEBUG
+    // the lane's last row inside the head
+    L.wrow = (int)GDN_AT(L.row0 + L.wrow + L.r + (M - 1) * RPG, 1, DV, a.status) - (L.row0 + L.r + (M - 1) * RPG);
+#endif
     const size_t head_elems = (size_t)DV * DK;
+    // extents of the state array and of the per-sequence head arrays (debug build's checks)
+    [[maybe_unused]] const size_t state_end =
+        (size_t)(a.state_slot != nullptr ? a.n_slots : a.batch) * a.h_v * head_elems;
+    [[maybe_unused]] const size_t heads_end = (size_t)a.batch * a.h_v * head_elems;
     float* cache_head = (a.state_w != nullptr ? a.state_w : const_cast<float*>(a.state)) +
-                        ((size_t)s * a.h_v + h) * head_elems;
+                        GDN_AT(((size_t)s * a.h_v + h) * head_elems, head_elems, state_end, a.status);
     // The starting state: the cached state, or (fused commit) the previous step's accepted
     // node -- its exact fp32 final state when the whole chain was accepted, else (and
     // always after a tree) its persisted copy, widened to fp32 -- which is also written
     // back to the state cache.
     // Its loads are issued first; the staging's LDS work runs while they are in flight.
-    const void* src_head = a.state + ((size_t)s * a.h_v + h) * head_elems;
+    const void* src_head = a.state + GDN_AT(((size_t)s * a.h_v + h) * head_elems, head_elems, state_end, a.status);
     bool src_f16 = false;
     if constexpr (FUSED) {
         if (!TREE && a.final_prev != nullptr && acc == N - 1) {
-            src_head = a.final_prev + ((size_t)b * a.h_v + h) * head_elems;
+            src_head = a.final_prev + GDN_AT(((size_t)b * a.h_v + h) * head_elems, head_elems, heads_end, a.status);
         } else {
             src_f16 = a.persist_prev_f16 != 0;
-            const size_t off = (((size_t)b * N + acc) * a.h_v + h) * head_elems;
+            const size_t off = GDN_AT((((size_t)b * N + acc) * a.h_v + h) * head_elems, head_elems,
+                                      heads_end * N, a.status);
             src_head = src_f16 ? static_cast<const void*>(static_cast<const _Float16*>(a.persist_prev) + off)
                                : static_cast<const void*>(static_cast<const float*>(a.persist_prev) + off);
         }
@@ -629,7 +643,9 @@ __device__ __forceinline__ void verify_body(const VerifyArgs& a, const uint16_t*
         // 4. final state (chains): the exact fp32 state after node N-1
         if constexpr (!TREE) {
             if (a.final_state != nullptr)
-                store_state_rows<DK, M, EPL, NT>(a.final_state + ((size_t)b * a.h_v + h) * head_elems, L, S);
+                store_state_rows<DK, M, EPL, NT>(
+                    a.final_state + GDN_AT(((size_t)b * a.h_v + h) * head_elems, head_elems, heads_end, a.status), L,
+                    S);
         }
     }
 }

@@ -43,6 +43,10 @@
  *    code into *status when `status` is not NULL.  The caller zeroes
  *    *status beforehand; concurrent errors leave one of their codes.
  *  - A failed kernel launch returns GDN_ERR_HIP.
+ *  - The library built with -DGDN_DEBUG (libgdn_debug.so) checks the indices
+ *    its kernels form into the caller's arrays and the workspace: one past
+ *    its array's end stores GDN_ERR_INTERNAL into *status and is clamped into
+ *    the array.  The release build carries no such checks.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -71,7 +75,8 @@ typedef enum gdn_status {
     GDN_ERR_UNSUPPORTED = -8, /* valid request this library does not implement */
     GDN_ERR_HIP = -9,         /* the HIP runtime refused the launch */
     GDN_ERR_SLOT = -10,       /* device: state slot outside [0, n_slots) */
-    GDN_ERR_RANGE = -11       /* device: a prefill value left the f16 range of the matrix-core operands */
+    GDN_ERR_RANGE = -11,      /* device: a prefill value left the f16 range of the matrix-core operands */
+    GDN_ERR_INTERNAL = -12    /* device, debug build only: an index check inside a kernel failed */
 } gdn_status;
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype;
