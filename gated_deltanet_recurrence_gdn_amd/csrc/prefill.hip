@@ -66,6 +66,14 @@ __device__ __forceinline__ h8 to_h8(const float (&x)[8]) {
     return __builtin_convertvector(v, h8);
 }
 
+// Two accumulator tiles (rows 4 g + r of each) as one f16 operand fragment:
+// whole-vector conversions (one packed convert per pair, round to nearest even).
+__device__ __forceinline__ h8 pack_h8(const f32x4& lo, const f32x4& hi) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 a = __builtin_convertvector(lo, h4), b = __builtin_convertvector(hi, h4);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Raw 16-byte loads of 8 elements (bf16 or fp32 source, BF16 fixed at compile
 // time) kept in registers until they are converted into LDS; fp32 needs two.
 // Loads are unconditional (callers clamp the index), so no load waits on a
@@ -170,34 +178,39 @@ __device__ __forceinline__ SeqInfo seq_info(const PrefillArgs& a, const PrefillS
 // ---------------------------------------------------------------------------
 // prepare: one (sequence, chunk, q/k head) per workgroup
 // ---------------------------------------------------------------------------
-// K and Q are loaded and K K^T, Q K^T formed once per q/k head on the matrix
-// cores: 20 lower 16 x 16 tiles, five per wave, kept in the registers of the
-// wave that formed them.  Every value head's gates are formed up front, one
-// head per wave.  Then the four waves take the head's value heads one after
-// another, together: each turns its K K^T tiles into tiles of
-// A = strict_lower(beta_t Gamma_{t,i} k_t.k_i) and its Q K^T tiles into tiles of
-// P = Gamma o tril(Q K^T); one wave forms the diagonal 16 x 16 blocks of
-// T = (I + A)^-1 by forward substitution while the others write P's fragments;
-// the off-diagonal blocks follow one column per wave (three, two and one
-// blocks, v_mfma_f32_16x16x4_f32); then all four write T' = T diag(beta).
+// K and Q are loaded and, once per q/k head on the matrix cores, the 10 lower
+// 16 x 16 tiles of K K^T (four on wave 0, two on each other wave) and, on
+// waves 1-3, the 12 tiles of (Q K^T)^T that P's six fragments need, kept in
+// the registers of the wave that formed them.  The (Q K^T)^T tiles take keys
+// in rows pair_row(pi, .) and queries in columns pair_row(pt, .), so tiles
+// (2v, p) and (2v + 1, p) are P's fragment (p, v) as they stand: P's
+// fragments go from those registers to the workspace, never through LDS.
+// Every value head's gates are formed up front, one head per wave.  Then the
+// value heads, one after another: the K K^T tiles become the tiles of
+// A = strict_lower(beta_t Gamma_{t,i} k_t.k_i) in LDS; one wave forms the
+// diagonal 16 x 16 blocks of T = (I + A)^-1 by forward substitution while the
+// others write P = Gamma o tril(Q K^T); the off-diagonal blocks follow one
+// column per wave (three, two and one blocks, v_mfma_f32_16x16x4_f32); then
+// all four write T' = T diag(beta) and, in the same phase, form the next value
+// head's A in the other of two A buffers (three barriers per value head).
 // Lower tiles are kept tile-major: tile (it, jt), jt <= it, is tile number
 // it (it + 1) / 2 + jt, element (r, c) at r * kTS + c: rows padded to 20 floats
 // (16-byte aligned), so the column reads of the matrix-core operands and the
 // row reads of the output fragments fall on different banks.  The working set
-// of one value head reuses the LDS of the K, Q chunk; four workgroups fit a CU.
+// reuses the LDS of the K, Q chunk; four workgroups fit a CU.
 __device__ __forceinline__ constexpr int tix(int it, int jt) { return it * (it + 1) / 2 + jt; }
 constexpr int kTS = 20;           // row stride of a 16 x 16 fp32 tile in LDS (floats)
 constexpr int kTile = 16 * kTS;   // floats per tile
 __device__ __forceinline__ constexpr int tile_row(int tx) { return tx < 1 ? 0 : tx < 3 ? 1 : tx < 6 ? 2 : 3; }
 
-// The working set of one value head.  The diagonal tiles of T replace those
-// of A (each is read in full before it is overwritten); the off-diagonal
-// tiles of T have their own slots.
+// The working set: A of two value heads (buffer j % 2 for head j, so the
+// next head's A is formed while this head's T' goes out) and the T of one.
+// The diagonal tiles of T replace those of its head's A (each is read in full
+// before it is overwritten); the off-diagonal tiles of T have their own slots.
 struct PrepHead {
-    float A[10][kTile];  // strict lower beta Gamma K K^T; diagonal tiles then hold T
-    float To[6][kTile];  // off-diagonal tiles of T = (I + A)^-1
-    float P[10][kTile];  // Gamma o tril(Q K^T)
-    __device__ float* T(int it, int jt) { return it == jt ? A[tix(it, it)] : To[tix(it, jt) - it]; }
+    float A[2][10][kTile];  // strict lower beta Gamma K K^T; diagonal tiles then hold T
+    float To[6][kTile];     // off-diagonal tiles of T = (I + A)^-1
+    __device__ float* T(int b, int it, int jt) { return it == jt ? A[b][tix(it, it)] : To[tix(it, jt) - it]; }
 };
 
 // LDS: the gates of the q/k head's `group` value heads ([group][2][64] fp32:
@@ -264,29 +277,27 @@ __device__ __forceinline__ void head_gates(const Gate gt, float* gl, float* gw) 
     gw[2 * kC + lane] = exp2_fast(lC - x);
 }
 
-// Fragment f (0 .. 5, the lower-triangular (tile, block) pairs in the scan's
-// order) of T' = T diag(beta) or of P, f16, to the workspace.  Lane (c, lg)
-// writes row pair_row(tile, c), columns 32 blk + 8 lg .. + 8.
-template <bool TPRIME>
-__device__ __forceinline__ void write_frag(PrepHead& W, const float* gl, _Float16* dst, int f) {
+// The (tile, block) pair of fragment f (0 .. 5) of a lower-triangular C x C
+// operand, in the scan's order (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
+__device__ __forceinline__ constexpr int frag_tile(int f) { return f < 2 ? f : 2 + (f - 2) / 2; }
+__device__ __forceinline__ constexpr int frag_blk(int f) { return f < 2 ? 0 : (f - 2) % 2; }
+
+// Fragment f of T' = T diag(beta) (T of buffer b), f16, to the workspace.
+// Lane (c, lg) writes row pair_row(tile, c), columns 32 blk + 8 lg .. + 8.
+__device__ __forceinline__ void write_tprime(PrepHead& W, int b, const float* gl, _Float16* dst, int f) {
     const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
-    const int tile = f < 2 ? f : 2 + (f - 2) / 2, blk = f < 2 ? 0 : (f - 2) % 2;
+    const int tile = frag_tile(f), blk = frag_blk(f);
     const int t = pair_row(tile, c), i0 = 32 * blk + 8 * lg;
     const int it = t >> 4, jt = i0 >> 4;
     h8 v;
     if (jt <= it) {
-        const float* row = (TPRIME ? W.T(it, jt) : W.P[tix(it, jt)]) + (t & 15) * kTS + (i0 & 15);
+        const float* row = W.T(b, it, jt) + (t & 15) * kTS + (i0 & 15);
         const f32x4 xa = *reinterpret_cast<const f32x4*>(row), xb = *reinterpret_cast<const f32x4*>(row + 4);
         float x[8];
-        if constexpr (TPRIME) {
-            const f32x4 ba = *reinterpret_cast<const f32x4*>(gl + kC + i0);
-            const f32x4 bb = *reinterpret_cast<const f32x4*>(gl + kC + i0 + 4);
+        const f32x4 ba = *reinterpret_cast<const f32x4*>(gl + kC + i0);
+        const f32x4 bb = *reinterpret_cast<const f32x4*>(gl + kC + i0 + 4);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = i0 + e <= t ? (e < 4 ? xa[e] * ba[e] : xb[e - 4] * bb[e - 4]) : 0.f;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = e < 4 ? xa[e] : xb[e - 4];  // zero above the diagonal
-        }
+        for (int e = 0; e < 8; ++e) x[e] = i0 + e <= t ? (e < 4 ? xa[e] * ba[e] : xb[e - 4] * bb[e - 4]) : 0.f;
         v = to_h8(x);
     } else {
 #pragma unroll
@@ -304,27 +315,27 @@ __device__ __forceinline__ void write_frag(PrepHead& W, const float* gl, _Float1
 // columns need only the diagonal blocks, so they run side by side on three
 // waves (v_mfma_f32_16x16x4_f32).
 template <int JB>
-__device__ __forceinline__ void offdiag_column(PrepHead& W) {
+__device__ __forceinline__ void offdiag_column(PrepHead& W, int b) {
     const int lane = threadIdx.x & 63, c = lane & 15, lg = lane >> 4;
     constexpr int N = 3 - JB;  // blocks below the diagonal
-    const float* Tjj = W.T(JB, JB);
+    const float* Tjj = W.T(b, JB, JB);
     f32x4 tcol[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         const int ib = JB + 1 + n;
-        const float* Aij = W.A[tix(ib, JB)];
+        const float* Aij = W.A[b][tix(ib, JB)];
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             y = __builtin_amdgcn_mfma_f32_16x16x4f32(Aij[c * kTS + 4 * s + lg], Tjj[(4 * s + lg) * kTS + c], y, 0, 0, 0);
 #pragma unroll
         for (int m = 0; m < n; ++m) {
-            const float* Aik = W.A[tix(ib, JB + 1 + m)];
+            const float* Aik = W.A[b][tix(ib, JB + 1 + m)];
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 y = __builtin_amdgcn_mfma_f32_16x16x4f32(Aik[c * kTS + 4 * lg + s], tcol[m][s], y, 0, 0, 0);
         }
-        const float* Ti = W.T(ib, ib);
+        const float* Ti = W.T(b, ib, ib);
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -334,7 +345,7 @@ __device__ __forceinline__ void offdiag_column(PrepHead& W) {
 #pragma unroll
     for (int n = 0; n < N; ++n)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) W.T(JB + 1 + n, JB)[(4 * lg + r) * kTS + c] = tcol[n][r];
+        for (int r = 0; r < 4; ++r) W.T(b, JB + 1 + n, JB)[(4 * lg + r) * kTS + c] = tcol[n][r];
 }
 
 // Forward substitution of (I + A) x = e_jc for a strictly lower 16 x 16 block A,
@@ -431,25 +442,46 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
     }
     __syncthreads();
 
-    // 2. K K^T and Q K^T on the lower 16 x 16 tiles (20 jobs over the four waves, job
-    //    wave + 4 jj: matrix job / 10, tile job % 10), kept in registers; K and Q ->
-    //    workspace in fragment order
-    f32x4 gram[5];
+    // 2. On the matrix cores (registers of the wave that forms them): K K^T's lower tiles
+    //    (wave 0 tiles 0-3, wave w > 0 tiles 2 + 2 w and 3 + 2 w) and, on waves 1-3, the
+    //    (Q K^T)^T tiles of P's fragments 2 (w - 1) and 2 (w - 1) + 1: tiles (2 v, p) and
+    //    (2 v + 1, p) of fragment (p, v), keys in rows pair_row(2 v + h, .), queries in
+    //    columns pair_row(p, .).  K and Q -> workspace in fragment order.
+    const int nkk = wave == 0 ? 4 : 2;          // K K^T tiles of this wave (uniform)
+    const int kk0 = wave == 0 ? 0 : 2 + 2 * wave;
+    f32x4 kk[4], pq[2][2];
 #pragma unroll
-    for (int jj = 0; jj < 5; ++jj) {
-        const int job = wave + 4 * jj;
-        const int mat = job / 10, tx = job % 10;
-        const int it = tile_row(tx), jt = tx - it * (it + 1) / 2;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < 4; ++jj) {
+        if (jj < nkk) {
+            const int tx = kk0 + jj;
+            const int it = tile_row(tx), jt = tx - it * (it + 1) / 2;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks)
-            acc = mfma16(frag(mat ? Qf : Kf, kLdK, 16 * it, 32 * ks, lane), frag(Kf, kLdK, 16 * jt, 32 * ks, lane), acc);
-        gram[jj] = acc;
+            for (int ks = 0; ks < KSD; ++ks)
+                acc = mfma16(frag(Kf, kLdK, 16 * it, 32 * ks, lane), frag(Kf, kLdK, 16 * jt, 32 * ks, lane), acc);
+            kk[jj] = acc;
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int sf = 0; sf < 2; ++sf) {
+            const int f = 2 * (wave - 1) + sf, p = frag_tile(f), v = frag_blk(f);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                const _Float16* kr = Kf + pair_row(2 * v + h, c) * kLdK + 8 * lg;
+                const _Float16* qr = Qf + pair_row(p, c) * kLdK + 8 * lg;
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks)
+                    acc = mfma16(*reinterpret_cast<const h8*>(kr + 32 * ks), *reinterpret_cast<const h8*>(qr + 32 * ks),
+                                 acc);
+                pq[sf][h] = acc;
+            }
+        }
     }
     {
-        const size_t kq0 = GDN_AT(unit_q * kC * DK, kC * DK, (size_t)a.units * a.h_qk * kC * DK, a.status);
-        _Float16* kw = reinterpret_cast<_Float16*>(wsb + ws.K) + kq0;
-        _Float16* qw = reinterpret_cast<_Float16*>(wsb + ws.Q) + kq0;
+        _Float16* kw = reinterpret_cast<_Float16*>(wsb + ws.K) + unit_q * kC * DK;
+        _Float16* qw = reinterpret_cast<_Float16*>(wsb + ws.Q) + unit_q * kC * DK;
         constexpr int PIECES = DK * kC / 8;
         for (int e = tid; e < 2 * PIECES; e += 256) {
             const int m = e / PIECES, i = e % PIECES;
@@ -459,69 +491,91 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
             *reinterpret_cast<h8*>((m == 0 ? kw : qw) + 8 * i) = v;
         }
     }
-    __syncthreads();  // K, Q are dead: the value-head working set takes their bytes
+    __syncthreads();  // K, Q are dead: the working set takes their bytes
 
-    // 3. the value heads one after another, all four waves on each
-    for (int j = 0; j < a.group; ++j) {
-        const float* gl = gates + j * 2 * kC;  // l2_t [64], beta_t [64]
-        const size_t unit_v = unit_v0 + j;
-        // A and P tiles from this wave's Gram tiles
+    // This wave's K K^T tiles -> the A tiles of value head j in buffer b: strictly lower (i < t),
+    // carrying beta_t.  Selects, not branches: i and t vary over the wave.
+    auto form_a = [&](int j, int b) {
+        const float* gl = gates + j * 2 * kC;
 #pragma unroll
-        for (int jj = 0; jj < 5; ++jj) {
-            const int job = wave + 4 * jj;
-            const int mat = job / 10, tx = job % 10;
-            const int it = tile_row(tx), jt = tx - it * (it + 1) / 2;
-            const f32x4 lt = *reinterpret_cast<const f32x4*>(gl + 16 * it + 4 * lg);
-            const f32x4 bt = *reinterpret_cast<const f32x4*>(gl + kC + 16 * it + 4 * lg);
-            const float li = gl[16 * jt + c];
-            const int i = 16 * jt + c;
-            float* dst = mat ? W.P[tx] : W.A[tx];
-            // P keeps the diagonal (i <= t); A is strictly lower (i < t) and carries beta_t.
-            // Selects, not branches: mat is uniform over the wave, i and t are not.
-            const int below = mat ? 0 : 1;
+        for (int jj = 0; jj < 4; ++jj) {
+            if (jj < nkk) {
+                const int tx = kk0 + jj;
+                const int it = tile_row(tx), jt = tx - it * (it + 1) / 2;
+                const f32x4 lt = *reinterpret_cast<const f32x4*>(gl + 16 * it + 4 * lg);
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(gl + kC + 16 * it + 4 * lg);
+                const float li = gl[16 * jt + c];
+                const int i = 16 * jt + c;
+                float* dst = W.A[b][tx];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * it + 4 * lg + r;
-                const float e2 = exp2_fast(lt[r] - li);
-                const float v = (mat ? e2 : bt[r] * e2) * gram[jj][r];
-                dst[(4 * lg + r) * kTS + c] = i + below <= t ? v : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * it + 4 * lg + r;
+                    const float e2 = exp2_fast(lt[r] - li);
+                    dst[(4 * lg + r) * kTS + c] = i < t ? bt[r] * e2 * kk[jj][r] : 0.f;
+                }
             }
         }
-        __syncthreads();
+    };
+    // Waves 1-3: P's fragments 2 (w - 1) and 2 (w - 1) + 1 of value head j, straight from the
+    // (Q K^T)^T registers: lane (c, lg) holds queries t = pair_row(p, c) and keys
+    // i = pair_row(2 v + h, 4 lg + r) = 32 v + 8 lg + 4 h + r.
+    auto write_p = [&](int j, _Float16* Pw) {
+        const float* gl = gates + j * 2 * kC;
+#pragma unroll
+        for (int sf = 0; sf < 2; ++sf) {
+            const int f = 2 * (wave - 1) + sf, p = frag_tile(f), v = frag_blk(f);
+            const int t = pair_row(p, c);
+            const float lt = gl[t];
+            f32x4 x[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int i0 = 32 * v + 8 * lg + 4 * h;
+                const f32x4 li = *reinterpret_cast<const f32x4*>(gl + i0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[h][r] = i0 + r <= t ? exp2_fast(lt - li[r]) * pq[sf][h][r] : 0.f;
+            }
+            *reinterpret_cast<h8*>(Pw + (f * 64 + lane) * 8) = pack_h8(x[0], x[1]);
+        }
+    };
+
+    // 3. the value heads one after another, all four waves on each; head j's A in buffer j % 2
+    form_a(0, 0);
+    __syncthreads();
+    for (int j = 0; j < a.group; ++j) {
+        const int b = j & 1;
+        const float* gl = gates + j * 2 * kC;  // l2_t [64], beta_t [64]
+        const size_t unit_v = unit_v0 + j;
         if (wave == 0) {
             // diagonal 16 x 16 blocks of T by forward substitution, one column of one block
             // per lane: lane (bb, jc) reads column jc of A_bb once, then solves for column jc
             // of T_bb (see fwd_column)
             const int bb = lane >> 4, jc = lane & 15;
-            const float* Ab = W.A[tix(bb, bb)];
-            float a[16], x[16];
+            const float* Ab = W.A[b][tix(bb, bb)];
+            float av[16], x[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                a[t] = Ab[t * kTS + jc];
+                av[t] = Ab[t * kTS + jc];
                 x[t] = t == jc ? 1.f : 0.f;
             }
-            fwd_column<0>(a, x);
+            fwd_column<0>(av, x);
 #pragma unroll
-            for (int t = 0; t < 16; ++t) W.T(bb, bb)[t * kTS + jc] = x[t];  // after all reads of A_bb
+            for (int t = 0; t < 16; ++t) W.T(b, bb, bb)[t * kTS + jc] = x[t];  // after all reads of A_bb
         } else {
-            // meanwhile the P fragments (two per wave)
-            _Float16* Pw = reinterpret_cast<_Float16*>(wsb + ws.P) +
-                           GDN_AT(unit_v * kC * kC, kC * kC, (size_t)a.units * a.h_v * kC * kC, a.status);
-            write_frag<false>(W, gl, Pw, 2 * (wave - 1));
-            write_frag<false>(W, gl, Pw, 2 * (wave - 1) + 1);
+            // meanwhile P's fragments (two per wave)
+            write_p(j, reinterpret_cast<_Float16*>(wsb + ws.P) + unit_v * kC * kC);
         }
         __syncthreads();
         // the off-diagonal blocks, one column per wave
-        if (wave == 0) offdiag_column<0>(W);
-        else if (wave == 1) offdiag_column<1>(W);
-        else if (wave == 2) offdiag_column<2>(W);
+        if (wave == 0) offdiag_column<0>(W, b);
+        else if (wave == 1) offdiag_column<1>(W, b);
+        else if (wave == 2) offdiag_column<2>(W, b);
         __syncthreads();
-        // T' = T diag(beta) fragments
-        _Float16* Tw = reinterpret_cast<_Float16*>(wsb + ws.T) +
-                       GDN_AT(unit_v * kC * kC, kC * kC, (size_t)a.units * a.h_v * kC * kC, a.status);
-        write_frag<true>(W, gl, Tw, wave);
-        if (wave < 2) write_frag<true>(W, gl, Tw, wave + 4);
-        __syncthreads();  // the next value head overwrites A and P
+        // T' = T diag(beta) fragments, and the next value head's A in the other buffer
+        _Float16* Tw = reinterpret_cast<_Float16*>(wsb + ws.T) + unit_v * kC * kC;
+        write_tprime(W, b, gl, Tw, wave);
+        if (wave < 2) write_tprime(W, b, gl, Tw, wave + 4);
+        if (j + 1 < a.group) form_a(j + 1, b ^ 1);
+        __syncthreads();  // the next value head overwrites T's tiles
     }
 }
 
@@ -554,12 +608,6 @@ __global__ __launch_bounds__(256) void prefill_prepare_kernel(const PrefillArgs 
 // each output wave's wait for its loads of the chunk (publishing the chunk,
 // and telling every wave that the block of the chunk before is free), and in
 // the middle, where the chain waves hand U to the output waves.
-__device__ __forceinline__ h8 pack_h8(const f32x4& lo, const f32x4& hi) {
-    // whole-vector conversions (one packed convert per pair, round to nearest even)
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    const h4 a = __builtin_convertvector(lo, h4), b = __builtin_convertvector(hi, h4);
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
 
 // Buffer resources: a uniform base per matrix and chunk, bounded by its size,
 // so a load past it returns zero and a store past it is dropped (the rows of a
